@@ -1,0 +1,170 @@
+"""Python access to the float64 CPU oracle of the fused MoE + multi-LoRA layer.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, the smoke check and the benchmark's
+CPU-baseline leg, never by the library. It shares no code with the HIP path and does not
+import it. The arithmetic lives in moelora_oracle.c; this file only marshals arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moelora_oracle.c")
+_LIB = os.path.join(_HERE, "libmoelora_oracle.so")
+
+ORC_BF16, ORC_F32, ORC_F64 = 0, 1, 2
+
+
+def build() -> str:
+    """Compile the oracle with gcc (host code only)."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-Wall", "-shared", "-fPIC", _SRC, "-o", _LIB, "-lm"]
+    subprocess.run(cmd, check=True)
+    return _LIB
+
+
+class _Dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("T", "hidden", "inter", "n_experts", "n_adapters", "rank", "topk")]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i32 = ctypes.c_int32
+        L.oracle_route.argtypes = [P, i32, i32, i32, P, P]
+        L.oracle_align.argtypes = [P, P, i32, i32, i32, i32, i32, i32, P, ctypes.c_int64, P, P, i32, P]
+        L.oracle_forward.argtypes = [ctypes.POINTER(_Dims), P, P, P, P, P, i32, P, P]
+        L.oracle_num_threads.argtypes = []
+        for f in (L.oracle_route, L.oracle_align, L.oracle_forward, L.oracle_num_threads):
+            f.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _np(a):
+    """numpy view of a CPU array or torch tensor; bf16 comes back as uint16 bit patterns."""
+    if hasattr(a, "detach"):
+        import torch
+        a = a.detach()
+        if a.device.type != "cpu":
+            raise ValueError("the oracle takes host arrays")
+        if a.dtype == torch.bfloat16:
+            return np.ascontiguousarray(a.contiguous().view(torch.int16).numpy().view(np.uint16)), ORC_BF16
+        a = a.contiguous().numpy()
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return a, ORC_BF16
+    if a.dtype == np.float32:
+        return a, ORC_F32
+    if a.dtype == np.float64:
+        return a, ORC_F64
+    raise TypeError(f"unsupported dtype {a.dtype}")
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _i32(a):
+    if hasattr(a, "detach"):
+        a = a.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise OracleError(f"{what} failed with code {rc}")
+
+
+def route(logits, k: int):
+    """Top-k expert ids per token (slot order) and their softmax weights (float64)."""
+    L, dtc = _np(logits)
+    if dtc != ORC_F32:
+        raise TypeError("router logits are float32")
+    T, E = L.shape
+    ids = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float64)
+    _check(lib().oracle_route(_ptr(L), T, E, k, _ptr(ids), _ptr(w)), "oracle_route")
+    return ids, w
+
+
+def align(topk_ids, adapter_ids, n_experts: int, n_adapters: int, seg_pad: int = 1, block_m: int = 1):
+    """Sorted pair list, padded expert offsets and segment table (see moelora_oracle.c)."""
+    ids = _i32(topk_ids)
+    ad = _i32(adapter_ids)
+    T, k = ids.shape
+    P = T * k
+    cap = P * seg_pad + n_experts * block_m
+    sp = np.empty(max(cap, 1), np.int32)
+    off = np.empty(n_experts + 1, np.int32)
+    seg_cap = max(P, 1)
+    seg = np.empty((seg_cap, 4), np.int32)
+    ns = np.zeros(1, np.int32)
+    _check(lib().oracle_align(_ptr(ids), _ptr(ad), T, k, n_experts, n_adapters, seg_pad, block_m,
+                              _ptr(sp), cap, _ptr(off), _ptr(seg), seg_cap, _ptr(ns)), "oracle_align")
+    total = int(off[-1])
+    return {"sorted_pairs": sp[:total].copy(), "expert_offsets": off, "seg_table": seg[: int(ns[0])].copy(),
+            "n_seg": int(ns[0])}
+
+
+def forward(inputs: dict, topk: int, tokens=None, return_pairs: bool = False):
+    """y[len(tokens)][h] in float64 (all tokens when tokens is None).
+
+    `inputs` holds x, logits, W1, W2, A1, B1, A2, B2, adapter_ids with the stored layouts
+    x[T][h], W1[E][2I][h], W2[E][h][I], A1[nA][E][r][h], B1[nA][E][2I][r], A2[nA][E][r][I],
+    B2[nA][E][h][r]; each may be bf16, float32 or float64."""
+    arrs = []
+    dts = []
+    for name in ("x", "W1", "W2", "A1", "B1", "A2", "B2"):
+        a, dtc = _np(inputs[name])
+        arrs.append(a)
+        dts.append(dtc)
+    x, W1, W2, A1, B1, A2, B2 = arrs
+    T, h = x.shape
+    E, twoI, h1 = W1.shape
+    I = twoI // 2
+    nA, E1, r, h2 = A1.shape
+    if not (h1 == h2 == h and E1 == E and W2.shape == (E, h, I) and B1.shape == (nA, E, 2 * I, r)
+            and A2.shape == (nA, E, r, I) and B2.shape == (nA, E, h, r)):
+        raise ValueError("inconsistent shapes")
+    L, ldt = _np(inputs["logits"])
+    if ldt != ORC_F32 or L.shape != (T, E):
+        raise ValueError("logits must be float32 [T][E]")
+    ad = _i32(inputs["adapter_ids"])
+    if ad.shape != (T,):
+        raise ValueError("adapter_ids must be [T]")
+    dims = _Dims(T, h, I, E, nA, r, topk)
+    if tokens is None:
+        toks = None
+        n = T
+    else:
+        toks = _i32(tokens).reshape(-1)
+        n = toks.size
+    y = np.zeros((n, h), np.float64)
+    dp = np.zeros((n, topk, h), np.float64) if return_pairs else None
+    tptr = (ctypes.c_void_p * 7)(*[a.ctypes.data for a in arrs])
+    dtarr = (ctypes.c_int32 * 7)(*dts)
+    rc = lib().oracle_forward(ctypes.byref(dims), tptr, dtarr, _ptr(L), _ptr(ad),
+                              None if toks is None else _ptr(toks), n, _ptr(y),
+                              None if dp is None else _ptr(dp))
+    _check(rc, "oracle_forward")
+    return (y, dp) if return_pairs else y
+
+
+def num_threads() -> int:
+    return int(lib().oracle_num_threads())
