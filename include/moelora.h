@@ -1,0 +1,121 @@
+/*
+ * moelora.h — C ABI of the fused MoE + multi-LoRA layer for AMD Instinct MI355X (gfx950).
+ *
+ * The layer (page "vLLM MoE LoRA SageMaker Bedrock", sections "Entendendo os Modelos MoE" and
+ * "O Papel da Multi-LoRA"; page "Punica: Multi-Tenant LoRA Serving", proposed-method section):
+ * each token is routed to its top-k experts; every selected expert applies a frozen gate_up
+ * projection, SiLU-and-mul and a frozen down projection, and both projections also apply the
+ * token's own LoRA adapter (shrink z = xA to rank r, expand z B added to the base output).
+ * The expert outputs are combined with the router weights.
+ *
+ * Conventions fixed by this library where the pages are silent:
+ *   - routing weights: softmax over the k selected logits; ties go to the lower expert id;
+ *     slots are in descending logit order;
+ *   - W1 rows 0..I-1 are gate, I..2I-1 up; act = silu(gate) * up; LoRA scale 1;
+ *   - one (A1, B1) pair per (adapter, expert) for gate_up, one (A2, B2) for down;
+ *   - adapter id -1 means "no adapter" for that token.
+ *
+ * Stored layouts ("out x in", the reduction dimension contiguous; the pages' math matrices
+ * are the transposes). All tensors are dense, row-major, device memory:
+ *   x            bf16 [T][h]
+ *   router_logits f32 [T][E]
+ *   W1           bf16 [E][2I][h]        W2  bf16 [E][h][I]
+ *   A1           bf16 [nA][E][r][h]     B1  bf16 [nA][E][2I][r]
+ *   A2           bf16 [nA][E][r][I]     B2  bf16 [nA][E][h][r]
+ *   adapter_ids  int32 [T], each in [-1, nA)
+ *   y            bf16 [T][h]  (written, not accumulated)
+ *
+ * Ownership and ordering: the caller owns every buffer (inputs, outputs, workspace). The
+ * library allocates nothing on the call path, keeps no per-call state, and enqueues its
+ * kernels asynchronously on `stream` (a hipStream_t; NULL is the null stream). No call
+ * synchronises the host except moe_lora_debug_status. Two calls that share a workspace
+ * must be ordered on one stream.
+ *
+ * Errors: every entry point validates its arguments on the host before enqueueing any work
+ * and returns a negative MOELORA_E* code without touching the device when they are invalid.
+ * Data-dependent problems (non-finite logits, adapter ids out of range) cannot be seen on the
+ * host; kernels record them as flags in the workspace, treat such a token's adapter as -1 and
+ * such a logit as -infinity, and moe_lora_debug_status reads the flags back.
+ */
+#ifndef MOELORA_H
+#define MOELORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define MOELORA_OK 0
+#define MOELORA_EINVAL_DIMS (-1) /* a size is out of the supported range (see below) */
+#define MOELORA_ENULL (-2)       /* a required pointer is NULL */
+#define MOELORA_EALIGN (-3)      /* a tensor pointer is not 16-byte aligned */
+#define MOELORA_EWORKSPACE (-4)  /* workspace too small or misaligned (256-byte alignment) */
+#define MOELORA_EHIP (-5)        /* a HIP launch or runtime call failed */
+#define MOELORA_EDEVICE (-6)     /* the current device is not gfx950 */
+
+/* Device-side flags reported by moe_lora_debug_status. */
+#define MOELORA_FLAG_NONFINITE_LOGIT 1u
+#define MOELORA_FLAG_ADAPTER_RANGE 2u
+
+/* Layer sizes. Supported: T >= 0; hidden and inter positive multiples of 128; n_experts in
+ * [1, 1024]; n_adapters >= 1; rank in {8, 16, 32, 64}; 1 <= topk <= min(n_experts, 16). */
+typedef struct {
+  int32_t T, hidden, inter, n_experts, n_adapters, rank;
+} moe_lora_dims;
+
+/* Bytes of device workspace moe_lora_forward needs for these sizes (0 when the sizes are
+ * unsupported). The workspace must be 256-byte aligned; its contents need no initialisation
+ * and are overwritten by every call. */
+size_t moe_lora_workspace_size(const moe_lora_dims *d, int32_t topk);
+
+/* The fused layer: routing (top-k softmax), sorting token-expert pairs by (expert, adapter,
+ * token), LoRA shrink for gate_up, gate_up GEMM with the LoRA expand and SiLU-and-mul fused in
+ * its epilogue, LoRA shrink for down, down GEMM with the LoRA expand fused, and the weighted
+ * top-k combine. See the header comment for layouts. Returns MOELORA_OK once the work is
+ * enqueued on `stream`. With T = 0 nothing is enqueued and no pointer is inspected. */
+int moe_lora_forward(const void *x, const float *router_logits, const void *W1, const void *W2,
+                     const void *A1, const void *B1, const void *A2, const void *B2,
+                     const int32_t *adapter_ids, int32_t topk, const moe_lora_dims *d, void *y,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* Upper bound on the padded sorted-pair length for (seg_pad, block_m):
+ * T*topk*seg_pad + n_experts*(block_m-1), or -1 for invalid arguments. */
+int64_t moe_lora_sorted_capacity(const moe_lora_dims *d, int32_t topk, int32_t seg_pad,
+                                 int32_t block_m);
+
+/* Routing and align on their own, for inspection and tests.
+ *   topk_ids   int32 [T][topk]  expert of slot j, slots in descending logit order
+ *   topk_w     f32   [T][topk]  softmax of the selected logits
+ *   sorted_pairs int32 [sorted_cap]  pair ids p = t*topk + j ordered by the key
+ *              (expert, adapter, token); each (expert, adapter) segment padded with -1 to a
+ *              multiple of seg_pad, each expert block to a multiple of block_m; entries past
+ *              the padded total are left untouched
+ *   expert_offsets int32 [E+1]  padded start of each expert block; [E] = padded total
+ *   seg_table  int32 [T*topk][4]  rows (expert, adapter, padded start, real count) in key
+ *              order (adapter -1 first within an expert)
+ *   n_seg      int32 [1]        number of seg_table rows written
+ * All outputs are device pointers. seg_pad and block_m are in [1, 256]; sorted_cap must be at
+ * least moe_lora_sorted_capacity(...). The workspace is the same as moe_lora_forward's. With
+ * T = 0, router_logits, adapter_ids, topk_ids and topk_w may be NULL. */
+int moe_lora_route_align(const float *router_logits, const int32_t *adapter_ids, int32_t topk,
+                         const moe_lora_dims *d, int32_t seg_pad, int32_t block_m,
+                         int32_t *topk_ids, float *topk_w, int32_t *sorted_pairs,
+                         int64_t sorted_cap, int32_t *expert_offsets, int32_t *seg_table,
+                         int32_t *n_seg, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Text for a return code. Never NULL. */
+const char *moe_lora_strerror(int code);
+
+/* Synchronises `stream`, then reads the device flags of the last call that used this
+ * workspace into *flags (MOELORA_FLAG_* bits). Returns MOELORA_OK or an error code. */
+int moe_lora_debug_status(const void *workspace, size_t workspace_bytes, void *stream,
+                          uint32_t *flags);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOELORA_H */

@@ -1,0 +1,181 @@
+"""Fused MoE + multi-LoRA layer for AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding over libmoelora.so (include/moelora.h). Every step of the layer runs in
+the library's HIP kernels; this module only checks tensor shapes, allocates outputs and the
+workspace with torch when the caller does not pass them, and hands raw device pointers and
+torch's current HIP stream to the C ABI. There is no fallback: without the built library or
+a gfx950 device every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoelora.so")
+
+OK, EINVAL_DIMS, ENULL, EALIGN, EWORKSPACE, EHIP, EDEVICE = 0, -1, -2, -3, -4, -5, -6
+FLAG_NONFINITE_LOGIT, FLAG_ADAPTER_RANGE = 1, 2
+
+EXPORTS = ("moe_lora_workspace_size", "moe_lora_forward", "moe_lora_sorted_capacity",
+           "moe_lora_route_align", "moe_lora_strerror", "moe_lora_debug_status")
+
+
+class MoeLoraError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {strerror(code)} (code {code})")
+        self.code = code
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("T", "hidden", "inter", "n_experts", "n_adapters", "rank")]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with lora_mixture_experts_amd.build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        D = ctypes.POINTER(Dims)
+        L.moe_lora_workspace_size.argtypes = [D, i32]
+        L.moe_lora_workspace_size.restype = ctypes.c_size_t
+        L.moe_lora_forward.argtypes = [P, P, P, P, P, P, P, P, P, i32, D, P, P, ctypes.c_size_t, P]
+        L.moe_lora_forward.restype = ctypes.c_int
+        L.moe_lora_sorted_capacity.argtypes = [D, i32, i32, i32]
+        L.moe_lora_sorted_capacity.restype = i64
+        L.moe_lora_route_align.argtypes = [P, P, i32, D, i32, i32, P, P, P, i64, P, P, P, P,
+                                           ctypes.c_size_t, P]
+        L.moe_lora_route_align.restype = ctypes.c_int
+        L.moe_lora_strerror.argtypes = [ctypes.c_int]
+        L.moe_lora_strerror.restype = ctypes.c_char_p
+        L.moe_lora_debug_status.argtypes = [P, ctypes.c_size_t, P, ctypes.POINTER(ctypes.c_uint32)]
+        L.moe_lora_debug_status.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().moe_lora_strerror(code).decode()
+
+
+def _check(code: int, what: str):
+    if code != OK:
+        raise MoeLoraError(code, what)
+
+
+def dims_of(x: torch.Tensor, W1: torch.Tensor, A1: torch.Tensor) -> Dims:
+    T, h = x.shape
+    E, twoI, _ = W1.shape
+    nA, _, r, _ = A1.shape
+    return Dims(T, h, twoI // 2, E, nA, r)
+
+
+def workspace_size(d: Dims, topk: int) -> int:
+    return int(lib().moe_lora_workspace_size(ctypes.byref(d), topk))
+
+
+def sorted_capacity(d: Dims, topk: int, seg_pad: int, block_m: int) -> int:
+    return int(lib().moe_lora_sorted_capacity(ctypes.byref(d), topk, seg_pad, block_m))
+
+
+def new_workspace(d: Dims, topk: int, device) -> torch.Tensor:
+    n = workspace_size(d, topk)
+    if n == 0:
+        raise MoeLoraError(EINVAL_DIMS, "workspace_size")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _expect(t: torch.Tensor, name: str, dtype, shape):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU")
+
+
+def forward(x, router_logits, W1, W2, A1, B1, A2, B2, adapter_ids, topk: int, y=None,
+            workspace=None) -> torch.Tensor:
+    """y[T][h] (bf16) of the fused MoE + multi-LoRA layer; see include/moelora.h."""
+    d = dims_of(x, W1, A1)
+    T, h, I, E, nA, r = d.T, d.hidden, d.inter, d.n_experts, d.n_adapters, d.rank
+    bf = torch.bfloat16
+    _expect(x, "x", bf, (T, h))
+    _expect(router_logits, "router_logits", torch.float32, (T, E))
+    _expect(W1, "W1", bf, (E, 2 * I, h))
+    _expect(W2, "W2", bf, (E, h, I))
+    _expect(A1, "A1", bf, (nA, E, r, h))
+    _expect(B1, "B1", bf, (nA, E, 2 * I, r))
+    _expect(A2, "A2", bf, (nA, E, r, I))
+    _expect(B2, "B2", bf, (nA, E, h, r))
+    _expect(adapter_ids, "adapter_ids", torch.int32, (T,))
+    if y is None:
+        y = torch.empty((T, h), dtype=bf, device=x.device)
+    _expect(y, "y", bf, (T, h))
+    if workspace is None:
+        workspace = new_workspace(d, topk, x.device)
+    rc = lib().moe_lora_forward(_ptr(x), _ptr(router_logits), _ptr(W1), _ptr(W2), _ptr(A1),
+                                _ptr(B1), _ptr(A2), _ptr(B2), _ptr(adapter_ids), topk,
+                                ctypes.byref(d), _ptr(y), _ptr(workspace), workspace.numel(),
+                                _stream(x.device))
+    _check(rc, "moe_lora_forward")
+    return y
+
+
+def route_align(router_logits, adapter_ids, topk: int, d: Dims, seg_pad: int = 1, block_m: int = 1,
+                workspace=None) -> dict:
+    """Routing and align outputs as device tensors; see moe_lora_route_align."""
+    dev = router_logits.device
+    _expect(router_logits, "router_logits", torch.float32, (d.T, d.n_experts))
+    _expect(adapter_ids, "adapter_ids", torch.int32, (d.T,))
+    cap = sorted_capacity(d, topk, seg_pad, block_m)
+    if cap < 0:
+        raise MoeLoraError(EINVAL_DIMS, "sorted_capacity")
+    P = d.T * topk
+    out = {
+        "topk_ids": torch.empty((d.T, topk), dtype=torch.int32, device=dev),
+        "topk_w": torch.empty((d.T, topk), dtype=torch.float32, device=dev),
+        "sorted_pairs": torch.full((max(cap, 1),), -7, dtype=torch.int32, device=dev),
+        "expert_offsets": torch.empty(d.n_experts + 1, dtype=torch.int32, device=dev),
+        "seg_table": torch.empty((max(P, 1), 4), dtype=torch.int32, device=dev),
+        "n_seg": torch.empty(1, dtype=torch.int32, device=dev),
+    }
+    if workspace is None:
+        workspace = new_workspace(d, topk, dev)
+    rc = lib().moe_lora_route_align(_ptr(router_logits), _ptr(adapter_ids), topk, ctypes.byref(d),
+                                    seg_pad, block_m, _ptr(out["topk_ids"]), _ptr(out["topk_w"]),
+                                    _ptr(out["sorted_pairs"]), cap, _ptr(out["expert_offsets"]),
+                                    _ptr(out["seg_table"]), _ptr(out["n_seg"]), _ptr(workspace),
+                                    workspace.numel(), _stream(dev))
+    _check(rc, "moe_lora_route_align")
+    out["workspace"] = workspace
+    return out
+
+
+def debug_status(workspace: torch.Tensor) -> int:
+    """Device flags (FLAG_* bits) of the last call that used `workspace`; synchronises."""
+    flags = ctypes.c_uint32(0)
+    rc = lib().moe_lora_debug_status(_ptr(workspace), workspace.numel(), _stream(workspace.device),
+                                     ctypes.byref(flags))
+    _check(rc, "moe_lora_debug_status")
+    return int(flags.value)

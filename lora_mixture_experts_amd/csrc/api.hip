@@ -1,0 +1,336 @@
+// C ABI of libmoelora: argument validation, workspace carve-up and the launch sequence of the
+// fused MoE + multi-LoRA layer (declared in include/moelora.h).
+#include <string.h>
+
+#include "common.h"
+#include "kernels.h"
+#include "moelora.h"
+
+using namespace moelora;
+
+namespace {
+
+constexpr int kMaxBM = 256;  // largest row block any GEMM path uses
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+int64_t round_up64(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+int validate_dims(const moe_lora_dims* d, int32_t topk) {
+  if (!d) return MOELORA_ENULL;
+  if (d->T < 0 || d->hidden <= 0 || d->inter <= 0 || d->n_experts <= 0 || d->n_adapters <= 0)
+    return MOELORA_EINVAL_DIMS;
+  if (d->hidden % 128 != 0 || d->inter % 128 != 0) return MOELORA_EINVAL_DIMS;
+  if (d->n_experts > kMaxExperts) return MOELORA_EINVAL_DIMS;
+  if (!(d->rank == 8 || d->rank == 16 || d->rank == 32 || d->rank == 64)) return MOELORA_EINVAL_DIMS;
+  if (topk < 1 || topk > d->n_experts || topk > kMaxTopk) return MOELORA_EINVAL_DIMS;
+  // every index the kernels form in 32 bits must fit
+  const int64_t P = (int64_t)d->T * topk;
+  if (P + (int64_t)d->n_experts * kMaxBM >= ((int64_t)1 << 30)) return MOELORA_EINVAL_DIMS;
+  if ((int64_t)d->n_experts * (d->n_adapters + 1) >= ((int64_t)1 << 28)) return MOELORA_EINVAL_DIMS;
+  return MOELORA_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_device() {
+  static int known[64];  // 0 unknown, 1 gfx950, -1 other
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOELORA_EHIP;
+  if (dev < 0 || dev >= 64) return MOELORA_EDEVICE;
+  if (known[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOELORA_EHIP;
+    known[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+  }
+  return known[dev] == 1 ? MOELORA_OK : MOELORA_EDEVICE;
+}
+
+// Where the align kernel keeps its tables: LDS when they fit, else the workspace.
+size_t align_lds_plan(int T, int k, int E, int nA, AlignArgs* a) {
+  const size_t budget = (size_t)(kLdsBytes - kAlignStaticLds);
+  const size_t tables = 2 * sizeof(int) * (size_t)E * (nA + 1);
+  const size_t stage = sizeof(int) * ((size_t)T * k + T);
+  a->tables_in_lds = 0;
+  a->stage_inputs = 0;
+  size_t used = 0;
+  if (tables <= budget) {
+    a->tables_in_lds = 1;
+    used += tables;
+  }
+  if (used + stage <= budget) {
+    a->stage_inputs = 1;
+    used += stage;
+  }
+  return used;
+}
+
+// Row-block size (16 * NT) of the skinny GEMM path from the mean rows per expert.
+int pick_nt(int64_t P, int E) {
+  const double mean = (double)P / E;
+  if (mean <= 12.0) return 1;
+  if (mean <= 24.0) return 2;
+  return 4;
+}
+
+int pick_splits(int64_t tiles, int K) {
+  int s = (int)((1024 + tiles - 1) / (tiles > 0 ? tiles : 1));
+  s = s < 1 ? 1 : (s > kMaxSplit ? kMaxSplit : s);
+  const int nks = K / 128;
+  return s > nks ? nks : s;
+}
+
+}  // namespace
+
+bool moelora_make_layout(int T, int h, int I, int E, int nA, int r, int topk, MoeLoraLayout* L) {
+  const int64_t P = (int64_t)T * topk;
+  L->max_bm = kMaxBM;
+  L->splits = kMaxSplit;
+  L->cap = round_up64(P + (int64_t)E * (kMaxBM - 1), 256);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + (bytes ? bytes : 1));
+    return o;
+  };
+  L->flags = take(16);  // first, so moe_lora_debug_status can find it without the sizes
+  L->topk_ids = take(4 * (size_t)P);
+  L->topk_w = take(4 * (size_t)P);
+  L->tok_flags = take(4 * (size_t)T);
+  L->sorted = take(4 * (size_t)L->cap);
+  L->expert_off = take(4 * (size_t)(E + 1));
+  L->n_blocks = take(4);
+  L->block_expert = take(4 * (size_t)(L->cap / 16 + 1));
+  L->seg_table = take(16 * (size_t)P);
+  L->n_seg = take(4);
+  L->z1 = take(4 * (size_t)kMaxSplit * L->cap * r);
+  L->z2 = take(4 * (size_t)kMaxSplit * L->cap * r);
+  L->act = take(2 * (size_t)L->cap * I);
+  L->dpair = take(4 * (size_t)P * h);
+  L->align_cnt = take(4 * (size_t)E * (nA + 1));
+  L->align_start = take(4 * (size_t)E * (nA + 1));
+  L->total = off;
+  return true;
+}
+
+extern "C" {
+
+size_t moe_lora_workspace_size(const moe_lora_dims* d, int32_t topk) {
+  if (validate_dims(d, topk) != MOELORA_OK) return 0;
+  MoeLoraLayout L;
+  moelora_make_layout(d->T, d->hidden, d->inter, d->n_experts, d->n_adapters, d->rank, topk, &L);
+  return L.total;
+}
+
+int64_t moe_lora_sorted_capacity(const moe_lora_dims* d, int32_t topk, int32_t seg_pad,
+                                 int32_t block_m) {
+  if (validate_dims(d, topk) != MOELORA_OK) return -1;
+  if (seg_pad < 1 || seg_pad > 256 || block_m < 1 || block_m > 256) return -1;
+  return (int64_t)d->T * topk * seg_pad + (int64_t)d->n_experts * (block_m - 1);
+}
+
+const char* moe_lora_strerror(int code) {
+  switch (code) {
+    case MOELORA_OK: return "ok";
+    case MOELORA_EINVAL_DIMS: return "sizes out of the supported range";
+    case MOELORA_ENULL: return "a required pointer is NULL";
+    case MOELORA_EALIGN: return "a tensor pointer is not 16-byte aligned";
+    case MOELORA_EWORKSPACE: return "workspace too small or not 256-byte aligned";
+    case MOELORA_EHIP: return "HIP launch or runtime error";
+    case MOELORA_EDEVICE: return "current device is not gfx950";
+    default: return "unknown error code";
+  }
+}
+
+int moe_lora_forward(const void* x, const float* router_logits, const void* W1, const void* W2,
+                     const void* A1, const void* B1, const void* A2, const void* B2,
+                     const int32_t* adapter_ids, int32_t topk, const moe_lora_dims* d, void* y,
+                     void* workspace, size_t workspace_bytes, void* stream_) {
+  int rc = validate_dims(d, topk);
+  if (rc != MOELORA_OK) return rc;
+  if (d->T == 0) return MOELORA_OK;  // empty batch: nothing to do, pointers may be NULL
+  const void* ptrs[] = {x, router_logits, W1, W2, A1, B1, A2, B2, adapter_ids, y, workspace};
+  for (const void* p : ptrs)
+    if (!p) return MOELORA_ENULL;
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOELORA_EALIGN;
+  if (((uintptr_t)workspace & 255u) != 0) return MOELORA_EWORKSPACE;
+  MoeLoraLayout L;
+  moelora_make_layout(d->T, d->hidden, d->inter, d->n_experts, d->n_adapters, d->rank, topk, &L);
+  if (workspace_bytes < L.total) return MOELORA_EWORKSPACE;
+  rc = check_device();
+  if (rc != MOELORA_OK) return rc;
+
+  hipStream_t stream = (hipStream_t)stream_;
+  char* ws = (char*)workspace;
+  const int T = d->T, h = d->hidden, I = d->inter, E = d->n_experts, nA = d->n_adapters, r = d->rank;
+  const int64_t P = (int64_t)T * topk;
+  int* topk_ids = (int*)(ws + L.topk_ids);
+  float* topk_w = (float*)(ws + L.topk_w);
+  int* tok_flags = (int*)(ws + L.tok_flags);
+  int* sorted = (int*)(ws + L.sorted);
+  int* n_blocks = (int*)(ws + L.n_blocks);
+  int* block_expert = (int*)(ws + L.block_expert);
+  float* z1 = (float*)(ws + L.z1);
+  float* z2 = (float*)(ws + L.z2);
+  uint16_t* act = (uint16_t*)(ws + L.act);
+  float* dpair = (float*)(ws + L.dpair);
+
+  if (launch_route(router_logits, T, E, topk, topk_ids, topk_w, tok_flags, stream) != hipSuccess)
+    return MOELORA_EHIP;
+
+  const int nt = pick_nt(P, E);
+  const int bm = 16 * nt;
+  AlignArgs al;
+  al.topk_ids = topk_ids;
+  al.adapter_ids = adapter_ids;
+  al.tok_flags = tok_flags;
+  al.T = T;
+  al.k = topk;
+  al.E = E;
+  al.nA = nA;
+  al.seg_pad = 1;
+  al.block_m = bm;
+  al.sorted_pairs = sorted;
+  al.expert_offsets = (int*)(ws + L.expert_off);
+  al.seg_table = (int*)(ws + L.seg_table);
+  al.n_seg = (int*)(ws + L.n_seg);
+  al.flags = (int*)(ws + L.flags);
+  al.block_expert = block_expert;
+  al.n_blocks = n_blocks;
+  al.g_cnt = (int*)(ws + L.align_cnt);
+  al.g_start = (int*)(ws + L.align_start);
+  const size_t lds = align_lds_plan(T, topk, E, nA, &al);
+  if (launch_align(al, lds, stream) != hipSuccess) return MOELORA_EHIP;
+
+  const int64_t max_rows = P + (int64_t)E * (bm - 1);
+  const int max_blocks = (int)((max_rows + bm - 1) / bm);
+  const int tiles16 = max_blocks * nt;
+  const int s1 = pick_splits(tiles16, h), s2 = pick_splits(tiles16, I);
+
+  ShrinkArgs sh;
+  sh.sorted_pairs = sorted;
+  sh.block_expert = block_expert;
+  sh.n_blocks = n_blocks;
+  sh.bm = bm;
+  sh.adapter_ids = adapter_ids;
+  sh.k = topk;
+  sh.nA = nA;
+  sh.E = E;
+  sh.r = r;
+  sh.cap = L.cap;
+
+  GemmArgs g;
+  g.cap = L.cap;
+  g.sorted_pairs = sorted;
+  g.block_expert = block_expert;
+  g.n_blocks = n_blocks;
+  g.adapter_ids = adapter_ids;
+  g.k = topk;
+  g.nA = nA;
+  g.E = E;
+  g.r = r;
+  g.act_out = act;
+  g.d_out = dpair;
+
+  // gate_up: shrink z1 = x A1, then W1 GEMM + z1 B1 + SiLU-and-mul -> act
+  sh.X = (const uint16_t*)x;
+  sh.Aw = (const uint16_t*)A1;
+  sh.K = h;
+  sh.S = s1;
+  sh.zpart = z1;
+  if (launch_shrink(true, sh, tiles16, stream) != hipSuccess) return MOELORA_EHIP;
+  g.X = (const uint16_t*)x;
+  g.W = (const uint16_t*)W1;
+  g.Bw = (const uint16_t*)B1;
+  g.zpart = z1;
+  g.S = s1;
+  g.K = h;
+  g.N = I;
+  if (launch_skinny(nt, true, g, (I + 63) / 64, max_blocks, stream) != hipSuccess) return MOELORA_EHIP;
+
+  // down: shrink z2 = act A2, then W2 GEMM + z2 B2 -> D (fp32, pair order)
+  sh.X = act;
+  sh.Aw = (const uint16_t*)A2;
+  sh.K = I;
+  sh.S = s2;
+  sh.zpart = z2;
+  if (launch_shrink(false, sh, tiles16, stream) != hipSuccess) return MOELORA_EHIP;
+  g.X = act;
+  g.W = (const uint16_t*)W2;
+  g.Bw = (const uint16_t*)B2;
+  g.zpart = z2;
+  g.S = s2;
+  g.K = I;
+  g.N = h;
+  if (launch_skinny(nt, false, g, (h + 63) / 64, max_blocks, stream) != hipSuccess) return MOELORA_EHIP;
+
+  // weighted top-k combine -> y (bf16)
+  if (launch_combine(dpair, topk_w, T, topk, h, (uint16_t*)y, stream) != hipSuccess) return MOELORA_EHIP;
+  return MOELORA_OK;
+}
+
+int moe_lora_route_align(const float* router_logits, const int32_t* adapter_ids, int32_t topk,
+                         const moe_lora_dims* d, int32_t seg_pad, int32_t block_m,
+                         int32_t* topk_ids, float* topk_w, int32_t* sorted_pairs,
+                         int64_t sorted_cap, int32_t* expert_offsets, int32_t* seg_table,
+                         int32_t* n_seg, void* workspace, size_t workspace_bytes, void* stream_) {
+  int rc = validate_dims(d, topk);
+  if (rc != MOELORA_OK) return rc;
+  const int64_t need = moe_lora_sorted_capacity(d, topk, seg_pad, block_m);
+  if (need < 0 || sorted_cap < need) return MOELORA_EINVAL_DIMS;
+  const void* ptrs[] = {router_logits, adapter_ids, topk_ids, topk_w, sorted_pairs,
+                        expert_offsets, seg_table, n_seg, workspace};
+  for (int i = 0; i < 9; ++i)  // the [T]-sized tensors may be NULL when T == 0
+    if (!ptrs[i] && !(d->T == 0 && i < 4)) return MOELORA_ENULL;
+  for (const void* p : ptrs)
+    if (((uintptr_t)p & 3u) != 0) return MOELORA_EALIGN;
+  if (((uintptr_t)workspace & 255u) != 0) return MOELORA_EWORKSPACE;
+  MoeLoraLayout L;
+  moelora_make_layout(d->T, d->hidden, d->inter, d->n_experts, d->n_adapters, d->rank, topk, &L);
+  if (workspace_bytes < L.total) return MOELORA_EWORKSPACE;
+  rc = check_device();
+  if (rc != MOELORA_OK) return rc;
+
+  hipStream_t stream = (hipStream_t)stream_;
+  char* ws = (char*)workspace;
+  int* tok_flags = (int*)(ws + L.tok_flags);
+  if (launch_route(router_logits, d->T, d->n_experts, topk, topk_ids, topk_w, tok_flags, stream) !=
+      hipSuccess)
+    return MOELORA_EHIP;
+  AlignArgs al;
+  al.topk_ids = topk_ids;
+  al.adapter_ids = adapter_ids;
+  al.tok_flags = tok_flags;
+  al.T = d->T;
+  al.k = topk;
+  al.E = d->n_experts;
+  al.nA = d->n_adapters;
+  al.seg_pad = seg_pad;
+  al.block_m = block_m;
+  al.sorted_pairs = sorted_pairs;
+  al.expert_offsets = expert_offsets;
+  al.seg_table = seg_table;
+  al.n_seg = n_seg;
+  al.flags = (int*)(ws + L.flags);
+  al.block_expert = nullptr;
+  al.n_blocks = nullptr;
+  al.g_cnt = (int*)(ws + L.align_cnt);
+  al.g_start = (int*)(ws + L.align_start);
+  const size_t lds = align_lds_plan(d->T, topk, d->n_experts, d->n_adapters, &al);
+  if (launch_align(al, lds, stream) != hipSuccess) return MOELORA_EHIP;
+  return MOELORA_OK;
+}
+
+int moe_lora_debug_status(const void* workspace, size_t workspace_bytes, void* stream_,
+                          uint32_t* flags) {
+  if (!workspace || !flags) return MOELORA_ENULL;
+  if (((uintptr_t)workspace & 255u) != 0 || workspace_bytes < 16) return MOELORA_EWORKSPACE;
+  hipStream_t stream = (hipStream_t)stream_;
+  if (hipStreamSynchronize(stream) != hipSuccess) return MOELORA_EHIP;
+  int32_t v = 0;
+  if (hipMemcpy(&v, workspace, sizeof v, hipMemcpyDeviceToHost) != hipSuccess) return MOELORA_EHIP;
+  *flags = (uint32_t)v;
+  return MOELORA_OK;
+}
+
+}  // extern "C"

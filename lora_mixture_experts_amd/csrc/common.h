@@ -1,0 +1,82 @@
+// Internal helpers shared by the HIP kernels and the host entry points of libmoelora.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moelora {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kMaxTopk = 16;
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxSplit = 8;  // split-K parts of the LoRA shrink
+
+// ------------------------------------------------------------------------------------------
+// bf16 <-> f32. A bf16 is the upper half of an IEEE binary32.
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+// Round-to-nearest-even to bf16; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// D += A(16x32) * B(32x16), bf16 inputs, fp32 accumulate. Lane l supplies row (l % 16) of A
+// and column (l % 16) of B, 8 reduction elements each, in the same reduction-slot order; lane
+// l receives D rows 4*(l/16) .. 4*(l/16)+3 of column (l % 16).
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 ldg16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  return (1ull << (threadIdx.x & 63)) - 1ull;
+}
+
+// The sorted-row layout every GEMM pass shares: rows are token-expert pairs sorted by
+// (expert, adapter, token), each expert block padded to a multiple of the row-block size;
+// padding rows hold pair id -1.
+struct RowInfo {
+  int pair;     // t * topk + j, or -1 for padding
+  int token;    // pair / topk
+  int adapter;  // adapter of the token, -1 for none or padding
+};
+
+__device__ __forceinline__ int sanitize_adapter(int a, int nA) {
+  return (a >= 0 && a < nA) ? a : -1;
+}
+
+}  // namespace moelora
+
+// ------------------------------------------------------------------------------------------
+// Workspace layout (host side). Every region starts on a 256-byte boundary.
+// ------------------------------------------------------------------------------------------
+struct MoeLoraLayout {
+  size_t topk_ids, topk_w, tok_flags, flags, sorted, expert_off, n_blocks, block_expert,
+      seg_table, n_seg, z1, z2, act, dpair, align_cnt, align_start;
+  size_t total;
+  int64_t cap;     // rows of the sorted layout at the largest row-block size
+  int max_bm;      // largest row-block size any path uses
+  int splits;      // split-K parts of the LoRA shrink
+};
+
+bool moelora_make_layout(int T, int h, int I, int E, int nA, int r, int topk, MoeLoraLayout* L);

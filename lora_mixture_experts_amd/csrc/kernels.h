@@ -1,0 +1,74 @@
+// Kernel argument blocks and kernel declarations of libmoelora (internal).
+#pragma once
+
+#include "common.h"
+
+namespace moelora {
+
+struct AlignArgs {
+  const int* topk_ids;     // [T*k]
+  const int* adapter_ids;  // [T]
+  const int* tok_flags;    // [T]
+  int T, k, E, nA, seg_pad, block_m;
+  int* sorted_pairs;    // [>= padded total]
+  int* expert_offsets;  // [E+1]
+  int* seg_table;       // [T*k][4]
+  int* n_seg;           // [1]
+  int* flags;           // [1]
+  int* block_expert;    // [padded total / block_m] or nullptr
+  int* n_blocks;        // [1] or nullptr
+  int* g_cnt;           // [E*(nA+1)] global scratch when the tables do not fit in LDS
+  int* g_start;         // [E*(nA+1)]
+  int tables_in_lds;
+  int stage_inputs;
+};
+
+// LoRA shrink z = X A^T for the rows of the sorted layout (split-K partial sums).
+struct ShrinkArgs {
+  const uint16_t* X;  // gather: x [T][K]; otherwise act [cap][K]
+  const int* sorted_pairs;
+  const int* block_expert;
+  const int* n_blocks;
+  int bm;
+  const int* adapter_ids;
+  int k, nA, E, r, K, S;
+  const uint16_t* Aw;  // [nA][E][r][K]
+  float* zpart;        // [S][cap][r]
+  int64_t cap;
+};
+
+// Base GEMM of one projection for the rows of the sorted layout, with the LoRA expand (and
+// for gate_up the SiLU-and-mul) in the epilogue.
+struct GemmArgs {
+  const uint16_t* X;   // gate_up: x [T][K]; down: act [cap][K]
+  const uint16_t* W;   // gate_up: W1 [E][2I][h]; down: W2 [E][h][I]
+  const uint16_t* Bw;  // gate_up: B1 [nA][E][2I][r]; down: B2 [nA][E][h][r]
+  const float* zpart;  // [S][cap][r]
+  int S;
+  int64_t cap;
+  const int* sorted_pairs;
+  const int* block_expert;
+  const int* n_blocks;
+  const int* adapter_ids;
+  int k, nA, E, r;
+  int K;  // reduction length
+  int N;  // gate_up: I (act columns); down: h
+  uint16_t* act_out;  // gate_up: [cap][I]
+  float* d_out;       // down: [T*k][h]
+};
+
+// Host launchers (each defined next to its kernel). They return the launch status.
+hipError_t launch_route(const float* logits, int T, int E, int k, int* topk_ids, float* topk_w,
+                        int* tok_flags, hipStream_t stream);
+hipError_t launch_align(const AlignArgs& a, size_t dyn_lds, hipStream_t stream);
+hipError_t launch_shrink(bool gather, const ShrinkArgs& a, int tiles, hipStream_t stream);
+hipError_t launch_skinny(int nt, bool gateup, const GemmArgs& a, int grid_x, int grid_y,
+                         hipStream_t stream);
+hipError_t launch_combine(const float* D, const float* topk_w, int T, int k, int h, uint16_t* y,
+                          hipStream_t stream);
+
+constexpr int kAlignThreads = 1024;
+constexpr int kAlignStaticLds = 13 * 1024;  // >= the align kernel's static LDS (12.6 KB)
+constexpr int kLdsBytes = 160 * 1024;
+
+}  // namespace moelora

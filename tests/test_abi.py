@@ -1,0 +1,123 @@
+"""The C ABI library loads on a host without a GPU, exports every entry point the header
+declares, and rejects bad arguments on the host before any device call. CPU only."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import lora_mixture_experts_amd as ml
+from lora_mixture_experts_amd import Dims
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", fn)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(moe_lora_\w+)\s*\(", src))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ml.lib()
+    declared = _declared()
+    assert declared == set(ml.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_workspace_size_and_capacity():
+    d = Dims(64, 4096, 11008, 16, 8, 16)
+    n = ml.workspace_size(d, 2)
+    assert n > 2 * 128 * 11008 * 2  # at least the intermediate activations
+    assert n % 256 == 0
+    assert ml.sorted_capacity(d, 2, 1, 16) == 128 + 16 * 15
+    assert ml.sorted_capacity(d, 2, 4, 64) == 128 * 4 + 16 * 63
+    assert ml.sorted_capacity(d, 2, 0, 16) == -1
+    assert ml.sorted_capacity(d, 2, 1, 257) == -1
+
+
+@pytest.mark.parametrize("bad", [
+    dict(hidden=100), dict(inter=64 * 3), dict(rank=12), dict(n_experts=0), dict(n_experts=2000),
+    dict(n_adapters=0), dict(T=-1), dict(hidden=0),
+])
+def test_workspace_size_rejects_bad_dims(bad):
+    base = dict(T=16, hidden=256, inter=512, n_experts=8, n_adapters=4, rank=8)
+    base.update(bad)
+    assert ml.workspace_size(Dims(**base), 2) == 0
+
+
+@pytest.mark.parametrize("topk", [0, 9, 17])
+def test_workspace_size_rejects_bad_topk(topk):
+    assert ml.workspace_size(Dims(16, 256, 512, 8, 4, 8), topk) == 0
+
+
+def test_strerror_covers_codes():
+    for code in (ml.OK, ml.EINVAL_DIMS, ml.ENULL, ml.EALIGN, ml.EWORKSPACE, ml.EHIP, ml.EDEVICE):
+        assert ml.strerror(code) not in ("", "unknown error code")
+    assert ml.strerror(123) == "unknown error code"
+
+
+def _fwd(ptrs, d, topk=2, ws_bytes=None):
+    lib = ml.lib()
+    if ws_bytes is None:
+        ws_bytes = ml.workspace_size(d, topk) if ml.workspace_size(d, topk) else 1 << 40
+    return lib.moe_lora_forward(*ptrs[:9], topk, ctypes.byref(d), ptrs[9], ptrs[10], ws_bytes, None)
+
+
+FAKE = [0x10000 * (i + 1) for i in range(11)]  # aligned, never dereferenced: checks fail first
+
+
+def test_forward_host_validation_without_device():
+    d = Dims(16, 256, 512, 8, 4, 8)
+    for i in range(11):
+        p = list(FAKE)
+        p[i] = None
+        assert _fwd(p, d) == ml.ENULL
+    for i in range(10):
+        p = list(FAKE)
+        p[i] += 8
+        assert _fwd(p, d) == ml.EALIGN
+    p = list(FAKE)
+    p[10] += 16  # workspace 16- but not 256-aligned
+    assert _fwd(p, d) == ml.EWORKSPACE
+    assert _fwd(FAKE, d, ws_bytes=ml.workspace_size(d, 2) - 1) == ml.EWORKSPACE
+    assert _fwd(FAKE, Dims(16, 250, 512, 8, 4, 8)) == ml.EINVAL_DIMS
+    assert _fwd(FAKE, d, topk=9) == ml.EINVAL_DIMS
+    # T = 0 is a valid empty call: nothing is enqueued, no pointer is read, no device is needed
+    assert _fwd(FAKE, Dims(0, 256, 512, 8, 4, 8)) == ml.OK
+    assert _fwd([None] * 11, Dims(0, 256, 512, 8, 4, 8)) == ml.OK
+
+
+def test_route_align_host_validation_without_device():
+    lib = ml.lib()
+    d = Dims(16, 256, 512, 8, 4, 8)
+    ws = ml.workspace_size(d, 2)
+    cap = ml.sorted_capacity(d, 2, 1, 16)
+    p = [0x10000 * (i + 1) for i in range(9)]
+
+    def call(pp, cap_=cap, seg_pad=1, block_m=16, ws_=ws):
+        return lib.moe_lora_route_align(pp[0], pp[1], 2, ctypes.byref(d), seg_pad, block_m, pp[2], pp[3],
+                                        pp[4], cap_, pp[5], pp[6], pp[7], pp[8], ws_, None)
+
+    assert call(p, cap_=cap - 1) == ml.EINVAL_DIMS
+    assert call(p, seg_pad=0) == ml.EINVAL_DIMS
+    for i in range(9):
+        q = list(p)
+        q[i] = None
+        assert call(q) == ml.ENULL
+    q = list(p)
+    q[2] += 2
+    assert call(q) == ml.EALIGN
+    assert call(p, ws_=ws - 1) == ml.EWORKSPACE
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    x = torch.zeros(4, 128, dtype=torch.bfloat16)
+    with pytest.raises((ValueError, TypeError)):
+        ml._expect(x, "x", torch.bfloat16, (4, 128))

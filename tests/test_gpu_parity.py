@@ -1,0 +1,244 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Routing ids, slot order, sorted pairs, expert offsets and the segment table must match
+bit for bit; y must satisfy max|y - y_ref| <= 2e-2 * max|y_ref| globally and per token."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import lora_mixture_experts_amd as ml
+import oracle
+from synth import configs
+from synth.configs import Workload
+from tests.helpers import check_close, oracle_rows, sample_tokens
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _dims(w: Workload) -> ml.Dims:
+    return ml.Dims(w.T, w.hidden, w.inter, w.n_experts, w.n_adapters, w.rank)
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+# ----------------------------------------------------------------------------- route + align
+
+ROUTE_CASES = [
+    ("tiny", 1, 1), ("tiny", 4, 16), ("decode", 1, 16), ("decode", 16, 16), ("prefill", 1, 64),
+    ("prefill", 16, 128), ("fg", 1, 32), ("fg", 8, 32), ("stress_distinct", 1, 64),
+    ("stress_same", 1, 64), ("stress_distinct", 16, 256),
+]
+
+
+def _route_align_case(w: Workload, L: torch.Tensor, ad: torch.Tensor, seg_pad: int, block_m: int):
+    _say(f"route_align {w.name} T={w.T} E={w.n_experts} k={w.topk} nA={w.n_adapters} "
+         f"seg_pad={seg_pad} block_m={block_m}")
+    d = _dims(w)
+    out = ml.route_align(L.to(DEV), ad.to(DEV), w.topk, d, seg_pad, block_m)
+    torch.cuda.synchronize()
+    ids_ref, w_ref = oracle.route(L, w.topk)
+    al = oracle.align(ids_ref, ad.numpy(), w.n_experts, w.n_adapters, seg_pad, block_m)
+    np.testing.assert_array_equal(out["topk_ids"].cpu().numpy(), ids_ref)
+    np.testing.assert_allclose(out["topk_w"].cpu().numpy(), w_ref, rtol=0, atol=2e-6)
+    total = int(al["expert_offsets"][-1])
+    np.testing.assert_array_equal(out["expert_offsets"].cpu().numpy(), al["expert_offsets"])
+    sp = out["sorted_pairs"].cpu().numpy()
+    np.testing.assert_array_equal(sp[:total], al["sorted_pairs"])
+    assert np.all(sp[total:] == -7), "wrote past the padded total"
+    assert int(out["n_seg"].item()) == al["n_seg"]
+    np.testing.assert_array_equal(out["seg_table"].cpu().numpy()[: al["n_seg"]], al["seg_table"])
+    assert ml.debug_status(out["workspace"]) == 0
+
+
+@pytest.mark.parametrize("name,seg_pad,block_m", ROUTE_CASES)
+def test_route_align_bit_exact(name, seg_pad, block_m):
+    w = configs.WORKLOADS[name]
+    _route_align_case(w, configs.make_logits(w, 0), configs.make_adapter_ids(w, 0), seg_pad, block_m)
+
+
+@pytest.mark.parametrize("E,k,levels", [(8, 2, 2), (128, 8, 3), (16, 16, 1), (1, 1, 1)])
+def test_route_align_ties_and_no_adapter(E, k, levels):
+    w = Workload("ties", 300, 128, 128, E, k, 7, 8)
+    rng = np.random.default_rng(E + k)
+    L = np.round(rng.standard_normal((w.T, E)) * levels / 2) / levels
+    L = L.astype(np.float32)
+    L[L == 0] = np.where(rng.random(int((L == 0).sum())) < 0.5, -0.0, 0.0)
+    ad = rng.integers(-1, 7, w.T).astype(np.int32)
+    _route_align_case(w, torch.from_numpy(L), torch.from_numpy(ad), 4, 32)
+
+
+@pytest.mark.parametrize("T,E,k,nA", [(512, 64, 4, 1000), (20000, 16, 2, 4), (3000, 200, 6, 300)])
+def test_route_align_large_tables(T, E, k, nA):
+    """Bucket tables or staged inputs too large for LDS take the workspace path."""
+    w = Workload("big", T, 128, 128, E, k, nA, 8)
+    L = configs.make_logits(w, 3)
+    ad = torch.from_numpy(np.random.default_rng(T).integers(-1, nA, T).astype(np.int32))
+    _route_align_case(w, L, ad, 1, 64)
+
+
+def test_route_align_empty():
+    w = Workload("empty", 0, 128, 128, 8, 2, 3, 8)
+    out = ml.route_align(torch.zeros((0, 8), device=DEV), torch.zeros(0, dtype=torch.int32, device=DEV),
+                         2, _dims(w), 1, 16)
+    torch.cuda.synchronize()
+    assert out["expert_offsets"].cpu().tolist() == [0] * 9
+    assert int(out["n_seg"].item()) == 0
+
+
+# ----------------------------------------------------------------------------- forward, small shapes
+
+SMALL = {
+    "tiny": configs.WORKLOADS["tiny"],
+    "ragged": Workload("ragged", 37, 384, 640, 6, 2, 5, 16),
+    "r8_k1": Workload("r8_k1", 23, 256, 256, 4, 1, 3, 8),
+    "r32_k4": Workload("r32_k4", 50, 512, 384, 16, 4, 7, 32),
+    "r64_E1": Workload("r64_E1", 19, 256, 512, 1, 1, 3, 64),
+    "mid": Workload("mid", 200, 256, 384, 8, 2, 6, 16),
+    "fg_small": Workload("fg_small", 64, 256, 256, 32, 8, 16, 32, hot_experts=4, hot_bias=2.0),
+    "one_token": Workload("one_token", 1, 256, 384, 8, 2, 4, 16),
+}
+
+
+def _small_inputs(w: Workload, seed: int, b_scale=1.0, no_adapter_every=5):
+    inp = configs.make_inputs(w, seed, b_scale=b_scale)
+    if no_adapter_every:
+        inp["adapter_ids"][::no_adapter_every] = -1
+    return inp
+
+
+def _run(inp: dict, topk: int, workspace=None):
+    g = {k: v.to(DEV) for k, v in inp.items()}
+    y = ml.forward(g["x"], g["logits"], g["W1"], g["W2"], g["A1"], g["B1"], g["A2"], g["B2"],
+                   g["adapter_ids"], topk, workspace=workspace)
+    torch.cuda.synchronize()
+    return y
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("b_scale", [1.0, 10.0])
+def test_forward_small_vs_oracle(name, b_scale):
+    w = SMALL[name]
+    _say(f"forward {name} b_scale={b_scale}")
+    inp = _small_inputs(w, 1, b_scale)
+    y = _run(inp, w.topk)
+    y_ref = oracle_rows(inp, w.topk)
+    check_close(y, y_ref, what=f"{name} b_scale={b_scale}")
+
+
+def test_forward_all_adapters_off_and_on():
+    w = SMALL["ragged"]
+    inp = _small_inputs(w, 2, 10.0, no_adapter_every=0)
+    off = dict(inp)
+    off["adapter_ids"] = torch.full_like(inp["adapter_ids"], -1)
+    y_off = _run(off, w.topk)
+    check_close(y_off, oracle_rows(off, w.topk), what="adapters off")
+    y_on = _run(inp, w.topk)
+    ref_on = oracle_rows(inp, w.topk)
+    check_close(y_on, ref_on, what="adapters on")
+    # the LoRA terms are visible at this scale: the adapter-free output must not pass as it
+    assert np.abs(y_off.double().cpu().numpy() - ref_on).max() > 0.1 * np.abs(ref_on).max()
+
+
+def test_forward_empty_batch():
+    w = SMALL["tiny"].with_(T=0)
+    inp = configs.make_inputs(w, 0)
+    y = _run(inp, w.topk)
+    assert y.shape == (0, w.hidden)
+
+
+def test_forward_flags_bad_adapter_and_nonfinite_logit():
+    w = SMALL["ragged"]
+    inp = _small_inputs(w, 3, 10.0)
+    bad = dict(inp)
+    bad["adapter_ids"] = inp["adapter_ids"].clone()
+    bad["adapter_ids"][4] = w.n_adapters + 3
+    g = {k: v.to(DEV) for k, v in bad.items()}
+    ws = ml.new_workspace(_dims(w), w.topk, DEV)
+    y = ml.forward(g["x"], g["logits"], g["W1"], g["W2"], g["A1"], g["B1"], g["A2"], g["B2"],
+                   g["adapter_ids"], w.topk, workspace=ws)
+    assert ml.debug_status(ws) == ml.FLAG_ADAPTER_RANGE
+    as_none = dict(inp)
+    as_none["adapter_ids"] = bad["adapter_ids"].clone()
+    as_none["adapter_ids"][4] = -1
+    check_close(y, oracle_rows(as_none, w.topk), what="out-of-range adapter acts as none")
+
+    nf = dict(inp)
+    nf["logits"] = inp["logits"].clone()
+    nf["logits"][6, 1] = float("nan")
+    g = {k: v.to(DEV) for k, v in nf.items()}
+    y = ml.forward(g["x"], g["logits"], g["W1"], g["W2"], g["A1"], g["B1"], g["A2"], g["B2"],
+                   g["adapter_ids"], w.topk, workspace=ws)
+    assert ml.debug_status(ws) == ml.FLAG_NONFINITE_LOGIT
+    keep = np.array([t for t in range(w.T) if t != 6], np.int32)
+    check_close(y[torch.from_numpy(keep).long().to(DEV)], oracle_rows(inp, w.topk, keep), what="finite tokens")
+
+
+def test_forward_poisoned_workspace_and_determinism():
+    w = SMALL["fg_small"]
+    inp = _small_inputs(w, 4)
+    ws = ml.new_workspace(_dims(w), w.topk, DEV)
+    ws.fill_(0xFF)
+    y1 = _run(inp, w.topk, workspace=ws).clone()
+    ws.fill_(0x7F)
+    y2 = _run(inp, w.topk, workspace=ws).clone()
+    y3 = _run(inp, w.topk)
+    assert torch.equal(y1, y2) and torch.equal(y1, y3)
+    check_close(y1, oracle_rows(inp, w.topk), what="poisoned workspace")
+
+
+# ----------------------------------------------------------------------------- full-size configs
+
+def _full_case(name: str, seed: int = 0, b_scale: float = 1.0, n_sample: int = 12):
+    w = configs.WORKLOADS[name]
+    _say(f"full-size {name}: generating inputs on the GPU")
+    inp = configs.make_inputs(w, seed, device=DEV, b_scale=b_scale)
+    _say(f"full-size {name}: forward")
+    y = ml.forward(inp["x"], inp["logits"], inp["W1"], inp["W2"], inp["A1"], inp["B1"], inp["A2"],
+                   inp["B2"], inp["adapter_ids"], w.topk)
+    torch.cuda.synchronize()
+    toks = sample_tokens(w.T, n_sample, seed)
+    _say(f"full-size {name}: oracle on {len(toks)} tokens")
+    y_ref = oracle_rows(inp, w.topk, toks)
+    rel = check_close(y[torch.from_numpy(toks).long().to(DEV)], y_ref, what=name)
+    _say(f"full-size {name}: max rel err {rel:.2e}")
+    return inp, y
+
+
+@pytest.mark.parametrize("name", ["decode", "prefill", "fg"])
+def test_forward_full_size_sampled(name):
+    inp, y = _full_case(name)
+    # the same call again gives the same bytes
+    w = configs.WORKLOADS[name]
+    y2 = ml.forward(inp["x"], inp["logits"], inp["W1"], inp["W2"], inp["A1"], inp["B1"], inp["A2"],
+                    inp["B2"], inp["adapter_ids"], w.topk)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    del inp
+    torch.cuda.empty_cache()
+
+
+def test_forward_full_size_decode_amplified_b():
+    _full_case("decode", seed=1, b_scale=10.0)
+    torch.cuda.empty_cache()
+
+
+def test_forward_full_size_stress_distinct_and_same():
+    w = configs.WORKLOADS["stress_distinct"]
+    inp, y = _full_case("stress_distinct", n_sample=8)
+    same = dict(inp)
+    same["adapter_ids"] = configs.make_adapter_ids(configs.WORKLOADS["stress_same"], 0, DEV)
+    y_same = ml.forward(same["x"], same["logits"], same["W1"], same["W2"], same["A1"], same["B1"],
+                        same["A2"], same["B2"], same["adapter_ids"], w.topk)
+    torch.cuda.synchronize()
+    toks = sample_tokens(w.T, 8, 1)
+    check_close(y_same[torch.from_numpy(toks).long().to(DEV)], oracle_rows(same, w.topk, toks),
+                what="stress_same")
+    del inp, same
+    torch.cuda.empty_cache()
