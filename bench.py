@@ -1,0 +1,218 @@
+#!/usr/bin/env python3
+"""Throughput of the fused MoE + multi-LoRA layer on one MI355X.
+
+One step = one call of moe_lora_forward (route, align, LoRA shrink, gate_up GEMM with LoRA
+expand and SiLU-and-mul, LoRA shrink, down GEMM with LoRA expand, combine) over one batch of
+seeded synthetic input already resident in HBM. Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+
+
+def algorithmic_work(w, seg_table, n_seg, topk_ids):
+    """Bytes and flops the method must move / compute for this routing (no padding, no
+    intermediates): touched expert weights, touched (expert, adapter) LoRA weights, x,
+    logits, adapter ids, y. Also the gate_up kernel's own share."""
+    import numpy as np
+    ids = topk_ids.cpu().numpy()
+    seg = seg_table.cpu().numpy()[:n_seg]
+    h, I, r, T, E, k = w.hidden, w.inter, w.rank, w.T, w.n_experts, w.topk
+    n_exp = len(np.unique(ids))
+    n_ea = int((seg[:, 1] >= 0).sum())  # (expert, adapter) segments that carry an adapter
+    P = T * k
+    pairs_with_adapter = int(seg[seg[:, 1] >= 0, 3].sum())
+    layer_bytes = (n_exp * 3 * h * I * 2 + n_ea * r * (2 * h + 3 * I) * 2
+                   + 2 * T * h + 4 * T * E + 4 * T + 2 * T * h)
+    layer_flops = 2 * P * 3 * h * I + 2 * pairs_with_adapter * r * (2 * h + 3 * I)
+    gateup_bytes = (n_exp * 2 * I * h * 2 + n_ea * 2 * I * r * 2 + 2 * T * h + 2 * P * I
+                    + 4 * pairs_with_adapter * r)
+    gateup_flops = 2 * P * 2 * I * h + 2 * pairs_with_adapter * 2 * I * r
+    return dict(n_experts_touched=n_exp, n_expert_adapter=n_ea, layer_bytes=layer_bytes,
+                layer_flops=layer_flops, gateup_bytes=gateup_bytes, gateup_flops=gateup_flops)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "lora_mixture_experts_amd", "csrc")
+    for fn in sorted(os.listdir(csrc)):
+        if fn.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, fn), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per gate_up launch from the committed rocprofv3 counter summary, or None when
+    the summary is missing or was taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_gate_up_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, inp, n_tokens: int):
+    """The oracle, as it stands, on a bounded sample of the same workload (host copies made
+    before timing)."""
+    import numpy as np
+    import torch
+    import oracle
+    toks = np.linspace(0, w.T - 1, num=min(n_tokens, w.T)).round().astype(np.int32)
+    toks = np.unique(toks)
+    tok_t = torch.from_numpy(toks.astype(np.int64)).to(inp["x"].device)
+    ad = inp["adapter_ids"].index_select(0, tok_t).cpu().numpy()
+    used = sorted({int(a) for a in ad if a >= 0}) or [0]
+    remap = {a: i for i, a in enumerate(used)}
+    used_t = torch.tensor(used, dtype=torch.int64, device=inp["x"].device)
+    host = {"x": inp["x"].index_select(0, tok_t).cpu(), "logits": inp["logits"].index_select(0, tok_t).cpu(),
+            "adapter_ids": np.array([remap.get(int(a), -1) for a in ad], np.int32),
+            "W1": inp["W1"].cpu(), "W2": inp["W2"].cpu()}
+    for n in ("A1", "B1", "A2", "B2"):
+        host[n] = inp[n].index_select(0, used_t).cpu()
+    t0 = time.perf_counter()
+    oracle.forward(host, w.topk)
+    dt = time.perf_counter() - t0
+    return {"value": len(toks) / dt, "unit": "tokens/s", "cores": min(oracle.num_threads(), len(toks)),
+            "kind": "oracle",
+            "sample": f"{len(toks)} of {w.T} tokens of the {w.name} batch, fp64 C oracle with OpenMP "
+                      f"over tokens, inputs already in host memory; {dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "prefill", "fg", "stress_distinct", "stress_same", "tiny"])
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-tokens", type=int, default=64, help="oracle sample size (tokens)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run a device-to-device copy of this size first (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the layer runs on a single MI355X here; "
+              "multi-GPU (expert-parallel) runs are not part of this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import lora_mixture_experts_amd as ml
+    from synth import configs
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    w = configs.WORKLOADS[args.workload]
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    inp = configs.make_inputs(w, args.seed, device=dev)
+    d = ml.dims_of(inp["x"], inp["W1"], inp["A1"])
+    ws = ml.new_workspace(d, w.topk, dev)
+    y = torch.empty((w.T, w.hidden), dtype=torch.bfloat16, device=dev)
+
+    ra = ml.route_align(inp["logits"], inp["adapter_ids"], w.topk, d, 1, 1, workspace=ws)
+    work = algorithmic_work(w, ra["seg_table"], int(ra["n_seg"].item()), ra["topk_ids"])
+    del ra
+
+    def step(events=None):
+        ml.forward(inp["x"], inp["logits"], inp["W1"], inp["W2"], inp["A1"], inp["B1"], inp["A2"],
+                   inp["B2"], inp["adapter_ids"], w.topk, y=y, workspace=ws, stage_events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(ml.N_STAGES + 1)] for _ in range(K)]
+    for evs in events:  # create the HIP events outside the timed region
+        for ev in evs:
+            ev.record()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    stage_ms = {name: [] for name in ml.STAGES}
+    step_ms = []
+    for evs in events:
+        for s, name in enumerate(ml.STAGES):
+            stage_ms[name].append(evs[s].elapsed_time(evs[s + 1]))
+        step_ms.append(evs[0].elapsed_time(evs[-1]))
+    stage_avg = {k: statistics.fmean(v) for k, v in stage_ms.items()}
+
+    ms_per_step = elapsed * 1e3 / K
+    value = w.T * K / elapsed
+    prefill_like = args.workload == "prefill"
+    gu_s = stage_avg["gate_up"] * 1e-3
+    if prefill_like:
+        achieved = work["gateup_flops"] / gu_s / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / BF16_PEAK_TFLOPS}
+    else:
+        achieved = work["gateup_bytes"] / gu_s / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS}
+    roof["kernel"] = "skinny_gemm_kernel (gate_up)"
+    roof["traffic"] = measured_traffic(args.workload)
+
+    layer_s = statistics.median(step_ms) * 1e-3
+    out = {
+        "metric": "tokens/s of fused MoE-LoRA layer",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "hidden": w.hidden, "inter": w.inter,
+                   "n_experts": w.n_experts, "topk": w.topk, "n_adapters": w.n_adapters,
+                   "rank": w.rank, "adapters": w.adapters, "seed": args.seed},
+        "roofline": roof,
+        "layer": {"bytes": work["layer_bytes"], "flops": work["layer_flops"],
+                  "median_ms": layer_s * 1e3,
+                  "hbm_frac": work["layer_bytes"] / layer_s / 1e9 / HBM_PEAK_GBS,
+                  "mfma_frac": work["layer_flops"] / layer_s / 1e12 / BF16_PEAK_TFLOPS},
+        "stages_ms": {k: round(v, 4) for k, v in stage_avg.items()},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

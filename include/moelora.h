@@ -81,6 +81,22 @@ int moe_lora_forward(const void *x, const float *router_logits, const void *W1, 
                      const int32_t *adapter_ids, int32_t topk, const moe_lora_dims *d, void *y,
                      void *workspace, size_t workspace_bytes, void *stream);
 
+/* Stages of moe_lora_forward, in launch order: 0 route, 1 align, 2 gate_up LoRA shrink,
+ * 3 gate_up GEMM (+ LoRA expand, SiLU-and-mul), 4 down LoRA shrink, 5 down GEMM (+ LoRA
+ * expand), 6 combine. */
+#define MOELORA_N_STAGES 7
+
+/* moe_lora_forward for measurement: additionally records stage_events[i] (caller-created
+ * hipEvent_t handles, MOELORA_N_STAGES + 1 of them) on `stream` right before stage i and
+ * stage_events[MOELORA_N_STAGES] after the last stage, so the elapsed time between events i
+ * and i+1 is stage i. Same results and errors as moe_lora_forward; MOELORA_ENULL when
+ * stage_events or one of its entries is NULL. With T = 0 no event is recorded. */
+int moe_lora_forward_timed(const void *x, const float *router_logits, const void *W1,
+                           const void *W2, const void *A1, const void *B1, const void *A2,
+                           const void *B2, const int32_t *adapter_ids, int32_t topk,
+                           const moe_lora_dims *d, void *y, void *workspace,
+                           size_t workspace_bytes, void *stream, void *const *stage_events);
+
 /* Upper bound on the padded sorted-pair length for (seg_pad, block_m):
  * T*topk*seg_pad + n_experts*(block_m-1), or -1 for invalid arguments. */
 int64_t moe_lora_sorted_capacity(const moe_lora_dims *d, int32_t topk, int32_t seg_pad,

@@ -19,8 +19,11 @@ LIB_PATH = os.path.join(_PKG, "libmoelora.so")
 OK, EINVAL_DIMS, ENULL, EALIGN, EWORKSPACE, EHIP, EDEVICE = 0, -1, -2, -3, -4, -5, -6
 FLAG_NONFINITE_LOGIT, FLAG_ADAPTER_RANGE = 1, 2
 
-EXPORTS = ("moe_lora_workspace_size", "moe_lora_forward", "moe_lora_sorted_capacity",
-           "moe_lora_route_align", "moe_lora_strerror", "moe_lora_debug_status")
+EXPORTS = ("moe_lora_workspace_size", "moe_lora_forward", "moe_lora_forward_timed",
+           "moe_lora_sorted_capacity", "moe_lora_route_align", "moe_lora_strerror",
+           "moe_lora_debug_status")
+N_STAGES = 7
+STAGES = ("route", "align", "shrink_gate_up", "gate_up", "shrink_down", "down", "combine")
 
 
 class MoeLoraError(RuntimeError):
@@ -49,6 +52,9 @@ def lib() -> ctypes.CDLL:
         L.moe_lora_workspace_size.restype = ctypes.c_size_t
         L.moe_lora_forward.argtypes = [P, P, P, P, P, P, P, P, P, i32, D, P, P, ctypes.c_size_t, P]
         L.moe_lora_forward.restype = ctypes.c_int
+        L.moe_lora_forward_timed.argtypes = [P, P, P, P, P, P, P, P, P, i32, D, P, P, ctypes.c_size_t, P,
+                                             ctypes.POINTER(ctypes.c_void_p)]
+        L.moe_lora_forward_timed.restype = ctypes.c_int
         L.moe_lora_sorted_capacity.argtypes = [D, i32, i32, i32]
         L.moe_lora_sorted_capacity.restype = i64
         L.moe_lora_route_align.argtypes = [P, P, i32, D, i32, i32, P, P, P, i64, P, P, P, P,
@@ -115,8 +121,11 @@ def _expect(t: torch.Tensor, name: str, dtype, shape):
 
 
 def forward(x, router_logits, W1, W2, A1, B1, A2, B2, adapter_ids, topk: int, y=None,
-            workspace=None) -> torch.Tensor:
-    """y[T][h] (bf16) of the fused MoE + multi-LoRA layer; see include/moelora.h."""
+            workspace=None, stage_events=None) -> torch.Tensor:
+    """y[T][h] (bf16) of the fused MoE + multi-LoRA layer; see include/moelora.h.
+
+    stage_events: optional list of N_STAGES + 1 torch.cuda.Event(enable_timing=True) that the
+    library records at the stage boundaries on the current stream (moe_lora_forward_timed)."""
     d = dims_of(x, W1, A1)
     T, h, I, E, nA, r = d.T, d.hidden, d.inter, d.n_experts, d.n_adapters, d.rank
     bf = torch.bfloat16
@@ -134,11 +143,19 @@ def forward(x, router_logits, W1, W2, A1, B1, A2, B2, adapter_ids, topk: int, y=
     _expect(y, "y", bf, (T, h))
     if workspace is None:
         workspace = new_workspace(d, topk, x.device)
-    rc = lib().moe_lora_forward(_ptr(x), _ptr(router_logits), _ptr(W1), _ptr(W2), _ptr(A1),
-                                _ptr(B1), _ptr(A2), _ptr(B2), _ptr(adapter_ids), topk,
-                                ctypes.byref(d), _ptr(y), _ptr(workspace), workspace.numel(),
-                                _stream(x.device))
-    _check(rc, "moe_lora_forward")
+    args = (_ptr(x), _ptr(router_logits), _ptr(W1), _ptr(W2), _ptr(A1), _ptr(B1), _ptr(A2), _ptr(B2),
+            _ptr(adapter_ids), topk, ctypes.byref(d), _ptr(y), _ptr(workspace), workspace.numel(),
+            _stream(x.device))
+    if stage_events is None:
+        _check(lib().moe_lora_forward(*args), "moe_lora_forward")
+    else:
+        if len(stage_events) != N_STAGES + 1:
+            raise ValueError(f"need {N_STAGES + 1} events")
+        for ev in stage_events:
+            if not ev.cuda_event:  # torch creates the HIP event on its first record
+                ev.record()
+        handles = (ctypes.c_void_p * (N_STAGES + 1))(*[ev.cuda_event for ev in stage_events])
+        _check(lib().moe_lora_forward_timed(*args, handles), "moe_lora_forward_timed")
     return y
 
 

@@ -141,10 +141,19 @@ const char* moe_lora_strerror(int code) {
   }
 }
 
-int moe_lora_forward(const void* x, const float* router_logits, const void* W1, const void* W2,
-                     const void* A1, const void* B1, const void* A2, const void* B2,
-                     const int32_t* adapter_ids, int32_t topk, const moe_lora_dims* d, void* y,
-                     void* workspace, size_t workspace_bytes, void* stream_) {
+}  // extern "C"
+
+namespace {
+
+// Records stage boundary i on the stream when the caller asked for timing events.
+bool mark(void* const* ev, int i, hipStream_t s) {
+  return !ev || hipEventRecord((hipEvent_t)ev[i], s) == hipSuccess;
+}
+
+int forward_impl(const void* x, const float* router_logits, const void* W1, const void* W2,
+                 const void* A1, const void* B1, const void* A2, const void* B2,
+                 const int32_t* adapter_ids, int32_t topk, const moe_lora_dims* d, void* y,
+                 void* workspace, size_t workspace_bytes, void* stream_, void* const* ev) {
   int rc = validate_dims(d, topk);
   if (rc != MOELORA_OK) return rc;
   if (d->T == 0) return MOELORA_OK;  // empty batch: nothing to do, pointers may be NULL
@@ -175,8 +184,10 @@ int moe_lora_forward(const void* x, const float* router_logits, const void* W1, 
   uint16_t* act = (uint16_t*)(ws + L.act);
   float* dpair = (float*)(ws + L.dpair);
 
+  if (!mark(ev, 0, stream)) return MOELORA_EHIP;
   if (launch_route(router_logits, T, E, topk, topk_ids, topk_w, tok_flags, stream) != hipSuccess)
     return MOELORA_EHIP;
+  if (!mark(ev, 1, stream)) return MOELORA_EHIP;
 
   const int nt = pick_nt(P, E);
   const int bm = 16 * nt;
@@ -201,6 +212,7 @@ int moe_lora_forward(const void* x, const float* router_logits, const void* W1, 
   al.g_start = (int*)(ws + L.align_start);
   const size_t lds = align_lds_plan(T, topk, E, nA, &al);
   if (launch_align(al, lds, stream) != hipSuccess) return MOELORA_EHIP;
+  if (!mark(ev, 2, stream)) return MOELORA_EHIP;
 
   const int64_t max_rows = P + (int64_t)E * (bm - 1);
   const int max_blocks = (int)((max_rows + bm - 1) / bm);
@@ -239,6 +251,7 @@ int moe_lora_forward(const void* x, const float* router_logits, const void* W1, 
   sh.S = s1;
   sh.zpart = z1;
   if (launch_shrink(true, sh, tiles16, stream) != hipSuccess) return MOELORA_EHIP;
+  if (!mark(ev, 3, stream)) return MOELORA_EHIP;
   g.X = (const uint16_t*)x;
   g.W = (const uint16_t*)W1;
   g.Bw = (const uint16_t*)B1;
@@ -247,6 +260,7 @@ int moe_lora_forward(const void* x, const float* router_logits, const void* W1, 
   g.K = h;
   g.N = I;
   if (launch_skinny(nt, true, g, (I + 63) / 64, max_blocks, stream) != hipSuccess) return MOELORA_EHIP;
+  if (!mark(ev, 4, stream)) return MOELORA_EHIP;
 
   // down: shrink z2 = act A2, then W2 GEMM + z2 B2 -> D (fp32, pair order)
   sh.X = act;
@@ -255,6 +269,7 @@ int moe_lora_forward(const void* x, const float* router_logits, const void* W1, 
   sh.S = s2;
   sh.zpart = z2;
   if (launch_shrink(false, sh, tiles16, stream) != hipSuccess) return MOELORA_EHIP;
+  if (!mark(ev, 5, stream)) return MOELORA_EHIP;
   g.X = act;
   g.W = (const uint16_t*)W2;
   g.Bw = (const uint16_t*)B2;
@@ -263,10 +278,36 @@ int moe_lora_forward(const void* x, const float* router_logits, const void* W1, 
   g.K = I;
   g.N = h;
   if (launch_skinny(nt, false, g, (h + 63) / 64, max_blocks, stream) != hipSuccess) return MOELORA_EHIP;
+  if (!mark(ev, 6, stream)) return MOELORA_EHIP;
 
   // weighted top-k combine -> y (bf16)
   if (launch_combine(dpair, topk_w, T, topk, h, (uint16_t*)y, stream) != hipSuccess) return MOELORA_EHIP;
+  if (!mark(ev, 7, stream)) return MOELORA_EHIP;
   return MOELORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_lora_forward(const void* x, const float* router_logits, const void* W1, const void* W2,
+                     const void* A1, const void* B1, const void* A2, const void* B2,
+                     const int32_t* adapter_ids, int32_t topk, const moe_lora_dims* d, void* y,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  return forward_impl(x, router_logits, W1, W2, A1, B1, A2, B2, adapter_ids, topk, d, y, workspace,
+                      workspace_bytes, stream, nullptr);
+}
+
+int moe_lora_forward_timed(const void* x, const float* router_logits, const void* W1,
+                           const void* W2, const void* A1, const void* B1, const void* A2,
+                           const void* B2, const int32_t* adapter_ids, int32_t topk,
+                           const moe_lora_dims* d, void* y, void* workspace,
+                           size_t workspace_bytes, void* stream, void* const* stage_events) {
+  if (!stage_events) return MOELORA_ENULL;
+  for (int i = 0; i <= MOELORA_N_STAGES; ++i)
+    if (!stage_events[i]) return MOELORA_ENULL;
+  return forward_impl(x, router_logits, W1, W2, A1, B1, A2, B2, adapter_ids, topk, d, y, workspace,
+                      workspace_bytes, stream, stage_events);
 }
 
 int moe_lora_route_align(const float* router_logits, const int32_t* adapter_ids, int32_t topk,
