@@ -1,5 +1,7 @@
 // C ABI of libmoelora: argument validation, workspace carve-up and the launch sequence of the
 // fused MoE + multi-LoRA layer (declared in include/moelora.h).
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "common.h"
@@ -10,7 +12,8 @@ using namespace moelora;
 
 namespace {
 
-constexpr int kMaxBM = 256;  // largest row block any GEMM path uses
+constexpr int kMaxBM = 256;      // largest row block any GEMM path uses
+constexpr int kMaxDownSplit = 2;  // K splits of the skinny down GEMM
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 int64_t round_up64(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
@@ -27,6 +30,10 @@ int validate_dims(const moe_lora_dims* d, int32_t topk) {
   const int64_t P = (int64_t)d->T * topk;
   if (P + (int64_t)d->n_experts * kMaxBM >= ((int64_t)1 << 30)) return MOELORA_EINVAL_DIMS;
   if ((int64_t)d->n_experts * (d->n_adapters + 1) >= ((int64_t)1 << 28)) return MOELORA_EINVAL_DIMS;
+  // x and the intermediate activations are read with 32-bit buffer offsets (< 2 GiB each)
+  if ((int64_t)d->T * d->hidden * 2 >= ((int64_t)1 << 31)) return MOELORA_EINVAL_DIMS;
+  if ((P + (int64_t)d->n_experts * kMaxBM) * d->inter * 2 >= ((int64_t)1 << 31))
+    return MOELORA_EINVAL_DIMS;
   return MOELORA_OK;
 }
 
@@ -72,6 +79,55 @@ int pick_nt(int64_t P, int E) {
   return 4;
 }
 
+bool skinny_instantiated(const SkinnyConfig& c, bool gateup) {
+  static const int have[][5] = {{1, 4, 1, 1, 0}, {1, 4, 1, 0, 0}, {1, 4, 2, 1, 0}, {1, 4, 2, 0, 0},
+                                {1, 8, 1, 1, 0}, {1, 8, 1, 0, 0}, {2, 4, 1, 1, 0}, {2, 8, 1, 1, 0},
+                                {4, 4, 1, 1, 0}, {1, 4, 1, 1, 1}, {1, 4, 1, 0, 1}, {1, 8, 1, 1, 1},
+                                {1, 8, 1, 0, 1}};
+  if (c.split && !gateup) return false;
+  for (const auto& h : have)
+    if (h[0] == c.nt && h[1] == c.p && h[2] == c.rt && h[3] == c.pipe && h[4] == c.split) return true;
+  return false;
+}
+
+// Tile shapes of the two skinny GEMMs and the down split. MOELORA_SKINNY_CFG=
+// "pg,rg,pipe_g,split_g,pd,rd,pipe_d,ks" overrides them for experiments (ignored when the
+// combination is not compiled or not valid for the sizes).
+struct SkinnyPlan {
+  SkinnyConfig gu, dn;
+  int ksplit;
+};
+
+SkinnyPlan pick_skinny(int nt, int h, int I) {
+  SkinnyPlan pl;
+  // measured on decode (16 experts, ~8 rows each): gate_up keeps gate and up rows in one
+  // wavefront; down streams two row tiles per wavefront and splits K in two
+  pl.gu = SkinnyConfig{nt, 4, 1, 1, 0};
+  pl.dn = SkinnyConfig{nt, 4, nt == 1 ? 2 : 1, 1, 0};
+  pl.ksplit = 2;
+  static int ov[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  static bool parsed = false;
+  if (!parsed) {
+    const char* env = getenv("MOELORA_SKINNY_CFG");
+    if (env)
+      sscanf(env, "%d,%d,%d,%d,%d,%d,%d,%d", &ov[0], &ov[1], &ov[2], &ov[3], &ov[4], &ov[5], &ov[6],
+             &ov[7]);
+    parsed = true;
+  }
+  if (ov[0]) {
+    const SkinnyConfig gu{nt, ov[0], ov[1], ov[2], ov[3]}, dn{nt, ov[4], ov[5], ov[6], 0};
+    const bool ok = skinny_instantiated(gu, true) && skinny_instantiated(dn, false) &&
+                    h % (32 * gu.p) == 0 && I % (32 * dn.p) == 0 && I % (32 * gu.rt) == 0 &&
+                    h % (16 * dn.rt) == 0 && ov[7] >= 1 && ov[7] <= kMaxDownSplit;
+    if (ok) {
+      pl.gu = gu;
+      pl.dn = dn;
+      pl.ksplit = ov[7];
+    }
+  }
+  return pl;
+}
+
 int pick_splits(int64_t tiles, int K) {
   int s = (int)((1024 + tiles - 1) / (tiles > 0 ? tiles : 1));
   s = s < 1 ? 1 : (s > kMaxSplit ? kMaxSplit : s);
@@ -105,7 +161,7 @@ bool moelora_make_layout(int T, int h, int I, int E, int nA, int r, int topk, Mo
   L->z1 = take(4 * (size_t)kMaxSplit * L->cap * r);
   L->z2 = take(4 * (size_t)kMaxSplit * L->cap * r);
   L->act = take(2 * (size_t)L->cap * I);
-  L->dpair = take(4 * (size_t)P * h);
+  L->dpair = take(4 * (size_t)kMaxDownSplit * P * h);
   L->align_cnt = take(4 * (size_t)E * (nA + 1));
   L->align_start = take(4 * (size_t)E * (nA + 1));
   L->total = off;
@@ -246,6 +302,7 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
 
   // gate_up: shrink z1 = x A1, then W1 GEMM + z1 B1 + SiLU-and-mul -> act
   sh.X = (const uint16_t*)x;
+  sh.x_bytes = (uint32_t)((size_t)T * h * 2);
   sh.Aw = (const uint16_t*)A1;
   sh.K = h;
   sh.S = s1;
@@ -253,17 +310,22 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   if (launch_shrink(true, sh, tiles16, stream) != hipSuccess) return MOELORA_EHIP;
   if (!mark(ev, 3, stream)) return MOELORA_EHIP;
   g.X = (const uint16_t*)x;
+  g.x_bytes = (uint32_t)((size_t)T * h * 2);
   g.W = (const uint16_t*)W1;
   g.Bw = (const uint16_t*)B1;
   g.zpart = z1;
   g.S = s1;
   g.K = h;
   g.N = I;
-  if (launch_skinny(nt, true, g, (I + 63) / 64, max_blocks, stream) != hipSuccess) return MOELORA_EHIP;
+  const SkinnyPlan plan = pick_skinny(nt, h, I);
+  g.ksplit = 1;
+  g.d_split_stride = P * (int64_t)h;
+  if (launch_skinny(plan.gu, true, g, max_blocks, stream) != hipSuccess) return MOELORA_EHIP;
   if (!mark(ev, 4, stream)) return MOELORA_EHIP;
 
   // down: shrink z2 = act A2, then W2 GEMM + z2 B2 -> D (fp32, pair order)
   sh.X = act;
+  sh.x_bytes = (uint32_t)((size_t)L.cap * I * 2);
   sh.Aw = (const uint16_t*)A2;
   sh.K = I;
   sh.S = s2;
@@ -271,17 +333,21 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   if (launch_shrink(false, sh, tiles16, stream) != hipSuccess) return MOELORA_EHIP;
   if (!mark(ev, 5, stream)) return MOELORA_EHIP;
   g.X = act;
+  g.x_bytes = (uint32_t)((size_t)L.cap * I * 2);
   g.W = (const uint16_t*)W2;
   g.Bw = (const uint16_t*)B2;
   g.zpart = z2;
   g.S = s2;
   g.K = I;
   g.N = h;
-  if (launch_skinny(nt, false, g, (h + 63) / 64, max_blocks, stream) != hipSuccess) return MOELORA_EHIP;
+  g.ksplit = plan.ksplit;
+  if (launch_skinny(plan.dn, false, g, max_blocks, stream) != hipSuccess) return MOELORA_EHIP;
   if (!mark(ev, 6, stream)) return MOELORA_EHIP;
 
   // weighted top-k combine -> y (bf16)
-  if (launch_combine(dpair, topk_w, T, topk, h, (uint16_t*)y, stream) != hipSuccess) return MOELORA_EHIP;
+  if (launch_combine(dpair, plan.ksplit, P * (int64_t)h, topk_w, T, topk, h, (uint16_t*)y, stream) !=
+      hipSuccess)
+    return MOELORA_EHIP;
   if (!mark(ev, 7, stream)) return MOELORA_EHIP;
   return MOELORA_OK;
 }

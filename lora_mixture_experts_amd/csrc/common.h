@@ -48,6 +48,17 @@ __device__ __forceinline__ u32x4 ldg16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+// Raw buffer loads: a load whose byte offset is at or past the buffer's size returns zeros
+// and touches no memory, so padding lanes can take part in a load without a branch.
+constexpr uint32_t kOutOfRange = 0x80000000u;  // offsets of padding lanes (buffers < 2 GiB)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4 bufld16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0);
+}
+
 __device__ __forceinline__ uint64_t lanemask_lt() {
   return (1ull << (threadIdx.x & 63)) - 1ull;
 }

@@ -39,7 +39,8 @@ __device__ __forceinline__ float dot8_bf16(const float* z, u32x4 v) {
   return s;
 }
 
-// out[v] += sum_q z[q] * Brow_v[q] for the 4 rows at Bbase + v*r (r multiple of 8).
+// out[v] += sum_q z[q] * Brow_v[q] for the 4 rows at Bbase + v*r (r multiple of 8); z is the
+// sum of the S split-K partials of the LoRA shrink, added in split order.
 __device__ __forceinline__ void lora_expand4(const float* __restrict__ zrow, int64_t zstride, int S,
                                              const uint16_t* __restrict__ Bbase, int r, float* out) {
   for (int q0 = 0; q0 < r; q0 += 8) {
@@ -47,41 +48,70 @@ __device__ __forceinline__ void lora_expand4(const float* __restrict__ zrow, int
 #pragma unroll
     for (int qq = 0; qq < 8; ++qq) z[qq] = 0.f;
     for (int s = 0; s < S; ++s) {
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(zrow + s * zstride + q0);
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(zrow + s * zstride + q0 + 4);
 #pragma unroll
-      for (int qq = 0; qq < 8; ++qq) z[qq] += zrow[s * zstride + q0 + qq];
+      for (int qq = 0; qq < 4; ++qq) {
+        z[qq] += lo[qq];
+        z[4 + qq] += hi[qq];
+      }
     }
 #pragma unroll
     for (int v = 0; v < 4; ++v) out[v] += dot8_bf16(z, ldg16(Bbase + (size_t)v * r + q0));
   }
 }
 
-template <int NT, bool GATEUP>
+// NT: 16-row token tiles per row block (BM = 16*NT). P: 16-byte loads per lane per weight row
+// and K step (K step = 32*P). RT: 16-row output tiles per wave (per projection for gate_up).
+// Down may split K over gridDim.z: split z writes its partial sums to its own D buffer and only
+// split 0 adds the LoRA term; the combine adds the splits in order.
+// PIPE: two register sets alternate so the next step's loads overlap the current MFMAs;
+// otherwise each step loads then computes and latency is hidden by other wavefronts only.
+// SPLIT (gate_up only, RT = 1): waves 0-1 stream gate rows and waves 2-3 the matching up rows,
+// one weight tile per wave; the up accumulators reach the gate waves through LDS.
+template <int NT, bool GATEUP, int P, int RT, bool PIPE, bool SPLIT>
 __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs a) {
-  constexpr int NW = GATEUP ? 2 : 1;
+  static_assert(!SPLIT || (GATEUP && RT == 1), "SPLIT is a gate_up mode with one tile per wave");
+  constexpr int NW = SPLIT ? 1 : (GATEUP ? 2 : 1) * RT;
   constexpr int BM = 16 * NT;
+  constexpr int KS = 32 * P;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n0 = (blockIdx.x * 4 + wave) * 16;
-  if (n0 >= a.N) return;
+  const int n0 = SPLIT ? (blockIdx.x * 2 + (wave & 1)) * 16 : (blockIdx.x * 4 + wave) * 16 * RT;
+  const bool up_wave = SPLIT && wave >= 2;
+  __shared__ f32x4 s_up[SPLIT ? 2 * 64 * NT : 1];
+  if (n0 >= a.N) return;  // never taken with SPLIT (N % 32 == 0 and an exact grid)
   const int blk = blockIdx.y;
   if (blk >= *a.n_blocks) return;
+  const int zsplit = blockIdx.z;
   const int e = a.block_expert[blk];
   const int m = lane & 15, kq = lane >> 4;
   const int K = a.K;
   const size_t N = (size_t)a.N;
+  const int nks = K / KS;
+  const int ks0 = (nks * zsplit) / a.ksplit, ks1 = (nks * (zsplit + 1)) / a.ksplit;
 
   const uint16_t* wp[NW];
-  if (GATEUP) {
-    wp[0] = a.W + ((size_t)e * 2 * N + n0 + m) * K;
-    wp[NW - 1] = a.W + ((size_t)e * 2 * N + N + n0 + m) * K;
-  } else {
-    wp[0] = a.W + ((size_t)e * N + n0 + m) * K;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    if (SPLIT) {
+      wp[0] = a.W + ((size_t)e * 2 * N + (up_wave ? N : 0) + n0 + m) * K;
+    } else if (GATEUP) {
+      wp[rt] = a.W + ((size_t)e * 2 * N + n0 + 16 * rt + m) * K;
+      wp[NW - RT + rt] = a.W + ((size_t)e * 2 * N + N + n0 + 16 * rt + m) * K;
+    } else {
+      wp[rt] = a.W + ((size_t)e * N + n0 + 16 * rt + m) * K;
+    }
   }
-  const uint16_t* xp[NT];
+  // Token rows, read with buffer loads: a padding row (pair -1) gets an out-of-range offset and
+  // loads zeros without touching memory. Every load stays unconditional, which keeps the
+  // compiler's count of outstanding loads exact, so the prefetch below overlaps the MFMAs.
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.X, a.x_bytes);
+  uint32_t xo[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int row = blk * BM + nt * 16 + m;
     const int p = a.sorted_pairs[row];
-    xp[nt] = p < 0 ? nullptr : (GATEUP ? a.X + (size_t)(p / a.k) * K : a.X + (size_t)row * K);
+    xo[nt] = p < 0 ? kOutOfRange : (uint32_t)((GATEUP ? (size_t)(p / a.k) : (size_t)row) * K * 2);
   }
 
   f32x4 acc[NW][NT];
@@ -90,109 +120,143 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[w][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nks = K / 128;
-  int kb = kq * 32;
-  u32x4 wc[NW][4], xc[NT][4];
-#pragma unroll
-  for (int w = 0; w < NW; ++w)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) wc[w][j] = ldg16(wp[w] + kb + 8 * j);
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) xc[nt][j] = xp[nt] ? ldg16(xp[nt] + kb + 8 * j) : u32x4{0u, 0u, 0u, 0u};
-
-  for (int ks = 0; ks < nks; ++ks) {
-    const bool more = ks + 1 < nks;
-    const int kn = kb + 128;
-    u32x4 wn[NW][4], xn[NT][4];
-    if (more) {
-#pragma unroll
-      for (int w = 0; w < NW; ++w)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) wn[w][j] = ldg16(wp[w] + kn + 8 * j);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          xn[nt][j] = xp[nt] ? ldg16(xp[nt] + kn + 8 * j) : u32x4{0u, 0u, 0u, 0u};
+  // Two register sets alternate (ping-pong): while one step's MFMAs run, the next step's loads
+  // are in flight. Loads are never conditional: past the last step they re-read the last step
+  // (L2 hits, results unused), so the compiler's outstanding-load count stays exact and its
+  // wait before each compute covers only the older set.
+  u32x4 wa[NW][P], xa[NT][P], wb[NW][P], xb[NT][P];
+#define MOELORA_LOAD(W_, X_, KB_)                                              \
+  do {                                                                         \
+    _Pragma("unroll") for (int w = 0; w < NW; ++w)                             \
+      _Pragma("unroll") for (int j = 0; j < P; ++j)                            \
+        W_[w][j] = ldg16(wp[w] + (KB_) + 8 * j);                               \
+    _Pragma("unroll") for (int nt = 0; nt < NT; ++nt)                          \
+      _Pragma("unroll") for (int j = 0; j < P; ++j)                            \
+        X_[nt][j] = bufld16(xr, xo[nt] + 2u * (uint32_t)((KB_) + 8 * j));      \
+  } while (0)
+#define MOELORA_COMPUTE(W_, X_)                                                \
+  do {                                                                         \
+    _Pragma("unroll") for (int j = 0; j < P; ++j)                              \
+      _Pragma("unroll") for (int w = 0; w < NW; ++w)                           \
+        _Pragma("unroll") for (int nt = 0; nt < NT; ++nt)                      \
+          acc[w][nt] = mfma16(W_[w][j], X_[nt][j], acc[w][nt]);                \
+  } while (0)
+  const int nsteps = ks1 - ks0;
+  if (!PIPE) {
+    for (int i = 0; i < nsteps; ++i) {
+      const int kb = (ks0 + i) * KS + kq * (8 * P);
+      MOELORA_LOAD(wa, xa, kb);
+      MOELORA_COMPUTE(wa, xa);
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int w = 0; w < NW; ++w)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[w][nt] = mfma16(wc[w][j], xc[nt][j], acc[w][nt]);
-    if (more) {
-#pragma unroll
-      for (int w = 0; w < NW; ++w)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) wc[w][j] = wn[w][j];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) xc[nt][j] = xn[nt][j];
+  } else if (nsteps > 0) {
+    const int kb0 = ks0 * KS + kq * (8 * P);
+    MOELORA_LOAD(wa, xa, kb0);
+    for (int i = 0; i < nsteps; i += 2) {
+      // sched_barrier(0) keeps the compiler from interleaving the phases (which would bring
+      // the waits for the in-flight set back in front of the MFMAs)
+      MOELORA_LOAD(wb, xb, kb0 + min(i + 1, nsteps - 1) * KS);
+      __builtin_amdgcn_sched_barrier(0);
+      MOELORA_COMPUTE(wa, xa);
+      __builtin_amdgcn_sched_barrier(0);
+      MOELORA_LOAD(wa, xa, kb0 + min(i + 2, nsteps - 1) * KS);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 1 < nsteps) MOELORA_COMPUTE(wb, xb);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    kb = kn;
   }
+#undef MOELORA_LOAD
+#undef MOELORA_COMPUTE
 
-  // Epilogue: lane holds weight rows n0 + 4*kq + v (v < 4) for token row (lane % 16).
+  // Epilogue: lane holds weight rows n0 + 16*rt + 4*kq + v (v < 4) for token row (lane % 16).
   const int64_t zstride = a.cap * a.r;
+  if (SPLIT) {
+    if (up_wave) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) s_up[((wave & 1) * NT + nt) * 64 + lane] = acc[0][nt];
+    }
+    __syncthreads();
+    if (up_wave) return;
+  }
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int row = blk * BM + nt * 16 + m;
     const int p = a.sorted_pairs[row];
     if (p < 0) continue;
     const int ad = sanitize_adapter(a.adapter_ids[p / a.k], a.nA);
-    const int nb = n0 + 4 * kq;
-    if (GATEUP) {
-      float g[4], u[4];
+    const float* zrow = a.zpart + (size_t)row * a.r;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        g[v] = acc[0][nt][v];
-        u[v] = acc[NW - 1][nt][v];
-      }
-      if (ad >= 0) {
-        const float* zrow = a.zpart + (size_t)row * a.r;
-        const uint16_t* bg = a.Bw + (((size_t)ad * a.E + e) * 2 * N + nb) * a.r;
-        lora_expand4(zrow, zstride, a.S, bg, a.r, g);
-        lora_expand4(zrow, zstride, a.S, bg + N * a.r, a.r, u);
-      }
-      float h[4];
+    for (int rt = 0; rt < RT; ++rt) {
+      const int nb = n0 + 16 * rt + 4 * kq;
+      if (GATEUP) {
+        float g[4], u[4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) h[v] = g[v] / (1.f + __expf(-g[v])) * u[v];
-      u32x2 packed = {pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
-      *reinterpret_cast<u32x2*>(a.act_out + (size_t)row * N + nb) = packed;
-    } else {
-      float d[4];
+        for (int v = 0; v < 4; ++v) {
+          g[v] = acc[rt][nt][v];
+          u[v] = SPLIT ? s_up[((wave & 1) * NT + nt) * 64 + lane][v] : acc[NW - RT + rt][nt][v];
+        }
+        if (ad >= 0) {
+          const uint16_t* bg = a.Bw + (((size_t)ad * a.E + e) * 2 * N + nb) * a.r;
+          lora_expand4(zrow, zstride, a.S, bg, a.r, g);
+          lora_expand4(zrow, zstride, a.S, bg + N * a.r, a.r, u);
+        }
+        float hv[4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) d[v] = acc[0][nt][v];
-      if (ad >= 0) {
-        const float* zrow = a.zpart + (size_t)row * a.r;
-        const uint16_t* bd = a.Bw + (((size_t)ad * a.E + e) * N + nb) * a.r;
-        lora_expand4(zrow, zstride, a.S, bd, a.r, d);
+        for (int v = 0; v < 4; ++v) hv[v] = g[v] / (1.f + __expf(-g[v])) * u[v];
+        u32x2 packed = {pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
+        *reinterpret_cast<u32x2*>(a.act_out + (size_t)row * N + nb) = packed;
+      } else {
+        float d[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) d[v] = acc[rt][nt][v];
+        if (ad >= 0 && zsplit == 0) {
+          const uint16_t* bd = a.Bw + (((size_t)ad * a.E + e) * N + nb) * a.r;
+          lora_expand4(zrow, zstride, a.S, bd, a.r, d);
+        }
+        *reinterpret_cast<f32x4*>(a.d_out + zsplit * a.d_split_stride + (size_t)p * N + nb) =
+            f32x4{d[0], d[1], d[2], d[3]};
       }
-      *reinterpret_cast<f32x4*>(a.d_out + (size_t)p * N + nb) = f32x4{d[0], d[1], d[2], d[3]};
     }
   }
 }
 
-hipError_t launch_skinny(int nt, bool gateup, const GemmArgs& a, int grid_x, int grid_y,
+hipError_t launch_skinny(const SkinnyConfig& c, bool gateup, const GemmArgs& a, int grid_y,
                          hipStream_t stream) {
+  const bool split = gateup && c.split;
+  const int cols_per_wg = split ? 32 : 4 * 16 * c.rt;
+  const int grid_x = (a.N + cols_per_wg - 1) / cols_per_wg;
   if (grid_x <= 0 || grid_y <= 0) return hipSuccess;
-  dim3 grid(grid_x, grid_y), block(256);
-#define MOELORA_SKINNY(NT_)                                                               \
-  if (nt == NT_) {                                                                        \
-    if (gateup)                                                                           \
-      hipLaunchKernelGGL((skinny_gemm_kernel<NT_, true>), grid, block, 0, stream, a);     \
-    else                                                                                  \
-      hipLaunchKernelGGL((skinny_gemm_kernel<NT_, false>), grid, block, 0, stream, a);    \
-    return hipGetLastError();                                                             \
+  dim3 grid(grid_x, grid_y, gateup ? 1 : a.ksplit), block(256);
+#define MOELORA_SKINNY(NT_, P_, RT_, PIPE_)                                                       \
+  if (c.nt == NT_ && c.p == P_ && c.rt == RT_ && c.pipe == PIPE_ && !split) {                     \
+    if (gateup)                                                                                   \
+      hipLaunchKernelGGL((skinny_gemm_kernel<NT_, true, P_, RT_, PIPE_, false>), grid, block, 0,  \
+                         stream, a);                                                              \
+    else                                                                                          \
+      hipLaunchKernelGGL((skinny_gemm_kernel<NT_, false, P_, RT_, PIPE_, false>), grid, block, 0, \
+                         stream, a);                                                              \
+    return hipGetLastError();                                                                     \
   }
-  MOELORA_SKINNY(1)
-  MOELORA_SKINNY(2)
-  MOELORA_SKINNY(4)
+#define MOELORA_SKINNY_SPLIT(NT_, P_, PIPE_)                                                      \
+  if (c.nt == NT_ && c.p == P_ && c.rt == 1 && c.pipe == PIPE_ && split) {                        \
+    hipLaunchKernelGGL((skinny_gemm_kernel<NT_, true, P_, 1, PIPE_, true>), grid, block, 0,       \
+                       stream, a);                                                                \
+    return hipGetLastError();                                                                     \
+  }
+  MOELORA_SKINNY(1, 4, 1, true)
+  MOELORA_SKINNY(1, 4, 1, false)
+  MOELORA_SKINNY(1, 4, 2, true)
+  MOELORA_SKINNY(1, 4, 2, false)
+  MOELORA_SKINNY(1, 8, 1, true)
+  MOELORA_SKINNY(1, 8, 1, false)
+  MOELORA_SKINNY(2, 4, 1, true)
+  MOELORA_SKINNY(2, 8, 1, true)
+  MOELORA_SKINNY(4, 4, 1, true)
+  MOELORA_SKINNY_SPLIT(1, 4, true)
+  MOELORA_SKINNY_SPLIT(1, 4, false)
+  MOELORA_SKINNY_SPLIT(1, 8, true)
+  MOELORA_SKINNY_SPLIT(1, 8, false)
 #undef MOELORA_SKINNY
+#undef MOELORA_SKINNY_SPLIT
   return hipErrorInvalidValue;
 }
 

@@ -26,6 +26,7 @@ struct AlignArgs {
 // LoRA shrink z = X A^T for the rows of the sorted layout (split-K partial sums).
 struct ShrinkArgs {
   const uint16_t* X;  // gather: x [T][K]; otherwise act [cap][K]
+  uint32_t x_bytes;   // size of X (< 2 GiB)
   const int* sorted_pairs;
   const int* block_expert;
   const int* n_blocks;
@@ -41,6 +42,7 @@ struct ShrinkArgs {
 // for gate_up the SiLU-and-mul) in the epilogue.
 struct GemmArgs {
   const uint16_t* X;   // gate_up: x [T][K]; down: act [cap][K]
+  uint32_t x_bytes;    // size of X (< 2 GiB)
   const uint16_t* W;   // gate_up: W1 [E][2I][h]; down: W2 [E][h][I]
   const uint16_t* Bw;  // gate_up: B1 [nA][E][2I][r]; down: B2 [nA][E][h][r]
   const float* zpart;  // [S][cap][r]
@@ -54,7 +56,18 @@ struct GemmArgs {
   int K;  // reduction length
   int N;  // gate_up: I (act columns); down: h
   uint16_t* act_out;  // gate_up: [cap][I]
-  float* d_out;       // down: [T*k][h]
+  float* d_out;       // down: [ksplit][T*k][h] partial sums
+  int ksplit;         // down: K splits (gridDim.z); gate_up: 1
+  int64_t d_split_stride;
+};
+
+// Tile shape of the skinny (few rows per expert) GEMM.
+struct SkinnyConfig {
+  int nt;  // 16-row token tiles per row block
+  int p;   // 16-byte loads per lane per weight row and K step (K step = 32 * p)
+  int rt;  // 16-row output tiles per wavefront
+  int pipe;   // 1: ping-pong register sets (loads of step k+1 overlap MFMAs of step k)
+  int split;  // gate_up: gate and up rows streamed by different wavefronts
 };
 
 // Host launchers (each defined next to its kernel). They return the launch status.
@@ -62,10 +75,10 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int* topk_ids,
                         int* tok_flags, hipStream_t stream);
 hipError_t launch_align(const AlignArgs& a, size_t dyn_lds, hipStream_t stream);
 hipError_t launch_shrink(bool gather, const ShrinkArgs& a, int tiles, hipStream_t stream);
-hipError_t launch_skinny(int nt, bool gateup, const GemmArgs& a, int grid_x, int grid_y,
+hipError_t launch_skinny(const SkinnyConfig& c, bool gateup, const GemmArgs& a, int grid_y,
                          hipStream_t stream);
-hipError_t launch_combine(const float* D, const float* topk_w, int T, int k, int h, uint16_t* y,
-                          hipStream_t stream);
+hipError_t launch_combine(const float* D, int ksplit, int64_t split_stride, const float* topk_w,
+                          int T, int k, int h, uint16_t* y, hipStream_t stream);
 
 constexpr int kAlignThreads = 1024;
 constexpr int kAlignStaticLds = 13 * 1024;  // >= the align kernel's static LDS (12.6 KB)

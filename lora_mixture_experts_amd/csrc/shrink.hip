@@ -44,10 +44,15 @@ __global__ __launch_bounds__(256) void lora_shrink_kernel(ShrinkArgs a) {
   const int m = lane & 15, kq = lane >> 4;
   const int n_ct = r < 16 ? 1 : r / 16;
 
-  const uint16_t* xrow = nullptr;
+  // Token rows through buffer loads: a padding row gets an out-of-range offset and reads zeros
+  // without touching memory (its outputs are never stored). Unconditional loads keep the
+  // compiler's outstanding-load count exact.
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.X, a.x_bytes);
+  uint32_t xo;
   {
     const int p = s_pair[m];
-    if (p >= 0) xrow = GATHER ? a.X + (size_t)(p / a.k) * K : a.X + (size_t)(row0 + m) * K;
+    xo = p < 0 ? kOutOfRange
+               : (uint32_t)((GATHER ? (size_t)(p / a.k) : (size_t)(row0 + m)) * K * 2);
   }
 
   int i = 0;
@@ -69,15 +74,14 @@ __global__ __launch_bounds__(256) void lora_shrink_kernel(ShrinkArgs a) {
       u32x4 xa[4];
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)
-        xa[jj] = xrow ? ldg16(xrow + kb + 8 * jj) : u32x4{0u, 0u, 0u, 0u};
+        xa[jj] = bufld16(xr, xo + 2u * (uint32_t)(kb + 8 * jj));
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         if (c < n_ct) {
-          const int q = c * 16 + m;
+          const int q = min(c * 16 + m, r - 1);  // columns q >= r (rank 8) are never stored
           u32x4 bw[4];
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj)
-            bw[jj] = q < r ? ldg16(Abase + (size_t)q * K + kb + 8 * jj) : u32x4{0u, 0u, 0u, 0u};
+          for (int jj = 0; jj < 4; ++jj) bw[jj] = ldg16(Abase + (size_t)q * K + kb + 8 * jj);
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) acc[c] = mfma16(xa[jj], bw[jj], acc[c]);
         }
