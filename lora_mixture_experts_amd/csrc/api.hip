@@ -71,12 +71,38 @@ size_t align_lds_plan(int T, int k, int E, int nA, AlignArgs* a) {
   return used;
 }
 
-// Row-block size (16 * NT) of the skinny GEMM path from the mean rows per expert.
-int pick_nt(int64_t P, int E) {
+// GEMM path from the mean rows per expert (known on the host; per-expert counts are not):
+// the skinny path streams weights once per 16/32-row block, the tiled path stages tiles in LDS
+// for MFMA-bound row counts. MOELORA_PATH=skinny|tiled64|tiled128 forces one for experiments.
+struct PathPlan {
+  bool tiled;
+  int nt;  // skinny: 16-row token tiles per row block
+  TiledConfig tc;
+  int bm;  // row-block size of the sorted layout
+};
+
+PathPlan pick_path(int64_t P, int E) {
   const double mean = (double)P / E;
-  if (mean <= 12.0) return 1;
-  if (mean <= 24.0) return 2;
-  return 4;
+  PathPlan pl;
+  pl.tiled = mean > 24.0;
+  pl.nt = mean <= 12.0 ? 1 : (mean <= 24.0 ? 2 : 4);
+  pl.tc = mean < 192.0 ? TiledConfig{64, 128, 32, 64} : TiledConfig{128, 128, 64, 64};
+  static int forced = -1;  // -1 unread, 0 none, 1 skinny, 2 tiled64, 3 tiled128
+  if (forced < 0) {
+    const char* env = getenv("MOELORA_PATH");
+    forced = !env ? 0 : !strcmp(env, "skinny") ? 1 : !strcmp(env, "tiled64") ? 2 : !strcmp(env, "tiled128") ? 3 : 0;
+  }
+  if (forced == 1) pl.tiled = false;
+  if (forced == 2) {
+    pl.tiled = true;
+    pl.tc = TiledConfig{64, 128, 32, 64};
+  }
+  if (forced == 3) {
+    pl.tiled = true;
+    pl.tc = TiledConfig{128, 128, 64, 64};
+  }
+  pl.bm = pl.tiled ? pl.tc.bm : 16 * pl.nt;
+  return pl;
 }
 
 bool skinny_instantiated(const SkinnyConfig& c, bool gateup) {
@@ -104,7 +130,7 @@ SkinnyPlan pick_skinny(int nt, int h, int I) {
   // wavefront; down streams two row tiles per wavefront and splits K in two
   pl.gu = SkinnyConfig{nt, 4, 1, 1, 0};
   pl.dn = SkinnyConfig{nt, 4, nt == 1 ? 2 : 1, 1, 0};
-  pl.ksplit = 2;
+  pl.ksplit = nt == 1 ? 2 : 1;
   static int ov[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   static bool parsed = false;
   if (!parsed) {
@@ -245,8 +271,9 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
     return MOELORA_EHIP;
   if (!mark(ev, 1, stream)) return MOELORA_EHIP;
 
-  const int nt = pick_nt(P, E);
-  const int bm = 16 * nt;
+  const PathPlan path = pick_path(P, E);
+  const int nt = path.nt;
+  const int bm = path.bm;
   AlignArgs al;
   al.topk_ids = topk_ids;
   al.adapter_ids = adapter_ids;
@@ -272,7 +299,7 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
 
   const int64_t max_rows = P + (int64_t)E * (bm - 1);
   const int max_blocks = (int)((max_rows + bm - 1) / bm);
-  const int tiles16 = max_blocks * nt;
+  const int tiles16 = max_blocks * (bm / 16);
   const int s1 = pick_splits(tiles16, h), s2 = pick_splits(tiles16, I);
 
   ShrinkArgs sh;
@@ -299,6 +326,7 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   g.r = r;
   g.act_out = act;
   g.d_out = dpair;
+  g.n_blocks_max = max_blocks;
 
   // gate_up: shrink z1 = x A1, then W1 GEMM + z1 B1 + SiLU-and-mul -> act
   sh.X = (const uint16_t*)x;
@@ -317,10 +345,13 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   g.S = s1;
   g.K = h;
   g.N = I;
-  const SkinnyPlan plan = pick_skinny(nt, h, I);
+  SkinnyPlan plan = pick_skinny(nt, h, I);
+  if (path.tiled) plan.ksplit = 1;
   g.ksplit = 1;
   g.d_split_stride = P * (int64_t)h;
-  if (launch_skinny(plan.gu, true, g, max_blocks, stream) != hipSuccess) return MOELORA_EHIP;
+  const hipError_t gu_err = path.tiled ? launch_tiled(path.tc, true, g, stream)
+                                       : launch_skinny(plan.gu, true, g, max_blocks, stream);
+  if (gu_err != hipSuccess) return MOELORA_EHIP;
   if (!mark(ev, 4, stream)) return MOELORA_EHIP;
 
   // down: shrink z2 = act A2, then W2 GEMM + z2 B2 -> D (fp32, pair order)
@@ -341,7 +372,9 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   g.K = I;
   g.N = h;
   g.ksplit = plan.ksplit;
-  if (launch_skinny(plan.dn, false, g, max_blocks, stream) != hipSuccess) return MOELORA_EHIP;
+  const hipError_t dn_err = path.tiled ? launch_tiled(path.tc, false, g, stream)
+                                       : launch_skinny(plan.dn, false, g, max_blocks, stream);
+  if (dn_err != hipSuccess) return MOELORA_EHIP;
   if (!mark(ev, 6, stream)) return MOELORA_EHIP;
 
   // weighted top-k combine -> y (bf16)

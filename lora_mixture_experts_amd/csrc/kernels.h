@@ -59,6 +59,12 @@ struct GemmArgs {
   float* d_out;       // down: [ksplit][T*k][h] partial sums
   int ksplit;         // down: K splits (gridDim.z); gate_up: 1
   int64_t d_split_stride;
+  int n_blocks_max;   // row blocks the grid is sized for (>= *n_blocks)
+};
+
+// Tile shape of the LDS-staged GEMM (four wavefronts of WM x WN each).
+struct TiledConfig {
+  int bm, bn, wm, wn;
 };
 
 // Tile shape of the skinny (few rows per expert) GEMM.
@@ -77,6 +83,7 @@ hipError_t launch_align(const AlignArgs& a, size_t dyn_lds, hipStream_t stream);
 hipError_t launch_shrink(bool gather, const ShrinkArgs& a, int tiles, hipStream_t stream);
 hipError_t launch_skinny(const SkinnyConfig& c, bool gateup, const GemmArgs& a, int grid_y,
                          hipStream_t stream);
+hipError_t launch_tiled(const TiledConfig& c, bool gateup, const GemmArgs& a, hipStream_t stream);
 hipError_t launch_combine(const float* D, int ksplit, int64_t split_stride, const float* topk_w,
                           int T, int k, int h, uint16_t* y, hipStream_t stream);
 

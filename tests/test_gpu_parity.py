@@ -103,6 +103,11 @@ SMALL = {
     "mid": Workload("mid", 200, 256, 384, 8, 2, 6, 16),
     "fg_small": Workload("fg_small", 64, 256, 256, 32, 8, 16, 32, hot_experts=4, hot_bias=2.0),
     "one_token": Workload("one_token", 1, 256, 384, 8, 2, 4, 16),
+    # mean rows per expert above 24 selects the LDS-tiled MFMA path (64- and 128-row blocks)
+    "tiled64": Workload("tiled64", 256, 384, 640, 4, 2, 5, 16),
+    "tiled64_r8": Workload("tiled64_r8", 300, 256, 256, 4, 1, 3, 8),
+    "tiled128_r64": Workload("tiled128_r64", 900, 256, 384, 3, 2, 6, 64),
+    "tiled128_runs": Workload("tiled128_runs", 1024, 256, 256, 4, 2, 9, 32, adapters="zipf_runs", run=40),
 }
 
 
