@@ -77,7 +77,8 @@ size_t align_lds_plan(int T, int k, int E, int nA, AlignArgs* a) {
 struct PathPlan {
   bool tiled;
   int nt;  // skinny: 16-row token tiles per row block
-  TiledConfig tc;
+  TiledConfig tc;     // gate_up tile
+  TiledConfig tc_dn;  // down tile (same bm)
   int bm;  // row-block size of the sorted layout
 };
 
@@ -86,20 +87,25 @@ PathPlan pick_path(int64_t P, int E) {
   PathPlan pl;
   pl.tiled = mean > 24.0;
   pl.nt = mean <= 12.0 ? 1 : (mean <= 24.0 ? 2 : 4);
-  pl.tc = mean < 192.0 ? TiledConfig{64, 128, 32, 64} : TiledConfig{128, 128, 64, 64};
-  static int forced = -1;  // -1 unread, 0 none, 1 skinny, 2 tiled64, 3 tiled128
+  const TiledConfig t64{64, 128, 32, 64}, t128{128, 128, 64, 64}, t256{256, 256, 128, 128},
+      t256d{256, 128, 128, 64};
+  pl.tc = mean < 192.0 ? t64 : t128;
+  pl.tc_dn = pl.tc.bm == 256 ? t256d : pl.tc;
+  static int forced = -1;  // -1 unread, 0 none, 1 skinny, 2 tiled64, 3 tiled128, 4 tiled256
   if (forced < 0) {
     const char* env = getenv("MOELORA_PATH");
-    forced = !env ? 0 : !strcmp(env, "skinny") ? 1 : !strcmp(env, "tiled64") ? 2 : !strcmp(env, "tiled128") ? 3 : 0;
+    forced = !env ? 0
+             : !strcmp(env, "skinny")   ? 1
+             : !strcmp(env, "tiled64")  ? 2
+             : !strcmp(env, "tiled128") ? 3
+             : !strcmp(env, "tiled256") ? 4
+                                        : 0;
   }
   if (forced == 1) pl.tiled = false;
-  if (forced == 2) {
+  if (forced >= 2) {
     pl.tiled = true;
-    pl.tc = TiledConfig{64, 128, 32, 64};
-  }
-  if (forced == 3) {
-    pl.tiled = true;
-    pl.tc = TiledConfig{128, 128, 64, 64};
+    pl.tc = forced == 2 ? t64 : (forced == 3 ? t128 : t256);
+    pl.tc_dn = forced == 4 ? t256d : pl.tc;
   }
   pl.bm = pl.tiled ? pl.tc.bm : 16 * pl.nt;
   return pl;
@@ -372,7 +378,7 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   g.K = I;
   g.N = h;
   g.ksplit = plan.ksplit;
-  const hipError_t dn_err = path.tiled ? launch_tiled(path.tc, false, g, stream)
+  const hipError_t dn_err = path.tiled ? launch_tiled(path.tc_dn, false, g, stream)
                                        : launch_skinny(plan.dn, false, g, max_blocks, stream);
   if (dn_err != hipSuccess) return MOELORA_EHIP;
   if (!mark(ev, 6, stream)) return MOELORA_EHIP;

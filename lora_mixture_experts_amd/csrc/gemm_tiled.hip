@@ -29,8 +29,11 @@
 
 namespace moelora {
 
-template <bool GATEUP, int BM, int BN, int BK, int WM, int WN>
-__global__ __launch_bounds__(256) void tiled_gemm_kernel(GemmArgs a, int n_tiles_n, int grid_total) {
+// DEPTH: K steps of global prefetch (1: one register staging set, 2: two). Tiles up to 128x128
+// keep two wavefronts per SIMD; 256-row tiles run one.
+template <bool GATEUP, int BM, int BN, int BK, int WM, int WN, int DEPTH>
+__global__ __launch_bounds__(256, (BM * BN > 128 * 128) ? 1 : 2) void tiled_gemm_kernel(
+    GemmArgs a, int n_tiles_n, int grid_total) {
   constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
   static_assert(WAVES_M * WAVES_N == 4, "four wavefronts per workgroup");
   static_assert(BK == 64, "8 chunks of 16 bytes per LDS row");
@@ -41,7 +44,7 @@ __global__ __launch_bounds__(256) void tiled_gemm_kernel(GemmArgs a, int n_tiles
   static_assert(CA * 256 == BM * CPR && CB * 256 == BN * CPR, "tile must split over 256 threads");
   static_assert(!GATEUP || FN % 2 == 0, "gate_up needs gate and up halves per wave");
 
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (BM + BN) * BK];
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];  // 2 * (BM + BN) * BK
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -100,55 +103,110 @@ __global__ __launch_bounds__(256) void tiled_gemm_kernel(GemmArgs a, int n_tiles
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nks = K / BK;
-  u32x4 ra[CA], rb[CB];
-  auto gload = [&](int ks) {
-#pragma unroll
-    for (int i = 0; i < CA; ++i) ra[i] = bufld16(xr, xo[i] + 2u * (uint32_t)(ks * BK));
-#pragma unroll
-    for (int i = 0; i < CB; ++i) rb[i] = ldg16(wsrc[i] + (size_t)ks * BK);
-  };
-  auto lstore = [&](int buf) {
-    uint16_t* A = lds_a(buf);
-    uint16_t* B = lds_b(buf);
-#pragma unroll
-    for (int i = 0; i < CA; ++i)
-      *reinterpret_cast<u32x4*>(A + a_row[i] * BK + 8 * (a_chk[i] ^ (a_row[i] & 7))) = ra[i];
-#pragma unroll
-    for (int i = 0; i < CB; ++i)
-      *reinterpret_cast<u32x4*>(B + b_row[i] * BK + 8 * (b_chk[i] ^ (b_row[i] & 7))) = rb[i];
-  };
+  // Global tiles are prefetched two K steps ahead into two register staging sets (s0, s1), so a
+  // load has two compute phases to land before it is written to LDS. Loads are unconditional
+  // (past the end they re-read the last step), which keeps the compiler's outstanding-load
+  // count exact; LDS is double-buffered with one barrier per K step.
+  u32x4 sa0[CA], sb0[CB], sa1[CA], sb1[CB];
+#define MOELORA_GLOAD(SA, SB, KS)                                                         \
+  do {                                                                                    \
+    const int ks_ = min((KS), nks - 1);                                                   \
+    _Pragma("unroll") for (int i = 0; i < CA; ++i) SA[i] =                                \
+        bufld16(xr, xo[i] + 2u * (uint32_t)(ks_ * BK));                                   \
+    _Pragma("unroll") for (int i = 0; i < CB; ++i) SB[i] = ldg16(wsrc[i] + (size_t)ks_ * BK); \
+  } while (0)
+#define MOELORA_LSTORE(SA, SB, BUF)                                                       \
+  do {                                                                                    \
+    uint16_t* A_ = lds_a(BUF);                                                            \
+    uint16_t* B_ = lds_b(BUF);                                                            \
+    _Pragma("unroll") for (int i = 0; i < CA; ++i) *reinterpret_cast<u32x4*>(            \
+        A_ + a_row[i] * BK + 8 * (a_chk[i] ^ (a_row[i] & 7))) = SA[i];                    \
+    _Pragma("unroll") for (int i = 0; i < CB; ++i) *reinterpret_cast<u32x4*>(            \
+        B_ + b_row[i] * BK + 8 * (b_chk[i] ^ (b_row[i] & 7))) = SB[i];                    \
+  } while (0)
 
   const int fr = lane & 15, fg = lane >> 4;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int ks = 0; ks < nks; ++ks) {
-    const int buf = ks & 1;
-    if (ks + 1 < nks) gload(ks + 1);
+  // MFMA fragments of the two 32-wide halves of a K step are read from LDS together into two
+  // register sets; the second half's reads land while the first half's MFMAs run.
+  auto read_frags = [&](const uint16_t* A, const uint16_t* B, int j, u32x4* af, u32x4* bf) {
+    const int chunk = fg + 4 * j;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int r = wm * WM + i * 16 + fr;
+      af[i] = *reinterpret_cast<const u32x4*>(A + r * BK + 8 * (chunk ^ (r & 7)));
+    }
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+      const int r = wn * WN + i * 16 + fr;
+      bf[i] = *reinterpret_cast<const u32x4*>(B + r * BK + 8 * (chunk ^ (r & 7)));
+    }
+  };
+  auto mfmas = [&](const u32x4* af, const u32x4* bf) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int jn = 0; jn < FN; ++jn) acc[i][jn] = mfma16(af[i], bf[jn], acc[i][jn]);
+  };
+  auto compute = [&](int buf) {
+    static_assert(BK == 64, "two 32-wide halves per K step");
     const uint16_t* A = lds_a(buf);
     const uint16_t* B = lds_b(buf);
+    u32x4 af0[FM], bf0[FN], af1[FM], bf1[FN];
+    read_frags(A, B, 0, af0, bf0);
+    __builtin_amdgcn_sched_barrier(0);
+    // the second half's reads are interleaved one per MFMA of the first half (the LDS counter
+    // holds at most 15 outstanding reads, so issuing all 16 up front would force a full wait)
+    read_frags(A, B, 1, af1, bf1);
+    mfmas(af0, bf0);
 #pragma unroll
-    for (int j = 0; j < BK / 32; ++j) {
-      const int chunk = fg + 4 * j;
-      u32x4 af[FM], bf[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int r = wm * WM + i * 16 + fr;
-        af[i] = *reinterpret_cast<const u32x4*>(A + r * BK + 8 * (chunk ^ (r & 7)));
-      }
-#pragma unroll
-      for (int i = 0; i < FN; ++i) {
-        const int r = wn * WN + i * 16 + fr;
-        bf[i] = *reinterpret_cast<const u32x4*>(B + r * BK + 8 * (chunk ^ (r & 7)));
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int jn = 0; jn < FN; ++jn) acc[i][jn] = mfma16(af[i], bf[jn], acc[i][jn]);
+    for (int t = 0; t < FM + FN; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
     }
-    if (ks + 1 < nks) lstore(buf ^ 1);
-    __syncthreads();
+    __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(af1, bf1);
+  };
+
+  MOELORA_GLOAD(sa0, sb0, 0);
+  if (DEPTH == 2) MOELORA_GLOAD(sa1, sb1, 1);
+  MOELORA_LSTORE(sa0, sb0, 0);
+  __syncthreads();
+  // sched_barrier(0) pins the phase order: without it the compiler sinks the prefetch below
+  // the MFMAs, which shortens the time the loads have to land. The LDS stores are
+  // unconditional as well (past the end they fill a buffer nobody reads), so the compiler can
+  // count exactly which loads are still in flight.
+  if (DEPTH == 2) {
+    for (int ks = 0; ks < nks; ks += 2) {
+      // even step: compute buffer 0, stage step ks+1 (set 1) into buffer 1
+      MOELORA_GLOAD(sa0, sb0, ks + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(0);
+      __builtin_amdgcn_sched_barrier(0);
+      MOELORA_LSTORE(sa1, sb1, 1);
+      __syncthreads();
+      // odd step (K is a multiple of 128, so the number of 64-wide steps is even): compute buffer 1, stage step ks+2 (set 0) into buffer 0
+      MOELORA_GLOAD(sa1, sb1, ks + 3);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(1);
+      __builtin_amdgcn_sched_barrier(0);
+      MOELORA_LSTORE(sa0, sb0, 0);
+      __syncthreads();
+    }
+  } else {
+    // one staging set: the next step's loads are issued before the current MFMAs
+    for (int ks = 0; ks < nks; ++ks) {
+      const int buf = ks & 1;
+      MOELORA_GLOAD(sa1, sb1, ks + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(buf);
+      __builtin_amdgcn_sched_barrier(0);
+      MOELORA_LSTORE(sa1, sb1, buf ^ 1);
+      __syncthreads();
+    }
   }
+#undef MOELORA_GLOAD
+#undef MOELORA_LSTORE
 
   // ---- epilogue ----
   // Weight row (within W1 or W2 of expert e) of column fragment jn for this lane's column.
@@ -237,24 +295,39 @@ __global__ __launch_bounds__(256) void tiled_gemm_kernel(GemmArgs a, int n_tiles
   }
 }
 
+template <bool GATEUP, int BM, int BN, int WM, int WN>
+hipError_t launch_tiled_t(const GemmArgs& a, int n_tiles_n, int total, hipStream_t stream) {
+  constexpr int DEPTH = BM * BN > 128 * 128 ? 1 : 2;
+  constexpr int lds_bytes = 2 * (BM + BN) * 64 * 2;
+  static bool attr_set[64] = {};
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev >= 0 && dev < 64 && !attr_set[dev]) {
+    err = hipFuncSetAttribute((const void*)tiled_gemm_kernel<GATEUP, BM, BN, 64, WM, WN, DEPTH>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+    if (err != hipSuccess) return err;
+    attr_set[dev] = true;
+  }
+  hipLaunchKernelGGL((tiled_gemm_kernel<GATEUP, BM, BN, 64, WM, WN, DEPTH>), dim3(total), dim3(256),
+                     lds_bytes, stream, a, n_tiles_n, total);
+  return hipGetLastError();
+}
+
 hipError_t launch_tiled(const TiledConfig& c, bool gateup, const GemmArgs& a, hipStream_t stream) {
   const int cols = gateup ? 2 * a.N : a.N;
   const int n_tiles_n = cols / c.bn;
   int total = n_tiles_n * a.n_blocks_max;
   total = (total + 7) / 8 * 8;
   if (total <= 0) return hipSuccess;
-#define MOELORA_TILED(BM_, BN_, WM_, WN_)                                                        \
-  if (c.bm == BM_ && c.bn == BN_ && c.wm == WM_ && c.wn == WN_) {                                \
-    if (gateup)                                                                                  \
-      hipLaunchKernelGGL((tiled_gemm_kernel<true, BM_, BN_, 64, WM_, WN_>), dim3(total),         \
-                         dim3(256), 0, stream, a, n_tiles_n, total);                             \
-    else                                                                                         \
-      hipLaunchKernelGGL((tiled_gemm_kernel<false, BM_, BN_, 64, WM_, WN_>), dim3(total),        \
-                         dim3(256), 0, stream, a, n_tiles_n, total);                             \
-    return hipGetLastError();                                                                    \
-  }
+#define MOELORA_TILED(BM_, BN_, WM_, WN_)                                              \
+  if (c.bm == BM_ && c.bn == BN_ && c.wm == WM_ && c.wn == WN_)                        \
+    return gateup ? launch_tiled_t<true, BM_, BN_, WM_, WN_>(a, n_tiles_n, total, stream) \
+                  : launch_tiled_t<false, BM_, BN_, WM_, WN_>(a, n_tiles_n, total, stream);
   MOELORA_TILED(128, 128, 64, 64)
   MOELORA_TILED(64, 128, 32, 64)
+  MOELORA_TILED(256, 256, 128, 128)
+  MOELORA_TILED(256, 128, 128, 64)
 #undef MOELORA_TILED
   return hipErrorInvalidValue;
 }

@@ -108,6 +108,9 @@ SMALL = {
     "tiled64_r8": Workload("tiled64_r8", 300, 256, 256, 4, 1, 3, 8),
     "tiled128_r64": Workload("tiled128_r64", 900, 256, 384, 3, 2, 6, 64),
     "tiled128_runs": Workload("tiled128_runs", 1024, 256, 256, 4, 2, 9, 32, adapters="zipf_runs", run=40),
+    # mean rows per expert of 768 and more selects 256-row blocks (256x256 gate_up, 256x128 down)
+    "tiled256_r64": Workload("tiled256_r64", 2048, 256, 384, 4, 2, 6, 64, adapters="zipf_runs", run=100),
+    "tiled256_k1": Workload("tiled256_k1", 1600, 384, 640, 2, 1, 4, 16),
 }
 
 
