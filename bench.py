@@ -56,15 +56,23 @@ def kernel_source_hash() -> str:
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per gate_up launch from the committed rocprofv3 counter summary, or None when
-    the summary is missing or was taken on different kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"traffic_gate_up_{workload}.json")
+    """HBM bytes per gate_up launch from the committed rocprofv3 counter summary
+    (profiles/traffic_gate_up_<workload>.txt: FETCH_SIZE and WRITE_SIZE scaled by a 1 GiB copy),
+    or None when the summary is missing or was taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_gate_up_{workload}.txt")
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path))
+    rec = {}
+    for line in open(path):
+        if ":" in line:
+            key, val = line.split(":", 1)
+            rec[key.strip()] = val.strip()
     if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    try:
+        return float(rec["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(w, inp, n_tokens: int):

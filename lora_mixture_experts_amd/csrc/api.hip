@@ -73,7 +73,7 @@ size_t align_lds_plan(int T, int k, int E, int nA, AlignArgs* a) {
 
 // GEMM path from the mean rows per expert (known on the host; per-expert counts are not):
 // the skinny path streams weights once per 16/32-row block, the tiled path stages tiles in LDS
-// for MFMA-bound row counts. MOELORA_PATH=skinny|tiled64|tiled128 forces one for experiments.
+// for MFMA-bound row counts. MOELORA_PATH=skinny forces the skinny path (experiments).
 struct PathPlan {
   bool tiled;
   int nt;  // skinny: 16-row token tiles per row block
@@ -82,30 +82,43 @@ struct PathPlan {
   int bm;  // row-block size of the sorted layout
 };
 
-PathPlan pick_path(int64_t P, int E) {
+PathPlan pick_path(int64_t P, int E, int h, int I) {
   const double mean = (double)P / E;
   PathPlan pl;
   pl.tiled = mean > 24.0;
   pl.nt = mean <= 12.0 ? 1 : (mean <= 24.0 ? 2 : 4);
-  const TiledConfig t64{64, 128, 32, 64}, t128{128, 128, 64, 64}, t256{256, 256, 128, 128},
-      t256d{256, 128, 128, 64};
+  const TiledConfig t64{64, 128, 32, 64, 2}, t128{128, 128, 64, 64, 2};
   pl.tc = mean < 192.0 ? t64 : t128;
-  pl.tc_dn = pl.tc.bm == 256 ? t256d : pl.tc;
-  static int forced = -1;  // -1 unread, 0 none, 1 skinny, 2 tiled64, 3 tiled128, 4 tiled256
+  pl.tc_dn = pl.tc;
+  // MOELORA_TILED="bm,bn,wm,wn,depth[,bm_d,bn_d,wm_d,wn_d,depth_d]" forces tiles (experiments)
+  static int forced = -1;  // -1 unread, 0 none, 1 skinny, 2 tiled
+  static TiledConfig ft, ftd;
   if (forced < 0) {
+    forced = 0;
     const char* env = getenv("MOELORA_PATH");
-    forced = !env ? 0
-             : !strcmp(env, "skinny")   ? 1
-             : !strcmp(env, "tiled64")  ? 2
-             : !strcmp(env, "tiled128") ? 3
-             : !strcmp(env, "tiled256") ? 4
-                                        : 0;
+    if (env && !strcmp(env, "skinny")) forced = 1;
+    const char* tenv = getenv("MOELORA_TILED");
+    if (tenv) {
+      int v[10] = {0};
+      const int n = sscanf(tenv, "%d,%d,%d,%d,%d,%d,%d,%d,%d,%d", &v[0], &v[1], &v[2], &v[3], &v[4],
+                           &v[5], &v[6], &v[7], &v[8], &v[9]);
+      if (n >= 5) {
+        ft = TiledConfig{v[0], v[1], v[2], v[3], v[4]};
+        ftd = n >= 10 ? TiledConfig{v[5], v[6], v[7], v[8], v[9]} : ft;
+        if (ftd.bm == ft.bm) forced = 2;
+      }
+    }
   }
   if (forced == 1) pl.tiled = false;
-  if (forced >= 2) {
+  if (forced == 2) {
     pl.tiled = true;
-    pl.tc = forced == 2 ? t64 : (forced == 3 ? t128 : t256);
-    pl.tc_dn = forced == 4 ? t256d : pl.tc;
+    pl.tc = ft;
+    pl.tc_dn = ftd;
+  }
+  // column tiles must divide the GEMM widths (2I for gate_up, h for down); 128 always does
+  if ((2 * I) % pl.tc.bn != 0 || h % pl.tc_dn.bn != 0) {
+    pl.tc = mean < 192.0 ? t64 : t128;
+    pl.tc_dn = pl.tc;
   }
   pl.bm = pl.tiled ? pl.tc.bm : 16 * pl.nt;
   return pl;
@@ -277,7 +290,7 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
     return MOELORA_EHIP;
   if (!mark(ev, 1, stream)) return MOELORA_EHIP;
 
-  const PathPlan path = pick_path(P, E);
+  const PathPlan path = pick_path(P, E, h, I);
   const int nt = path.nt;
   const int bm = path.bm;
   AlignArgs al;

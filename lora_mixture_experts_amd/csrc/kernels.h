@@ -65,6 +65,7 @@ struct GemmArgs {
 // Tile shape of the LDS-staged GEMM (four wavefronts of WM x WN each).
 struct TiledConfig {
   int bm, bn, wm, wn;
+  int depth;  // K steps of global prefetch held in registers (1 or 2)
 };
 
 // Tile shape of the skinny (few rows per expert) GEMM.
