@@ -52,28 +52,31 @@ int check_device() {
   return known[dev] == 1 ? MOELORA_OK : MOELORA_EDEVICE;
 }
 
-// Where the align kernel keeps its tables: LDS when they fit, else the workspace.
+// Where the align kernel keeps its lists and tables: LDS when they fit, else the workspace.
 size_t align_lds_plan(int T, int k, int E, int nA, AlignArgs* a) {
   const size_t budget = (size_t)(kLdsBytes - kAlignStaticLds);
   const size_t tables = 2 * sizeof(int) * (size_t)E * (nA + 1);
-  const size_t stage = sizeof(int) * ((size_t)T * k + T);
+  const size_t lists = sizeof(int) * align_list_ints(T, k, E);
   a->tables_in_lds = 0;
-  a->stage_inputs = 0;
+  a->lists_in_lds = 0;
   size_t used = 0;
-  if (tables <= budget) {
+  if (lists + tables <= budget) {
+    a->tables_in_lds = a->lists_in_lds = 1;
+    used = lists + tables;
+  } else if (lists <= budget) {
+    a->lists_in_lds = 1;
+    used = lists;
+  } else if (tables <= budget) {
     a->tables_in_lds = 1;
-    used += tables;
-  }
-  if (used + stage <= budget) {
-    a->stage_inputs = 1;
-    used += stage;
+    used = tables;
   }
   return used;
 }
 
 // GEMM path from the mean rows per expert (known on the host; per-expert counts are not):
 // the skinny path streams weights once per 16/32-row block, the tiled path stages tiles in LDS
-// for MFMA-bound row counts. MOELORA_PATH=skinny forces the skinny path (experiments).
+// for MFMA-bound row counts. MOELORA_PATH=skinny|skinny1|skinny2 forces the skinny path (and
+// its row-block size) for experiments.
 struct PathPlan {
   bool tiled;
   int nt;  // skinny: 16-row token tiles per row block
@@ -97,6 +100,8 @@ PathPlan pick_path(int64_t P, int E, int h, int I) {
     forced = 0;
     const char* env = getenv("MOELORA_PATH");
     if (env && !strcmp(env, "skinny")) forced = 1;
+    if (env && !strcmp(env, "skinny1")) forced = 3;
+    if (env && !strcmp(env, "skinny2")) forced = 4;
     const char* tenv = getenv("MOELORA_TILED");
     if (tenv) {
       int v[10] = {0};
@@ -110,6 +115,10 @@ PathPlan pick_path(int64_t P, int E, int h, int I) {
     }
   }
   if (forced == 1) pl.tiled = false;
+  if (forced == 3 || forced == 4) {
+    pl.tiled = false;
+    pl.nt = forced == 3 ? 1 : 2;
+  }
   if (forced == 2) {
     pl.tiled = true;
     pl.tc = ft;
@@ -209,6 +218,7 @@ bool moelora_make_layout(int T, int h, int I, int E, int nA, int r, int topk, Mo
   L->dpair = take(4 * (size_t)kMaxDownSplit * P * h);
   L->align_cnt = take(4 * (size_t)E * (nA + 1));
   L->align_start = take(4 * (size_t)E * (nA + 1));
+  L->align_lists = take(4 * align_list_ints(T, topk, E));
   L->total = off;
   return true;
 }
@@ -312,6 +322,7 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   al.n_blocks = n_blocks;
   al.g_cnt = (int*)(ws + L.align_cnt);
   al.g_start = (int*)(ws + L.align_start);
+  al.g_lists = (int*)(ws + L.align_lists);
   const size_t lds = align_lds_plan(T, topk, E, nA, &al);
   if (launch_align(al, lds, stream) != hipSuccess) return MOELORA_EHIP;
   if (!mark(ev, 2, stream)) return MOELORA_EHIP;
@@ -475,6 +486,7 @@ int moe_lora_route_align(const float* router_logits, const int32_t* adapter_ids,
   al.n_blocks = nullptr;
   al.g_cnt = (int*)(ws + L.align_cnt);
   al.g_start = (int*)(ws + L.align_start);
+  al.g_lists = (int*)(ws + L.align_lists);
   const size_t lds = align_lds_plan(d->T, topk, d->n_experts, d->n_adapters, &al);
   if (launch_align(al, lds, stream) != hipSuccess) return MOELORA_EHIP;
   return MOELORA_OK;

@@ -19,9 +19,15 @@ struct AlignArgs {
   int* n_blocks;        // [1] or nullptr
   int* g_cnt;           // [E*(nA+1)] global scratch when the tables do not fit in LDS
   int* g_start;         // [E*(nA+1)]
+  int* g_lists;         // [3*T*k + T + 16*E] global scratch when the lists do not fit in LDS
   int tables_in_lds;
-  int stage_inputs;
+  int lists_in_lds;
 };
+
+// ints of the align kernel's list scratch (staged ids, ranks, expert lists, adapters, counts)
+inline size_t align_list_ints(int T, int k, int E) {
+  return 3 * (size_t)T * k + (size_t)T + 16 * (size_t)E;
+}
 
 // LoRA shrink z = X A^T for the rows of the sorted layout (split-K partial sums).
 struct ShrinkArgs {
@@ -89,7 +95,7 @@ hipError_t launch_combine(const float* D, int ksplit, int64_t split_stride, cons
                           int T, int k, int h, uint16_t* y, hipStream_t stream);
 
 constexpr int kAlignThreads = 1024;
-constexpr int kAlignStaticLds = 13 * 1024;  // >= the align kernel's static LDS (12.6 KB)
+constexpr int kAlignStaticLds = 17 * 1024;  // >= the align kernel's static LDS (16.7 KB)
 constexpr int kLdsBytes = 160 * 1024;
 
 }  // namespace moelora

@@ -98,13 +98,16 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
 
 // ------------------------------------------------------------------------------------------
 // Align: one workgroup of 1024 threads.
-//   phase 0  validate adapter ids (out of range -> flag, treated as -1), collect flags
-//   phase 1  count pairs per bucket b = e*(nA+1) + (a+1); one wavefront owns each expert
+//   phase 0  validate adapter ids (out of range -> flag, treated as -1), collect flags, stage
+//   phase A  per-expert pair lists in token order: each wavefront ranks its slice of pairs by
+//            expert (stable), an (expert, wavefront) scan turns the ranks into positions
+//   phase D  count pairs per bucket b = e*(nA+1) + (a+1), one wavefront per expert list
 //   phase 2  exclusive scans: padded segment starts, expert offsets, segment table
 //   phase 3  padding slots (-1) and the row-block -> expert table
 //   phase 4  scatter pair ids; inside a bucket pairs keep token order
-// Within a wavefront, lanes with equal bucket are found by one ballot per key bit, so the
-// rank of a pair among equal-bucket pairs of earlier tokens is an exact popcount.
+// Within a wavefront, lanes with equal key are found by one ballot per key bit, so the rank of
+// a pair among equal-key pairs of earlier lanes is an exact popcount. Every table lives in LDS
+// when it fits and in the workspace otherwise.
 // ------------------------------------------------------------------------------------------
 __device__ __forceinline__ uint64_t match_key(bool member, int key, int nbits) {
   uint64_t eq = __ballot(member);
@@ -172,6 +175,7 @@ __global__ __launch_bounds__(1024) void align_kernel(AlignArgs a) {
   __shared__ int s_ebase[kMaxExperts];
   __shared__ int s_sexp[kMaxExperts];
   __shared__ int s_off[kMaxExperts + 1];
+  __shared__ int s_estart[kMaxExperts + 1];
   __shared__ int s_red[72];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwaves = blockDim.x >> 6;
@@ -180,6 +184,8 @@ __global__ __launch_bounds__(1024) void align_kernel(AlignArgs a) {
   const int nb1 = nA + 1, nb = E * nb1;
   const int seg_pad = a.seg_pad, block_m = a.block_m;
 
+  // carve LDS (or the workspace): tables cnt/start [nb]; lists tk [P], rank [P], elist [P],
+  // ad [T], cnt_we [nwaves][E]
   int* dyn = smem;
   int* cnt;
   int* start;
@@ -191,18 +197,18 @@ __global__ __launch_bounds__(1024) void align_kernel(AlignArgs a) {
     cnt = a.g_cnt;
     start = a.g_start;
   }
-  const int* tk = a.topk_ids;
-  int* s_ad = nullptr;
-  if (a.stage_inputs) {
-    int* s_tk = dyn;
-    s_ad = dyn + P;
-    for (int i = tid; i < P; i += bd) s_tk[i] = a.topk_ids[i];
-    tk = s_tk;
-  }
+  int* lists = a.lists_in_lds ? dyn : a.g_lists;
+  int* tk = lists;
+  int* rank = tk + P;
+  int* elist = rank + P;
+  int* adl = elist + P;
+  int* cnt_we = adl + T;
 
   // phase 0
   int fl_nonfinite = 0, fl_range = 0;
   for (int i = tid; i < nb; i += bd) cnt[i] = 0;
+  for (int i = tid; i < nwaves * E; i += bd) cnt_we[i] = 0;
+  for (int i = tid; i < P; i += bd) tk[i] = a.topk_ids[i];
   for (int t = tid; t < T; t += bd) {
     int av = a.adapter_ids[t];
     if (av < -1 || av >= nA) {
@@ -210,29 +216,63 @@ __global__ __launch_bounds__(1024) void align_kernel(AlignArgs a) {
       av = -1;
     }
     if (a.tok_flags[t]) fl_nonfinite = 1;
-    if (s_ad) s_ad[t] = av;
+    adl[t] = av;
   }
   fl_nonfinite = __syncthreads_or(fl_nonfinite);
   fl_range = __syncthreads_or(fl_range);
 
-  auto adapter_of = [&](int t) -> int {
-    if (s_ad) return s_ad[t];
-    const int av = a.adapter_ids[t];
-    return (av < -1 || av >= nA) ? -1 : av;
-  };
+  // phase A: stable rank of each pair among the pairs of its expert in this wavefront's slice
+  const int ebits = E > 1 ? 32 - __clz(E - 1) : 0;
+  const int PP = (P + nwaves - 1) / nwaves;
+  {
+    const int p0 = wave * PP, p1 = min(P, p0 + PP);
+    for (int base = p0; base < p1; base += 64) {
+      const int p = base + lane;
+      const bool valid = p < p1;
+      const int e = valid ? tk[p] : 0;
+      const uint64_t eq = match_key(valid, e, ebits);
+      int c = 0;
+      if (valid && (eq & lanemask_lt()) == 0ull) c = atomicAdd(&cnt_we[wave * E + e], (int)__popcll(eq));
+      const int src = valid ? (__ffsll((unsigned long long)eq) - 1) : lane;
+      c = __shfl(c, src);
+      if (valid) rank[p] = c + (int)__popcll(eq & lanemask_lt());
+    }
+  }
+  __syncthreads();
+  // exclusive scan of cnt_we in (expert, wavefront) order; expert e's list starts at s_estart[e]
+  {
+    const int n = nwaves * E;
+    const int per_t = (n + bd - 1) / bd;
+    const int lo = min(n, tid * per_t), hi = min(n, lo + per_t);
+    int sv = 0;
+    for (int i = lo; i < hi; ++i) sv += cnt_we[(i % nwaves) * E + i / nwaves];
+    int ex, d0, tot, d1;
+    block_excl_scan2(sv, 0, ex, d0, tot, d1, s_red);
+    int run = ex;
+    for (int i = lo; i < hi; ++i) {
+      const int idx = (i % nwaves) * E + i / nwaves;
+      const int c = cnt_we[idx];
+      if (i % nwaves == 0) s_estart[i / nwaves] = run;
+      cnt_we[idx] = run;
+      run += c;
+    }
+    if (tid == 0) s_estart[E] = P;
+  }
+  __syncthreads();
+  for (int p = tid; p < P; p += bd) elist[cnt_we[(p / PP) * E + tk[p]] + rank[p]] = p;
+  __syncthreads();
+
   const int nbits = 32 - __clz(nA);  // bits of a key in [0, nA]
 
-  // phase 1
+  // phase D: counts per (expert, adapter) bucket over each expert's list
   for (int e = wave; e < E; e += nwaves) {
-    for (int base = 0; base < T; base += 64) {
-      const int t = base + lane;
-      bool mem = false;
-      if (t < T)
-        for (int j = 0; j < k; ++j) mem |= (tk[t * k + j] == e);
-      if (__ballot(mem) == 0ull) continue;
-      const int key = mem ? adapter_of(t) + 1 : 0;
-      const uint64_t eq = match_key(mem, key, nbits);
-      if (mem && (eq & lanemask_lt()) == 0ull) atomicAdd(&cnt[e * nb1 + key], (int)__popcll(eq));
+    const int i1 = s_estart[e + 1];
+    for (int base = s_estart[e]; base < i1; base += 64) {
+      const int i = base + lane;
+      const bool valid = i < i1;
+      const int key = valid ? adl[elist[i] / k] + 1 : 0;
+      const uint64_t eq = match_key(valid, key, nbits);
+      if (valid && (eq & lanemask_lt()) == 0ull) atomicAdd(&cnt[e * nb1 + key], (int)__popcll(eq));
     }
   }
   __syncthreads();
@@ -319,27 +359,18 @@ __global__ __launch_bounds__(1024) void align_kernel(AlignArgs a) {
 
   // phase 4
   for (int e = wave; e < E; e += nwaves) {
-    for (int base = 0; base < T; base += 64) {
-      const int t = base + lane;
-      bool mem = false;
-      int jj = 0;
-      if (t < T)
-        for (int j = 0; j < k; ++j)
-          if (tk[t * k + j] == e) {
-            mem = true;
-            jj = j;
-          }
-      if (__ballot(mem) == 0ull) continue;
-      const int key = mem ? adapter_of(t) + 1 : 0;
-      const uint64_t eq = match_key(mem, key, nbits);
+    const int i1 = s_estart[e + 1];
+    for (int base = s_estart[e]; base < i1; base += 64) {
+      const int i = base + lane;
+      const bool valid = i < i1;
+      const int p = valid ? elist[i] : 0;
+      const int key = valid ? adl[p / k] + 1 : 0;
+      const uint64_t eq = match_key(valid, key, nbits);
       int cur = 0;
-      if (mem && (eq & lanemask_lt()) == 0ull) cur = atomicAdd(&cnt[e * nb1 + key], (int)__popcll(eq));
-      const int src = mem ? (__ffsll((unsigned long long)eq) - 1) : lane;
+      if (valid && (eq & lanemask_lt()) == 0ull) cur = atomicAdd(&cnt[e * nb1 + key], (int)__popcll(eq));
+      const int src = valid ? (__ffsll((unsigned long long)eq) - 1) : lane;
       cur = __shfl(cur, src);
-      if (mem) {
-        const int pos = start[e * nb1 + key] + cur + (int)__popcll(eq & lanemask_lt());
-        a.sorted_pairs[pos] = t * k + jj;
-      }
+      if (valid) a.sorted_pairs[start[e * nb1 + key] + cur + (int)__popcll(eq & lanemask_lt())] = p;
     }
   }
 }

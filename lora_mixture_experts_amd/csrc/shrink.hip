@@ -11,9 +11,9 @@
 // tile belong to one expert and are sorted by adapter, so the adapters of a tile form
 // contiguous runs; each run is one 16 x r x K MFMA product against A[adapter][expert]
 // (rows of the tile outside the run are computed and dropped). The four wavefronts of the
-// workgroup take interleaved 128-wide K steps of the split and are summed through LDS. The
-// partial sums of split s go to zpart[s]; consumers add the S parts in order, so the result
-// does not depend on scheduling.
+// workgroup take different runs, each over the split's whole K range. The partial sums of
+// split s go to zpart[s]; consumers add the S parts in order, so the result does not depend
+// on scheduling.
 #include "common.h"
 #include "kernels.h"
 
@@ -28,19 +28,36 @@ __global__ __launch_bounds__(256) void lora_shrink_kernel(ShrinkArgs a) {
   if (row0 >= nblk * a.bm) return;
   const int e = a.block_expert[row0 / a.bm];
 
-  __shared__ int s_pair[16], s_ad[16];
-  __shared__ float red[4][16][65];
+  // adapter runs of the tile: run_lo[i]..run_hi[i] share adapter run_ad[i]
+  __shared__ int s_pair[16], s_ad[16], s_nrun, s_lo[16], s_hi[16], s_rad[16];
   if (tid < 16) {
     const int p = a.sorted_pairs[row0 + tid];
     s_pair[tid] = p;
     s_ad[tid] = p >= 0 ? sanitize_adapter(a.adapter_ids[p / a.k], a.nA) : -1;
   }
   __syncthreads();
+  if (tid == 0) {
+    int n = 0;
+    for (int i = 0; i < 16;) {
+      const int ad = s_ad[i];
+      int j = i + 1;
+      while (j < 16 && s_ad[j] == ad) ++j;
+      if (ad >= 0) {
+        s_lo[n] = i;
+        s_hi[n] = j;
+        s_rad[n] = ad;
+        ++n;
+      }
+      i = j;
+    }
+    s_nrun = n;
+  }
+  __syncthreads();
 
   const int K = a.K, r = a.r;
   const int nks = K / 128;
   const int per = (nks + a.S - 1) / a.S;
-  const int ks0 = s * per, ks1 = min(nks, ks0 + per);
+  const int ks0 = min(nks, s * per), ks1 = min(nks, ks0 + per);
   const int m = lane & 15, kq = lane >> 4;
   const int n_ct = r < 16 ? 1 : r / 16;
 
@@ -55,56 +72,47 @@ __global__ __launch_bounds__(256) void lora_shrink_kernel(ShrinkArgs a) {
                : (uint32_t)((GATHER ? (size_t)(p / a.k) : (size_t)(row0 + m)) * K * 2);
   }
 
-  int i = 0;
-  while (i < 16) {
-    const int ad = s_ad[i];
-    if (ad < 0) {
-      ++i;
-      continue;
-    }
-    int j = i + 1;
-    while (j < 16 && s_ad[j] == ad) ++j;
-
+  // Each wavefront owns whole runs (run index = wave, wave + 4, ...) over this split's K range;
+  // no cross-wave reduction is needed.
+  for (int run = wave; run < s_nrun; run += 4) {
+    const int lo = s_lo[run], hi = s_hi[run], ad = s_rad[run];
+    const uint16_t* Abase = a.Aw + ((size_t)ad * a.E + e) * (size_t)r * K;
     f32x4 acc[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const uint16_t* Abase = a.Aw + ((size_t)ad * a.E + e) * (size_t)r * K;
-    for (int ks = ks0 + wave; ks < ks1; ks += 4) {
+    for (int ks = ks0; ks < ks1; ++ks) {
       const int kb = ks * 128 + kq * 32;
-      u32x4 xa[4];
+      u32x4 xa[4], bw[4][4];
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        xa[jj] = bufld16(xr, xo + 2u * (uint32_t)(kb + 8 * jj));
+      for (int jj = 0; jj < 4; ++jj) xa[jj] = bufld16(xr, xo + 2u * (uint32_t)(kb + 8 * jj));
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        // columns q >= r (rank 8) re-read row r-1; they are never stored
+        const int q = min(c * 16 + m, r - 1);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          bw[c][jj] = c < n_ct ? ldg16(Abase + (size_t)q * K + kb + 8 * jj) : u32x4{0u, 0u, 0u, 0u};
+      }
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         if (c < n_ct) {
-          const int q = min(c * 16 + m, r - 1);  // columns q >= r (rank 8) are never stored
-          u32x4 bw[4];
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) bw[jj] = ldg16(Abase + (size_t)q * K + kb + 8 * jj);
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) acc[c] = mfma16(xa[jj], bw[jj], acc[c]);
+          for (int jj = 0; jj < 4; ++jj) acc[c] = mfma16(xa[jj], bw[c][jj], acc[c]);
         }
       }
     }
     // acc[c] holds rows 4*(lane/16)+v of column q = 16c + lane%16
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      if (c < n_ct) {
+      const int q = c * 16 + m;
+      if (c < n_ct && q < r) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) red[wave][4 * kq + v][c * 16 + m] = acc[c][v];
+        for (int v = 0; v < 4; ++v) {
+          const int row = 4 * kq + v;
+          if (row >= lo && row < hi) a.zpart[((size_t)s * a.cap + row0 + row) * r + q] = acc[c][v];
+        }
       }
     }
-    __syncthreads();
-    for (int idx = tid; idx < 16 * r; idx += 256) {
-      const int row = idx / r, q = idx - row * r;
-      if (row >= i && row < j) {
-        const float z = (red[0][row][q] + red[1][row][q]) + (red[2][row][q] + red[3][row][q]);
-        a.zpart[((size_t)s * a.cap + row0 + row) * r + q] = z;
-      }
-    }
-    __syncthreads();
-    i = j;
   }
 }
 
