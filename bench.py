@@ -190,7 +190,9 @@ def main():
         achieved = work["gateup_bytes"] / gu_s / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS}
-    roof["kernel"] = "skinny_gemm_kernel (gate_up)"
+    # the library takes the LDS-tiled GEMM above 24 rows per expert on average
+    tiled = w.T * w.topk > 24 * w.n_experts
+    roof["kernel"] = ("tiled_gemm_kernel" if tiled else "skinny_gemm_kernel") + " (gate_up)"
     roof["traffic"] = measured_traffic(args.workload)
 
     layer_s = statistics.median(step_ms) * 1e-3

@@ -61,7 +61,9 @@ extern "C" {
 #define MOELORA_FLAG_ADAPTER_RANGE 2u
 
 /* Layer sizes. Supported: T >= 0; hidden and inter positive multiples of 128; n_experts in
- * [1, 1024]; n_adapters >= 1; rank in {8, 16, 32, 64}; 1 <= topk <= min(n_experts, 16). */
+ * [1, 1024]; n_adapters >= 1; rank in {8, 16, 32, 64}; 1 <= topk <= min(n_experts, 16).
+ * Buffers the kernels address with 32-bit offsets must stay under 2 GiB: x (T x hidden), the
+ * activations ((T*topk + 256*n_experts) x inter) and one expert's W1 (2*inter x hidden). */
 typedef struct {
   int32_t T, hidden, inter, n_experts, n_adapters, rank;
 } moe_lora_dims;

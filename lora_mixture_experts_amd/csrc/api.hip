@@ -34,6 +34,8 @@ int validate_dims(const moe_lora_dims* d, int32_t topk) {
   if ((int64_t)d->T * d->hidden * 2 >= ((int64_t)1 << 31)) return MOELORA_EINVAL_DIMS;
   if ((P + (int64_t)d->n_experts * kMaxBM) * d->inter * 2 >= ((int64_t)1 << 31))
     return MOELORA_EINVAL_DIMS;
+  // so is one expert's slice of W1 (2I x h, the larger of the two projections)
+  if ((int64_t)2 * d->inter * d->hidden * 2 >= ((int64_t)1 << 31)) return MOELORA_EINVAL_DIMS;
   return MOELORA_OK;
 }
 
@@ -90,11 +92,16 @@ PathPlan pick_path(int64_t P, int E, int h, int I) {
   PathPlan pl;
   pl.tiled = mean > 24.0;
   pl.nt = mean <= 12.0 ? 1 : (mean <= 24.0 ? 2 : 4);
-  const TiledConfig t64{64, 128, 32, 64, 2}, t128{128, 128, 64, 64, 2};
-  pl.tc = mean < 192.0 ? t64 : t128;
+  // Row-block size against padding: an expert wastes up to bm - 1 rows, so the 256-row tile
+  // (most MFMA work per loaded byte) only pays once experts hold several hundred rows.
+  const TiledConfig t64{64, 128, 32, 64, 64, 2}, t128{128, 128, 64, 64, 64, 2},
+      t256{256, 256, 128, 128, 64, 2};
+  const bool fits256 = (2 * I) % 256 == 0 && h % 256 == 0;
+  pl.tc = mean < 192.0 ? t64 : (mean < 768.0 || !fits256 ? t128 : t256);
   pl.tc_dn = pl.tc;
-  // MOELORA_TILED="bm,bn,wm,wn,depth[,bm_d,bn_d,wm_d,wn_d,depth_d]" forces tiles (experiments)
-  static int forced = -1;  // -1 unread, 0 none, 1 skinny, 2 tiled
+  // MOELORA_TILED="bm,bn,wm,wn,bk,nst[;bm,bn,wm,wn,bk,nst]" forces the tiles of gate_up (and of
+  // down when a second set with the same bm follows) for experiments
+  static int forced = -1;  // -1 unread, 0 none, 1 skinny, 2 tiled, 3/4 skinny with 1/2 tiles
   static TiledConfig ft, ftd;
   if (forced < 0) {
     forced = 0;
@@ -104,13 +111,18 @@ PathPlan pick_path(int64_t P, int E, int h, int I) {
     if (env && !strcmp(env, "skinny2")) forced = 4;
     const char* tenv = getenv("MOELORA_TILED");
     if (tenv) {
-      int v[10] = {0};
-      const int n = sscanf(tenv, "%d,%d,%d,%d,%d,%d,%d,%d,%d,%d", &v[0], &v[1], &v[2], &v[3], &v[4],
-                           &v[5], &v[6], &v[7], &v[8], &v[9]);
-      if (n >= 5) {
-        ft = TiledConfig{v[0], v[1], v[2], v[3], v[4]};
-        ftd = n >= 10 ? TiledConfig{v[5], v[6], v[7], v[8], v[9]} : ft;
-        if (ftd.bm == ft.bm) forced = 2;
+      auto parse = [](const char* str, TiledConfig* c) {
+        int v[6] = {0, 0, 0, 0, 64, 2};
+        const int n = sscanf(str, "%d,%d,%d,%d,%d,%d", &v[0], &v[1], &v[2], &v[3], &v[4], &v[5]);
+        *c = TiledConfig{v[0], v[1], v[2], v[3], v[4], v[5]};
+        return n >= 4;
+      };
+      if (parse(tenv, &ft)) {
+        ftd = ft;
+        const char* semi = strchr(tenv, ';');
+        TiledConfig d2;
+        if (semi && parse(semi + 1, &d2) && d2.bm == ft.bm) ftd = d2;
+        forced = 2;
       }
     }
   }

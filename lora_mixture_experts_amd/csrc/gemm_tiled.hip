@@ -10,296 +10,42 @@
 // adapter's weights in one batched operation.
 //
 // C[m][n] = sum_k X[m][k] W[n][k] for the BM token rows of one row block of the sorted layout
-// (all of one expert) and BN output features, on 32x32x16 bf16 MFMAs (the 16x16x32 form runs at
-// half their rate on CDNA4). Both operands are K-contiguous, so every fragment (32 rows x 8
-// consecutive k per lane) is one 16-byte LDS read. Tiles live row-major in LDS, 64 k per row,
-// with the 16-byte chunk index XOR-swizzled by the row; LDS is double-buffered with one barrier
-// per 64-wide K step, global tiles are prefetched DEPTH steps ahead in registers, and the
-// fragments of the next 16-wide sub-step are read while the current sub-step's MFMAs run.
+// (all of one expert) and BN output features. The main loop (TilePipe) loads both operand
+// tiles straight from HBM into a ring of LDS stages and runs 32x32x16 bf16 MFMAs on them (the
+// 16x16x32 form runs at half their rate on CDNA4).
 //
 // gate_up: the weight rows of each wave's column range are [gate i .. | up i ..] for the same
 // intermediate columns i, so each lane holds gate and up of the same act element and
 // SiLU-and-mul runs in registers, after the LoRA expand is added.
 //
-// LoRA expand (both projections): rows are sorted by adapter inside an expert, so each 32-row
-// MFMA group holds a few contiguous adapter runs. For every run the group's z rows (other rows
-// zero) multiply B[adapter][expert] as extra MFMAs over K = r: the segment's adapter weights are
-// read once per group, not per token. z is split into bf16 high and low parts (two MFMAs) so
-// the term keeps ~16 mantissa bits.
+// LoRA expand (both projections): rows are sorted by adapter inside an expert, so the rows of a
+// tile form a few contiguous adapter runs. For every run, the tile's columns of
+// B[adapter][expert] are loaded into LDS once and every 32-row MFMA group the run overlaps adds
+// (z restricted to the run's rows) x B as extra MFMAs over K = r: a segment's adapter weights
+// are read once per tile, not per token. z is split into bf16 high and low parts (two MFMAs)
+// so the term keeps ~16 mantissa bits.
 #include "common.h"
 #include "kernels.h"
+#include "tile_pipeline.h"
 
 namespace moelora {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-// D += A(32x16) * B(16x32). Lane l supplies row (l % 32) of A and column (l % 32) of B, 8
-// reduction elements each, in the same slot order; lane l receives D rows
-// 8*(v/4) + 4*(l/32) + (v%4), v < 16, of column (l % 32).
-__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
-}
-
-template <bool GATEUP, int BM, int BN, int WM, int WN, int DEPTH, int OCC>
-__global__ __launch_bounds__(256, OCC) void tiled_gemm_kernel(GemmArgs a, int n_tiles_n,
-                                                              int grid_total) {
-  constexpr int BK = 64;
-  constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
-  static_assert(WAVES_M * WAVES_N == 4, "four wavefronts per workgroup");
-  constexpr int FM = WM / 32, FN = WN / 32;
-  constexpr int CPR = BK / 8;                  // 16-byte chunks per tile row
-  constexpr int CA = BM * CPR / 256;           // chunks of the token tile per thread
-  constexpr int CB = BN * CPR / 256;           // chunks of the weight tile per thread
-  static_assert(CA * 256 == BM * CPR && CB * 256 == BN * CPR, "tile must split over 256 threads");
-  static_assert(!GATEUP || FN % 2 == 0, "gate_up needs gate and up halves per wave");
-  // a sub-step's reads are all complete before its first MFMA and the next sub-step's reads are
-  // interleaved after it, so at most FM + FN reads are outstanding (the LDS counter holds 15)
-  static_assert(FM + FN <= 15, "one sub-step of fragment reads must fit the LDS counter");
-
-  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];  // 2 * (BM + BN) * BK
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-
-  // Tile order. Hardware workgroup ids go round-robin over the 8 XCDs, so each XCD is given a
-  // contiguous range of logical tiles; the ~64 workgroups an XCD runs at once then cover a
-  // group of GROUP_M row blocks x GROUP_N column tiles, and every token tile and weight tile
-  // fetched into that XCD's L2 serves GROUP_N resp. GROUP_M workgroups (instead of streaming
-  // every token tile once per column tile).
-  constexpr int GROUP_M = 8, GROUP_N = 8;
-  const int hw = blockIdx.x;
-  const int logical = (hw & 7) * (grid_total >> 3) + (hw >> 3);
-  const int groups_m = (a.n_blocks_max + GROUP_M - 1) / GROUP_M;
-  const int grp = logical / (GROUP_M * GROUP_N), within = logical % (GROUP_M * GROUP_N);
-  const int blk = (grp % groups_m) * GROUP_M + within % GROUP_M;
-  const int ntile = (grp / groups_m) * GROUP_N + within / GROUP_M;
-  if (ntile >= n_tiles_n || blk >= a.n_blocks_max || blk >= *a.n_blocks) return;
-  const int e = a.block_expert[blk];
-  const int K = a.K;
-  const size_t N = (size_t)a.N;  // gate_up: I; down: h
-  const int row0 = blk * BM;
-
-  // ---- per-thread global load plan (fixed over K) ----
-  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.X, a.x_bytes);
-  uint32_t xo[CA];
-  int a_lds[CA];
-#pragma unroll
-  for (int i = 0; i < CA; ++i) {
-    const int q = tid + 256 * i;
-    const int row = q / CPR, chk = q % CPR;
-    a_lds[i] = row * BK + 8 * (chk ^ (row & 7));
-    const int srow = row0 + row;
-    const int p = a.sorted_pairs[srow];
-    xo[i] = p < 0 ? kOutOfRange
-                  : (uint32_t)((GATEUP ? (size_t)(p / a.k) : (size_t)srow) * K * 2) + 16u * chk;
-  }
-  const uint16_t* wsrc[CB];
-  int b_lds[CB];
-#pragma unroll
-  for (int i = 0; i < CB; ++i) {
-    const int q = tid + 256 * i;
-    const int row = q / CPR, chk = q % CPR;
-    b_lds[i] = row * BK + 8 * (chk ^ (row & 7));
-    size_t wrow;
-    if (GATEUP) {
-      const int g = row / WN, rr = row % WN;
-      const size_t col = (size_t)ntile * (BN / 2) + g * (WN / 2) + (rr % (WN / 2));
-      wrow = (size_t)e * 2 * N + (rr < WN / 2 ? col : N + col);
-    } else {
-      wrow = (size_t)e * N + (size_t)ntile * BN + row;
-    }
-    wsrc[i] = a.W + wrow * K + 8 * chk;
-  }
-
-  auto lds_a = [&](int buf) { return lds + buf * (BM + BN) * BK; };
-  auto lds_b = [&](int buf) { return lds + buf * (BM + BN) * BK + BM * BK; };
-
-  f32x16 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-  const int nks = K / BK;
-  u32x4 sa0[CA], sb0[CB], sa1[CA], sb1[CB];
-  // Loads are unconditional (past the end they re-read the last step), which keeps the
-  // compiler's outstanding-load count exact.
-#define MOELORA_GLOAD(SA, SB, KS)                                                         \
-  do {                                                                                    \
-    const int ks_ = min((KS), nks - 1);                                                   \
-    _Pragma("unroll") for (int i = 0; i < CA; ++i) SA[i] =                                \
-        bufld16(xr, xo[i] + 2u * (uint32_t)(ks_ * BK));                                   \
-    _Pragma("unroll") for (int i = 0; i < CB; ++i) SB[i] = ldg16(wsrc[i] + (size_t)ks_ * BK); \
-  } while (0)
-#define MOELORA_LSTORE(SA, SB, BUF)                                                       \
-  do {                                                                                    \
-    uint16_t* A_ = lds_a(BUF);                                                            \
-    uint16_t* B_ = lds_b(BUF);                                                            \
-    _Pragma("unroll") for (int i = 0; i < CA; ++i)                                        \
-        *reinterpret_cast<u32x4*>(A_ + a_lds[i]) = SA[i];                                 \
-    _Pragma("unroll") for (int i = 0; i < CB; ++i)                                        \
-        *reinterpret_cast<u32x4*>(B_ + b_lds[i]) = SB[i];                                 \
-  } while (0)
-
+// Store of a finished tile: SiLU-and-mul (gate_up, into act) or the plain store (down, into the
+// pair's row of D). Lane l holds rows 8*(v/4) + 4*(l/32) + (v%4) of each 32-row group and
+// column (l % 32) of each 32-column fragment.
+template <bool GATEUP, int BN, int WM, int WN, int FM, int FN>
+__device__ __forceinline__ void tiled_store(const GemmArgs& a, f32x16 (&acc)[FM][FN], int row0,
+                                            int wm, int wn, int ntile, int lane) {
+  const size_t N = (size_t)a.N;
   const int fr = lane & 31, fg = lane >> 5;
-  // Fragments of 16-wide sub-step j of a 64-wide K step: chunk 2j + (lane / 32).
-  auto read_frags = [&](const uint16_t* A, const uint16_t* B, int j, u32x4* af, u32x4* bf) {
-    const int chunk = 2 * j + fg;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int r = wm * WM + i * 32 + fr;
-      af[i] = *reinterpret_cast<const u32x4*>(A + r * BK + 8 * (chunk ^ (r & 7)));
-    }
-#pragma unroll
-    for (int i = 0; i < FN; ++i) {
-      const int r = wn * WN + i * 32 + fr;
-      bf[i] = *reinterpret_cast<const u32x4*>(B + r * BK + 8 * (chunk ^ (r & 7)));
-    }
-  };
-  auto mfmas = [&](const u32x4* af, const u32x4* bf) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int jn = 0; jn < FN; ++jn) acc[i][jn] = mfma32(af[i], bf[jn], acc[i][jn]);
-  };
-  // Four sub-steps; sub-step j+1's reads are issued between sub-step j's MFMAs.
-  auto compute = [&](int buf) {
-    const uint16_t* A = lds_a(buf);
-    const uint16_t* B = lds_b(buf);
-    u32x4 af0[FM], bf0[FN], af1[FM], bf1[FN];
-    read_frags(A, B, 0, af0, bf0);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      u32x4* an = (j & 1) ? af0 : af1;
-      u32x4* bn = (j & 1) ? bf0 : bf1;
-      const u32x4* ac = (j & 1) ? af1 : af0;
-      const u32x4* bc = (j & 1) ? bf1 : bf0;
-      if (j < 3) read_frags(A, B, j + 1, an, bn);
-      mfmas(ac, bc);
-      if (j < 3) {
-        constexpr int NR = FM + FN;
-        constexpr int NM = FM * FN;
-        constexpr int PAIRS = NR < NM ? NR : NM;
-#pragma unroll
-        for (int t = 0; t < PAIRS; ++t) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-        }
-        if (NR > NM) __builtin_amdgcn_sched_group_barrier(0x100, NR - NM, 0);
-        if (NM > NR) __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  MOELORA_GLOAD(sa0, sb0, 0);
-  if (DEPTH == 2) MOELORA_GLOAD(sa1, sb1, 1);
-  MOELORA_LSTORE(sa0, sb0, 0);
-  __syncthreads();
-  // sched_barrier(0) pins the phase order (the compiler would otherwise sink the prefetch below
-  // the MFMAs). The LDS stores are unconditional as well (past the end they fill a buffer nobody
-  // reads), so the in-flight load count stays exact.
-  if (DEPTH == 2) {
-    // K is a multiple of 128, so the number of 64-wide steps is even
-    for (int ks = 0; ks < nks; ks += 2) {
-      MOELORA_GLOAD(sa0, sb0, ks + 2);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(0);
-      __builtin_amdgcn_sched_barrier(0);
-      MOELORA_LSTORE(sa1, sb1, 1);
-      __syncthreads();
-      MOELORA_GLOAD(sa1, sb1, ks + 3);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(1);
-      __builtin_amdgcn_sched_barrier(0);
-      MOELORA_LSTORE(sa0, sb0, 0);
-      __syncthreads();
-    }
-  } else {
-    for (int ks = 0; ks < nks; ++ks) {
-      const int buf = ks & 1;
-      MOELORA_GLOAD(sa1, sb1, ks + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(buf);
-      __builtin_amdgcn_sched_barrier(0);
-      MOELORA_LSTORE(sa1, sb1, buf ^ 1);
-      __syncthreads();
-    }
-  }
-#undef MOELORA_GLOAD
-#undef MOELORA_LSTORE
-
-  // ---- epilogue ----
-  // Weight row (within W1 or W2 of expert e) of column fragment jn for this lane's column.
-  auto wrow_of = [&](int jn) -> size_t {
-    if (GATEUP) {
-      const int half = FN / 2;
-      const size_t col = (size_t)ntile * (BN / 2) + wn * (WN / 2) + (jn % half) * 32 + fr;
-      return jn < half ? col : N + col;
-    }
+  // column of fragment jn: gate_up act column (gate and up halves share it); down output column
+  auto col_of = [&](int jn) -> size_t {
+    if (GATEUP) return (size_t)ntile * (BN / 2) + wn * (WN / 2) + (jn % (FN / 2)) * 32 + fr;
     return (size_t)ntile * BN + wn * WN + jn * 32 + fr;
   };
-
-  const int r = a.r;
-  const int64_t zstride = a.cap * r;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
-    const int grow0 = row0 + wm * WM + i * 32;  // first sorted row of this 32-row group
-    int ad = -1;
-    {
-      const int p = a.sorted_pairs[grow0 + fr];
-      if (p >= 0) ad = sanitize_adapter(a.adapter_ids[p / a.k], a.nA);
-    }
-    uint64_t pending = __ballot(lane < 32 && ad >= 0);
-    while (pending) {
-      const int first = __ffsll((unsigned long long)pending) - 1;
-      const int acur = __shfl(ad, first);
-      const uint64_t run = __ballot(lane < 32 && ad == acur);
-      pending &= ~run;
-      const bool mine = (run >> fr) & 1ull;
-      const uint16_t* Bad = a.Bw + ((size_t)acur * a.E + e) * (GATEUP ? 2 * N : N) * r;
-      for (int q0 = 0; q0 < r; q0 += 16) {
-        const int q = q0 + 8 * fg;  // this lane's 8 reduction slots
-        float z[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) z[t] = 0.f;
-        if (mine && q < r) {
-          const float* zr = a.zpart + (size_t)(grow0 + fr) * r + q;
-          for (int s = 0; s < a.S; ++s) {
-            const f32x4 lo = *reinterpret_cast<const f32x4*>(zr + s * zstride);
-            const f32x4 hi = *reinterpret_cast<const f32x4*>(zr + s * zstride + 4);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              z[t] += lo[t];
-              z[4 + t] += hi[t];
-            }
-          }
-        }
-        u32x4 zh, zl;
-        {
-          uint32_t hb[8], lb[8];
-#pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            hb[t] = f32_to_bf16_bits(z[t]);
-            lb[t] = f32_to_bf16_bits(z[t] - __uint_as_float(hb[t] << 16));
-          }
-          zh = u32x4{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16),
-                     hb[6] | (hb[7] << 16)};
-          zl = u32x4{lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16), lb[4] | (lb[5] << 16),
-                     lb[6] | (lb[7] << 16)};
-        }
-#pragma unroll
-        for (int jn = 0; jn < FN; ++jn) {
-          const u32x4 bv = q < r ? ldg16(Bad + wrow_of(jn) * r + q) : u32x4{0u, 0u, 0u, 0u};
-          acc[i][jn] = mfma32(zh, bv, acc[i][jn]);
-          acc[i][jn] = mfma32(zl, bv, acc[i][jn]);
-        }
-      }
-    }
-    // store: lane holds rows grow0 + 8*(v/4) + 4*(lane/32) + (v%4) of column (lane % 32)
+    const int grow0 = row0 + wm * WM + i * 32;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int srow = grow0 + 8 * (v / 4) + 4 * fg + (v % 4);
@@ -310,20 +56,271 @@ __global__ __launch_bounds__(256, OCC) void tiled_gemm_kernel(GemmArgs a, int n_
         for (int jn = 0; jn < FN / 2; ++jn) {
           const float g = acc[i][jn][v], u = acc[i][jn + FN / 2][v];
           const float hv = g / (1.f + __expf(-g)) * u;
-          a.act_out[(size_t)srow * N + wrow_of(jn)] = (uint16_t)f32_to_bf16_bits(hv);
+          a.act_out[(size_t)srow * N + col_of(jn)] = (uint16_t)f32_to_bf16_bits(hv);
         }
       } else {
 #pragma unroll
-        for (int jn = 0; jn < FN; ++jn) a.d_out[(size_t)p * N + wrow_of(jn)] = acc[i][jn][v];
+        for (int jn = 0; jn < FN; ++jn) a.d_out[(size_t)p * N + col_of(jn)] = acc[i][jn][v];
       }
     }
   }
 }
 
-template <bool GATEUP, int BM, int BN, int WM, int WN, int DEPTH, int OCC>
+// LoRA expand of a whole tile through LDS (used after the LDS-staged main loop, whose LDS is
+// free by then). The tile's rows are sorted by adapter, so they form runs of one adapter; for
+// each run the tile's columns of B[adapter][expert] (BN rows x r, r-contiguous) are loaded
+// straight into LDS, up to as many runs at once as fit, with one wait per batch, and every
+// 32-row group the run overlaps adds (z restricted to the run's rows) x B over K = r. Each
+// wavefront first loads the z rows of its groups (summing the split-K parts) and keeps them as
+// bf16 high and low parts in registers.
+template <bool GATEUP, int BM, int BN, int WM, int WN, int FM, int FN, uint32_t LDS_BYTES>
+__device__ __forceinline__ void lora_expand_lds(const GemmArgs& a, f32x16 (&acc)[FM][FN],
+                                                uint16_t* lds, int row0, int wm, int wn,
+                                                int ntile, int e, int wave, int lane) {
+  constexpr int MAXSL = 4;  // 16-wide slices of r (r <= 64)
+  constexpr uint32_t TABLE_BYTES = ((5 * BM + 1) * 4 + 1023) / 1024 * 1024;
+  static_assert(LDS_BYTES >= TABLE_BYTES + BN * 64 * 2, "the B tile of one run must fit");
+  const int r = a.r;
+  const size_t N = (size_t)a.N;
+  const size_t w_rows = GATEUP ? 2 * N : N;
+  const int fr = lane & 31, fg = lane >> 5;
+  int* cp_t = reinterpret_cast<int*>(lds);  // change points of the row adapter
+  int* cp_ad = cp_t + BM;
+  int* s_lo = cp_ad + BM;  // runs with an adapter: tile rows [lo, hi)
+  int* s_hi = s_lo + BM;
+  int* s_ad = s_hi + BM;
+  int* s_n = s_ad + BM;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+
+  __syncthreads();  // every wavefront is done with the main loop's stages
+  if (wave == 0) {
+    int ncp = 0, prev = -2;
+    for (int t0 = 0; t0 < BM; t0 += 64) {
+      const int t = t0 + lane;
+      const int p = a.sorted_pairs[row0 + t];
+      const int ad = p >= 0 ? sanitize_adapter(a.adapter_ids[p / a.k], a.nA) : -1;
+      int before = __shfl(ad, (lane + 63) & 63);
+      if (lane == 0) before = prev;
+      const bool cp = ad != before;
+      const uint64_t m = __ballot(cp);
+      if (cp) {
+        const int pos = ncp + __popcll(m & lanemask_lt());
+        cp_t[pos] = t;
+        cp_ad[pos] = ad;
+      }
+      ncp += __popcll(m);
+      prev = __shfl(ad, 63);
+    }
+    int nrun = 0;
+    for (int j0 = 0; j0 < ncp; j0 += 64) {
+      const int j = j0 + lane;
+      const bool run = j < ncp && cp_ad[j] >= 0;
+      const uint64_t m = __ballot(run);
+      if (run) {
+        const int pos = nrun + __popcll(m & lanemask_lt());
+        s_lo[pos] = cp_t[j];
+        s_hi[pos] = j + 1 < ncp ? cp_t[j + 1] : BM;
+        s_ad[pos] = cp_ad[j];
+      }
+      nrun += __popcll(m);
+    }
+    if (lane == 0) *s_n = nrun;
+  }
+
+  // z of this wavefront's rows: fp32 sum of the split-K parts, kept as bf16 high and low parts.
+  // Loaded half the groups at a time (the fp32 sums of all groups at once would not fit beside
+  // the accumulators).
+  u32x4 zh[FM][MAXSL], zl[FM][MAXSL];
+  constexpr int GH = FM > 1 ? FM / 2 : 1;
+#pragma unroll
+  for (int i0 = 0; i0 < FM; i0 += GH) {
+    float zf[GH][MAXSL][8];
+#pragma unroll
+    for (int i = 0; i < GH; ++i)
+#pragma unroll
+      for (int sl = 0; sl < MAXSL; ++sl)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) zf[i][sl][t] = 0.f;
+    const int64_t zstride = a.cap * r;
+    for (int sp = 0; sp < a.S; ++sp) {
+#pragma unroll
+      for (int i = 0; i < GH; ++i) {
+        const float* zr =
+            a.zpart + sp * zstride + (size_t)(row0 + wm * WM + (i0 + i) * 32 + fr) * r;
+#pragma unroll
+        for (int sl = 0; sl < MAXSL; ++sl) {
+          const int q = 16 * sl + 8 * fg;
+          if (q < r) {
+            const f32x4 lo = *reinterpret_cast<const f32x4*>(zr + q);
+            const f32x4 hi = *reinterpret_cast<const f32x4*>(zr + q + 4);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              zf[i][sl][t] += lo[t];
+              zf[i][sl][4 + t] += hi[t];
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < GH; ++i)
+#pragma unroll
+      for (int sl = 0; sl < MAXSL; ++sl) {
+        uint32_t hb[8], lb[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          hb[t] = f32_to_bf16_bits(zf[i][sl][t]);
+          lb[t] = f32_to_bf16_bits(zf[i][sl][t] - __uint_as_float(hb[t] << 16));
+        }
+        zh[i0 + i][sl] = u32x4{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16),
+                               hb[4] | (hb[5] << 16), hb[6] | (hb[7] << 16)};
+        zl[i0 + i][sl] = u32x4{lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16),
+                               lb[4] | (lb[5] << 16), lb[6] | (lb[7] << 16)};
+      }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __syncthreads();  // run table visible
+  const int nrun = *s_n;
+  if (nrun == 0) return;
+
+  // B tile of one run in LDS: BN rows (the tile's weight rows) x r, the 16-byte chunk index
+  // XOR-swizzled by the row (rows of r/8 chunks; 1 KB load blocks of 512/r rows).
+  const int cpr = r / 8, rpb = 512 / r;
+  const int rsh = 8 / cpr;  // rows per swizzle step
+  auto swz = [&](int row, int c) { return c ^ ((row / rsh) & (cpr - 1)); };
+  const uint32_t run_bytes = (uint32_t)BN * r * 2;
+  const int rb = (int)((LDS_BYTES - TABLE_BYTES) / run_bytes);  // runs per batch (>= 3)
+  const int bpr = BN / rpb;                                      // load blocks per run
+  auto wrow_of_tile_row = [&](int row) -> size_t {
+    if (GATEUP) {
+      const int g = row / WN, rr = row % WN;
+      const size_t col = (size_t)ntile * (BN / 2) + g * (WN / 2) + (rr % (WN / 2));
+      return rr < WN / 2 ? col : N + col;
+    }
+    return (size_t)ntile * BN + row;
+  };
+  const uint16_t* btile = lds + TABLE_BYTES / 2;
+
+  for (int b0 = 0; b0 < nrun; b0 += rb) {
+    const int nb = min(rb, nrun - b0);
+    for (int blk = wave; blk < nb * bpr; blk += 4) {
+      const int kk = blk / bpr, bi = blk % bpr;
+      const int ad = __builtin_amdgcn_readfirstlane(s_ad[b0 + kk]);
+      const int row = bi * rpb + lane / cpr;
+      const int chunk = swz(row, lane % cpr);
+      const u32x4 br = buffer_desc(a.Bw + ((size_t)ad * a.E + e) * w_rows * r,
+                                   (uint32_t)(w_rows * r * 2));
+      lds_dma16(br, (uint32_t)(wrow_of_tile_row(row) * r * 2) + 16u * chunk, 0u,
+                lds0 + TABLE_BYTES + kk * run_bytes + bi * 1024);
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+    for (int kk = 0; kk < nb; ++kk) {
+      const int lo = s_lo[b0 + kk], hi = s_hi[b0 + kk];
+      const uint16_t* bt = btile + kk * (run_bytes / 2);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int g0 = wm * WM + i * 32;
+        if (lo >= g0 + 32 || hi <= g0) continue;
+        const bool in = g0 + fr >= lo && g0 + fr < hi;
+#pragma unroll
+        for (int sl = 0; sl < MAXSL; ++sl) {
+          if (16 * sl >= r) continue;
+          const int c = 2 * sl + fg;
+          const u32x4 zero{0u, 0u, 0u, 0u};
+          const u32x4 za = in ? zh[i][sl] : zero, zb = in ? zl[i][sl] : zero;
+#pragma unroll
+          for (int jn = 0; jn < FN; ++jn) {
+            const int n = wn * WN + jn * 32 + fr;
+            const u32x4 bv = 8 * c < r ? *reinterpret_cast<const u32x4*>(bt + n * r + 8 * swz(n, c))
+                                       : zero;
+            acc[i][jn] = mfma32(za, bv, acc[i][jn]);
+            acc[i][jn] = mfma32(zb, bv, acc[i][jn]);
+          }
+        }
+      }
+    }
+    __syncthreads();  // the next batch overwrites the B tiles
+  }
+}
+
+template <bool GATEUP, int BM, int BN, int WM, int WN, int BK, int NST>
+__global__ __launch_bounds__(256, 1) void tiled_gemm_kernel(GemmArgs a, int n_tiles_n,
+                                                            int grid_total) {
+  using Pipe = TilePipe<BM, BN, WM, WN, BK, NST>;
+  constexpr int FM = Pipe::FM, FN = Pipe::FN, NA = Pipe::NA, NB = Pipe::NB;
+  static_assert(!GATEUP || FN % 2 == 0, "gate_up needs gate and up halves per wave");
+
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];  // Pipe::LDS_BYTES
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / Pipe::WAVES_N, wn = wave % Pipe::WAVES_N;
+
+  // Tile order. Hardware workgroup ids go round-robin over the 8 XCDs, so each XCD is given a
+  // contiguous range of logical tiles; the workgroups an XCD runs at once then cover a group of
+  // GROUP_M row blocks x GROUP_N column tiles, and every token tile and weight tile fetched
+  // into that XCD's L2 serves several workgroups.
+  constexpr int GROUP_M = 8, GROUP_N = 8;
+  const int hw = blockIdx.x;
+  const int logical = (hw & 7) * (grid_total >> 3) + (hw >> 3);
+  const int groups_m = (a.n_blocks_max + GROUP_M - 1) / GROUP_M;
+  const int grp = logical / (GROUP_M * GROUP_N), within = logical % (GROUP_M * GROUP_N);
+  const int blk = (grp % groups_m) * GROUP_M + within % GROUP_M;
+  const int ntile = (grp / groups_m) * GROUP_N + within / GROUP_M;
+  if (ntile >= n_tiles_n || blk >= a.n_blocks_max || blk >= *a.n_blocks) return;
+  const int e = a.block_expert[blk];
+  const int K = a.K;
+  const size_t N = (size_t)a.N;
+  const int row0 = blk * BM;
+  const size_t w_rows = GATEUP ? 2 * N : N;  // weight rows of one expert
+
+  // byte offsets of the chunk each lane loads at K step 0 (padding rows: out of range, zeros)
+  const int chunk = Pipe::load_chunk(lane);
+  uint32_t xo[NA], wo[NB];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const int srow = row0 + Pipe::load_row(i, wave, lane);
+    const int p = a.sorted_pairs[srow];
+    xo[i] = p < 0 ? kOutOfRange
+                  : (uint32_t)((GATEUP ? (size_t)(p / a.k) : (size_t)srow) * K * 2) + 16u * chunk;
+  }
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int row = Pipe::load_row(i, wave, lane);
+    size_t wrow;
+    if (GATEUP) {
+      const int g = row / WN, rr = row % WN;
+      const size_t col = (size_t)ntile * (BN / 2) + g * (WN / 2) + (rr % (WN / 2));
+      wrow = rr < WN / 2 ? col : N + col;
+    } else {
+      wrow = (size_t)ntile * BN + row;
+    }
+    wo[i] = (uint32_t)(wrow * K * 2) + 16u * chunk;
+  }
+  const u32x4 xr = buffer_desc(a.X, a.x_bytes);
+  const u32x4 wr = buffer_desc(a.W + (size_t)e * w_rows * K, (uint32_t)(w_rows * K * 2));
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  Pipe::run(acc, xr, xo, wr, wo, lds, K, wave, lane);
+
+  lora_expand_lds<GATEUP, BM, BN, WM, WN, FM, FN, Pipe::LDS_BYTES>(a, acc, lds, row0, wm, wn,
+                                                                    ntile, e, wave, lane);
+  tiled_store<GATEUP, BN, WM, WN, FM, FN>(a, acc, row0, wm, wn, ntile, lane);
+}
+
+template <bool GATEUP, int BM, int BN, int WM, int WN, int BK, int NST>
 hipError_t launch_tiled_t(const GemmArgs& a, int n_tiles_n, int total, hipStream_t stream) {
-  constexpr int lds_bytes = 2 * (BM + BN) * 64 * 2;
-  auto kern = tiled_gemm_kernel<GATEUP, BM, BN, WM, WN, DEPTH, OCC>;
+  constexpr int lds_bytes = TilePipe<BM, BN, WM, WN, BK, NST>::LDS_BYTES;
+  static_assert(lds_bytes <= kLdsBytes, "LDS stages must fit");
+  auto kern = tiled_gemm_kernel<GATEUP, BM, BN, WM, WN, BK, NST>;
   static bool attr_set[64] = {};
   int dev = 0;
   hipError_t err = hipGetDevice(&dev);
@@ -348,21 +345,19 @@ hipError_t launch_tiled(const TiledConfig& c, bool gateup, const GemmArgs& a, hi
   int total = gm * gn * 64;
   total = (total + 7) / 8 * 8;
   if (total <= 0) return hipSuccess;
-#define MOELORA_TILED(BM_, BN_, WM_, WN_, DEPTH_, OCC_)                                       \
-  if (c.bm == BM_ && c.bn == BN_ && c.wm == WM_ && c.wn == WN_ && c.depth == DEPTH_)          \
-    return gateup                                                                             \
-        ? launch_tiled_t<true, BM_, BN_, WM_, WN_, DEPTH_, OCC_>(a, n_tiles_n, total, stream) \
-        : launch_tiled_t<false, BM_, BN_, WM_, WN_, DEPTH_, OCC_>(a, n_tiles_n, total, stream);
-  MOELORA_TILED(128, 128, 64, 64, 2, 2)
-  MOELORA_TILED(128, 128, 64, 64, 1, 2)
-  MOELORA_TILED(64, 128, 32, 64, 2, 2)
-  MOELORA_TILED(256, 128, 128, 64, 2, 1)
-  MOELORA_TILED(256, 128, 128, 64, 1, 1)
-  MOELORA_TILED(128, 256, 64, 128, 2, 1)
-  MOELORA_TILED(128, 256, 64, 128, 1, 1)
-  MOELORA_TILED(256, 256, 128, 128, 1, 1)
-  MOELORA_TILED(256, 256, 128, 128, 2, 1)
-  MOELORA_TILED(128, 512, 64, 256, 1, 1)
+#define MOELORA_TILED(BM_, BN_, WM_, WN_, BK_, NST_)                                       \
+  if (c.bm == BM_ && c.bn == BN_ && c.wm == WM_ && c.wn == WN_ && c.bk == BK_ && c.nst == NST_) \
+    return gateup                                                                           \
+        ? launch_tiled_t<true, BM_, BN_, WM_, WN_, BK_, NST_>(a, n_tiles_n, total, stream)  \
+        : launch_tiled_t<false, BM_, BN_, WM_, WN_, BK_, NST_>(a, n_tiles_n, total, stream);
+  MOELORA_TILED(64, 128, 32, 64, 64, 2)
+  MOELORA_TILED(128, 128, 64, 64, 64, 2)
+  MOELORA_TILED(256, 256, 128, 128, 64, 2)
+  MOELORA_TILED(64, 128, 32, 64, 64, 3)
+  MOELORA_TILED(128, 128, 64, 64, 32, 4)
+  MOELORA_TILED(256, 256, 128, 128, 32, 4)
+  MOELORA_TILED(256, 256, 128, 128, 32, 5)
+  MOELORA_TILED(256, 128, 128, 64, 64, 3)
 #undef MOELORA_TILED
   return hipErrorInvalidValue;
 }

@@ -68,10 +68,10 @@ struct GemmArgs {
   int n_blocks_max;   // row blocks the grid is sized for (>= *n_blocks)
 };
 
-// Tile shape of the LDS-staged GEMM (four wavefronts of WM x WN each).
+// Tile shape of the LDS-staged GEMM: four wavefronts of WM x WN each; NST LDS stages of BK k.
 struct TiledConfig {
   int bm, bn, wm, wn;
-  int depth;  // K steps of global prefetch held in registers (1 or 2)
+  int bk, nst;
 };
 
 // Tile shape of the skinny (few rows per expert) GEMM.

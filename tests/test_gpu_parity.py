@@ -103,14 +103,17 @@ SMALL = {
     "mid": Workload("mid", 200, 256, 384, 8, 2, 6, 16),
     "fg_small": Workload("fg_small", 64, 256, 256, 32, 8, 16, 32, hot_experts=4, hot_bias=2.0),
     "one_token": Workload("one_token", 1, 256, 384, 8, 2, 4, 16),
-    # mean rows per expert above 24 selects the LDS-tiled MFMA path (64- and 128-row blocks)
+    # mean rows per expert above 24 selects the LDS-tiled MFMA path: 64-row blocks below 192
+    # rows per expert, 128-row blocks below 768
     "tiled64": Workload("tiled64", 256, 384, 640, 4, 2, 5, 16),
     "tiled64_r8": Workload("tiled64_r8", 300, 256, 256, 4, 1, 3, 8),
     "tiled128_r64": Workload("tiled128_r64", 900, 256, 384, 3, 2, 6, 64),
     "tiled128_runs": Workload("tiled128_runs", 1024, 256, 256, 4, 2, 9, 32, adapters="zipf_runs", run=40),
-    # mean rows per expert of 768 and more selects 256-row blocks (256x256 gate_up, 256x128 down)
+    "tiled128_h384": Workload("tiled128_h384", 1600, 384, 640, 2, 1, 4, 16),  # 256 tiles do not divide h
+    # 768 rows per expert and more, with 2I and h multiples of 256, selects 256x256 tiles
     "tiled256_r64": Workload("tiled256_r64", 2048, 256, 384, 4, 2, 6, 64, adapters="zipf_runs", run=100),
-    "tiled256_k1": Workload("tiled256_k1", 1600, 384, 640, 2, 1, 4, 16),
+    "tiled256_k1": Workload("tiled256_k1", 1600, 512, 640, 2, 1, 4, 16),
+    "tiled256_shortk": Workload("tiled256_shortk", 1700, 256, 128, 3, 2, 4, 16),  # down: 2 K steps
 }
 
 
