@@ -9,17 +9,21 @@
 //
 // Work decomposition: one workgroup per (16-row tile of the sorted layout, K split). Rows of a
 // tile belong to one expert and are sorted by adapter, so the adapters of a tile form
-// contiguous runs; each run is one 16 x r x K MFMA product against A[adapter][expert]
-// (rows of the tile outside the run are computed and dropped). The four wavefronts of the
-// workgroup take different runs, each over the split's whole K range. The partial sums of
-// split s go to zpart[s]; consumers add the S parts in order, so the result does not depend
-// on scheduling.
+// contiguous runs; each run is one 16 x r x K MFMA product against A[adapter][expert] in which
+// only the run's rows load x (the other rows read zeros through out-of-range buffer offsets,
+// at no memory traffic, and their outputs are dropped). The shrink streams A (r x K per run),
+// so all four wavefronts share every run: each takes a quarter of the split's K range, with
+// the loads of its next 128-wide K step in flight while the current one is multiplied, and
+// the four partial products are added in LDS in wavefront order. The partial sums of split s
+// go to zpart[s]; consumers add the S parts in order, so the result does not depend on
+// scheduling.
 #include "common.h"
 #include "kernels.h"
 
 namespace moelora {
 
-template <bool GATHER>
+// NCT: 16-column tiles of z (rank 8 and 16: 1, 32: 2, 64: 4).
+template <bool GATHER, int NCT>
 __global__ __launch_bounds__(256) void lora_shrink_kernel(ShrinkArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row0 = blockIdx.x * 16;
@@ -58,71 +62,113 @@ __global__ __launch_bounds__(256) void lora_shrink_kernel(ShrinkArgs a) {
   const int nks = K / 128;
   const int per = (nks + a.S - 1) / a.S;
   const int ks0 = min(nks, s * per), ks1 = min(nks, ks0 + per);
+  // this wavefront's quarter of the split (contiguous 128-wide steps)
+  const int wper = (ks1 - ks0 + 3) / 4;
+  const int w0 = min(ks1, ks0 + wave * wper), w1 = min(ks1, w0 + wper);
   const int m = lane & 15, kq = lane >> 4;
-  const int n_ct = r < 16 ? 1 : r / 16;
 
-  // Token rows through buffer loads: a padding row gets an out-of-range offset and reads zeros
-  // without touching memory (its outputs are never stored). Unconditional loads keep the
-  // compiler's outstanding-load count exact.
+  __shared__ f32x4 s_part[4][NCT][64];  // [wave][column tile][lane]
+
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.X, a.x_bytes);
-  uint32_t xo;
-  {
-    const int p = s_pair[m];
-    xo = p < 0 ? kOutOfRange
-               : (uint32_t)((GATHER ? (size_t)(p / a.k) : (size_t)(row0 + m)) * K * 2);
-  }
+  const int p_m = s_pair[m];
+  const uint32_t x_row_off =
+      p_m < 0 ? kOutOfRange
+              : (uint32_t)((GATHER ? (size_t)(p_m / a.k) : (size_t)(row0 + m)) * K * 2);
 
-  // Each wavefront owns whole runs (run index = wave, wave + 4, ...) over this split's K range;
-  // no cross-wave reduction is needed.
-  for (int run = wave; run < s_nrun; run += 4) {
+  for (int run = 0; run < s_nrun; ++run) {
     const int lo = s_lo[run], hi = s_hi[run], ad = s_rad[run];
-    const uint16_t* Abase = a.Aw + ((size_t)ad * a.E + e) * (size_t)r * K;
-    f32x4 acc[4];
+    // rows outside the run read zeros without touching memory
+    const uint32_t xo = (m >= lo && m < hi) ? x_row_off : kOutOfRange;
+    const __amdgpu_buffer_rsrc_t ar =
+        make_rsrc(a.Aw + ((size_t)ad * a.E + e) * (size_t)r * K, (uint32_t)((size_t)r * K * 2));
+    // A rows q >= r (rank 8) read zeros as well; they are never stored
+    uint32_t ao[NCT];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int ks = ks0; ks < ks1; ++ks) {
-      const int kb = ks * 128 + kq * 32;
-      u32x4 xa[4], bw[4][4];
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) xa[jj] = bufld16(xr, xo + 2u * (uint32_t)(kb + 8 * jj));
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        // columns q >= r (rank 8) re-read row r-1; they are never stored
-        const int q = min(c * 16 + m, r - 1);
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          bw[c][jj] = c < n_ct ? ldg16(Abase + (size_t)q * K + kb + 8 * jj) : u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if (c < n_ct) {
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) acc[c] = mfma16(xa[jj], bw[c][jj], acc[c]);
-        }
-      }
-    }
-    // acc[c] holds rows 4*(lane/16)+v of column q = 16c + lane%16
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < NCT; ++c) {
       const int q = c * 16 + m;
-      if (c < n_ct && q < r) {
+      ao[c] = q < r ? (uint32_t)((size_t)q * K * 2) : kOutOfRange;
+    }
+    f32x4 acc[NCT];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int row = 4 * kq + v;
-          if (row >= lo && row < hi) a.zpart[((size_t)s * a.cap + row0 + row) * r + q] = acc[c][v];
+    for (int c = 0; c < NCT; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    u32x4 xa0[4], bw0[NCT][4], xa1[4], bw1[NCT][4];
+    auto load = [&](int ks, u32x4* xa, u32x4 (*bw)[4]) {
+      const uint32_t kb = (uint32_t)(ks * 128 + kq * 32) * 2;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) xa[jj] = bufld16(xr, xo + kb + 16u * jj);
+#pragma unroll
+      for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) bw[c][jj] = bufld16(ar, ao[c] + kb + 16u * jj);
+    };
+    auto mma = [&](const u32x4* xa, const u32x4 (*bw)[4]) {
+#pragma unroll
+      for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) acc[c] = mfma16(xa[jj], bw[c][jj], acc[c]);
+    };
+    // Steps in pairs with ping-pong register sets (the loads of the next step are in flight
+    // while the current one is multiplied), then an odd last step. Every load is
+    // unconditional (past the end it re-reads the last step), and no branch encloses an MFMA.
+    const int n = w1 - w0;
+    if (n > 0) {
+      load(w0, xa0, bw0);
+      int i = 0;
+      for (; i + 2 <= n; i += 2) {
+        load(w0 + i + 1, xa1, bw1);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(xa0, bw0);
+        __builtin_amdgcn_sched_barrier(0);
+        load(min(w0 + i + 2, w1 - 1), xa0, bw0);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(xa1, bw1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (i < n) mma(xa0, bw0);
+    }
+    // partial of this wavefront -> LDS; the sum over the four wavefronts in order
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) s_part[wave][c][lane] = acc[c];
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int c = 0; c < NCT; ++c) {
+        const int q = c * 16 + m;
+        if (q < r) {
+          const f32x4 t = s_part[0][c][lane] + s_part[1][c][lane] + s_part[2][c][lane] +
+                          s_part[3][c][lane];
+          // acc[c] holds rows 4*(lane/16)+v of column q
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int row = 4 * kq + v;
+            if (row >= lo && row < hi) a.zpart[((size_t)s * a.cap + row0 + row) * r + q] = t[v];
+          }
         }
       }
     }
+    __syncthreads();  // s_part is reused by the next run
   }
 }
 
 hipError_t launch_shrink(bool gather, const ShrinkArgs& a, int tiles, hipStream_t stream) {
   if (tiles <= 0) return hipSuccess;
   dim3 grid(tiles, a.S);
-  if (gather)
-    hipLaunchKernelGGL(lora_shrink_kernel<true>, grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(lora_shrink_kernel<false>, grid, dim3(256), 0, stream, a);
+#define MOELORA_SHRINK(NCT_)                                                           \
+  if (gather)                                                                          \
+    hipLaunchKernelGGL((lora_shrink_kernel<true, NCT_>), grid, dim3(256), 0, stream, a); \
+  else                                                                                 \
+    hipLaunchKernelGGL((lora_shrink_kernel<false, NCT_>), grid, dim3(256), 0, stream, a);
+  if (a.r <= 16) {
+    MOELORA_SHRINK(1)
+  } else if (a.r == 32) {
+    MOELORA_SHRINK(2)
+  } else if (a.r == 64) {
+    MOELORA_SHRINK(4)
+  } else {
+    return hipErrorInvalidValue;
+  }
+#undef MOELORA_SHRINK
   return hipGetLastError();
 }
 
