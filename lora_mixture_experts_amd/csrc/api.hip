@@ -194,6 +194,8 @@ SkinnyPlan pick_skinny(int nt, int h, int I) {
   return pl;
 }
 
+// K splits of the LoRA shrink: enough (tile, split) workgroups to fill the chip, at most
+// kMaxSplit and at least one 128-wide step each.
 int pick_splits(int64_t tiles, int K) {
   int s = (int)((1024 + tiles - 1) / (tiles > 0 ? tiles : 1));
   s = s < 1 ? 1 : (s > kMaxSplit ? kMaxSplit : s);
@@ -206,7 +208,6 @@ int pick_splits(int64_t tiles, int K) {
 bool moelora_make_layout(int T, int h, int I, int E, int nA, int r, int topk, MoeLoraLayout* L) {
   const int64_t P = (int64_t)T * topk;
   L->max_bm = kMaxBM;
-  L->splits = kMaxSplit;
   L->cap = round_up64(P + (int64_t)E * (kMaxBM - 1), 256);
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -335,14 +336,14 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   al.g_cnt = (int*)(ws + L.align_cnt);
   al.g_start = (int*)(ws + L.align_start);
   al.g_lists = (int*)(ws + L.align_lists);
-  const size_t lds = align_lds_plan(T, topk, E, nA, &al);
-  if (launch_align(al, lds, stream) != hipSuccess) return MOELORA_EHIP;
-  if (!mark(ev, 2, stream)) return MOELORA_EHIP;
-
   const int64_t max_rows = P + (int64_t)E * (bm - 1);
   const int max_blocks = (int)((max_rows + bm - 1) / bm);
   const int tiles16 = max_blocks * (bm / 16);
   const int s1 = pick_splits(tiles16, h), s2 = pick_splits(tiles16, I);
+  const size_t lds = align_lds_plan(T, topk, E, nA, &al);
+  if (launch_align(al, lds, stream) != hipSuccess) return MOELORA_EHIP;
+  if (!mark(ev, 2, stream)) return MOELORA_EHIP;
+
 
   ShrinkArgs sh;
   sh.sorted_pairs = sorted;
@@ -354,7 +355,6 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   sh.nA = nA;
   sh.E = E;
   sh.r = r;
-  sh.cap = L.cap;
 
   GemmArgs g;
   g.cap = L.cap;
@@ -377,6 +377,7 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   sh.K = h;
   sh.S = s1;
   sh.zpart = z1;
+  sh.cap = L.cap;
   if (launch_shrink(true, sh, tiles16, stream) != hipSuccess) return MOELORA_EHIP;
   if (!mark(ev, 3, stream)) return MOELORA_EHIP;
   g.X = (const uint16_t*)x;

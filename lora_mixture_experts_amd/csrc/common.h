@@ -87,7 +87,6 @@ struct MoeLoraLayout {
   size_t total;
   int64_t cap;     // rows of the sorted layout at the largest row-block size
   int max_bm;      // largest row-block size any path uses
-  int splits;      // split-K parts of the LoRA shrink
 };
 
 bool moelora_make_layout(int T, int h, int I, int E, int nA, int r, int topk, MoeLoraLayout* L);

@@ -39,25 +39,46 @@ __device__ __forceinline__ float dot8_bf16(const float* z, u32x4 v) {
   return s;
 }
 
-// out[v] += sum_q z[q] * Brow_v[q] for the 4 rows at Bbase + v*r (r multiple of 8); z is the
-// sum of the S split-K partials of the LoRA shrink, added in split order.
-__device__ __forceinline__ void lora_expand4(const float* __restrict__ zrow, int64_t zstride, int S,
-                                             const uint16_t* __restrict__ Bbase, int r, float* out) {
-  for (int q0 = 0; q0 < r; q0 += 8) {
-    float z[8];
+// out[b][v] += sum_q z[q] * B_b[v][q] for NB groups of 4 weight rows (gate_up: the gate and
+// the up rows) at Bb[b] + v*r; z is the row's shrink output (r floats). The loads of 16 rank
+// values of z and of every group are issued together before the products.
+template <int NB>
+__device__ __forceinline__ void lora_expand(const float* __restrict__ zrow,
+                                            const uint16_t* const (&Bb)[NB], int r,
+                                            float (&out)[NB][4]) {
+  for (int q0 = 0; q0 < r; q0 += 16) {
+    float z[16];
+    u32x4 bv[NB][4][2];
 #pragma unroll
-    for (int qq = 0; qq < 8; ++qq) z[qq] = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const f32x4 lo = *reinterpret_cast<const f32x4*>(zrow + s * zstride + q0);
-      const f32x4 hi = *reinterpret_cast<const f32x4*>(zrow + s * zstride + q0 + 4);
+    for (int c = 0; c < 2; ++c) {
+      const int q = q0 + 8 * c;
+      if (q < r) {
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(zrow + q);
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(zrow + q + 4);
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        z[qq] += lo[qq];
-        z[4 + qq] += hi[qq];
+        for (int t = 0; t < 4; ++t) {
+          z[8 * c + t] = lo[t];
+          z[8 * c + 4 + t] = hi[t];
+        }
+#pragma unroll
+        for (int g = 0; g < NB; ++g)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) bv[g][v][c] = ldg16(Bb[g] + (size_t)v * r + q);
+      } else {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) z[8 * c + t] = 0.f;
+#pragma unroll
+        for (int g = 0; g < NB; ++g)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) bv[g][v][c] = u32x4{0u, 0u, 0u, 0u};
       }
     }
 #pragma unroll
-    for (int v = 0; v < 4; ++v) out[v] += dot8_bf16(z, ldg16(Bbase + (size_t)v * r + q0));
+    for (int g = 0; g < NB; ++g)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) out[g][v] += dot8_bf16(z + 8 * c, bv[g][v][c]);
   }
 }
 
@@ -79,10 +100,27 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs a) {
   const int n0 = SPLIT ? (blockIdx.x * 2 + (wave & 1)) * 16 : (blockIdx.x * 4 + wave) * 16 * RT;
   const bool up_wave = SPLIT && wave >= 2;
   __shared__ f32x4 s_up[SPLIT ? 2 * 64 * NT : 1];
-  if (n0 >= a.N) return;  // never taken with SPLIT (N % 32 == 0 and an exact grid)
   const int blk = blockIdx.y;
   if (blk >= *a.n_blocks) return;
   const int zsplit = blockIdx.z;
+  constexpr int BMZ = 16 * NT;
+
+  // The LoRA shrink leaves z as S split-K parts; the block's z rows are added up once, in split
+  // order, into LDS for the epilogue (rows without an adapter hold values nobody reads). Only
+  // K split 0 of down adds the LoRA term.
+  __shared__ __attribute__((aligned(16))) float s_z[BMZ * 64];
+  if (zsplit == 0) {
+    const int nz = BMZ * a.r;
+    const float* zp = a.zpart + (size_t)blk * BMZ * a.r;
+    const size_t zstride = (size_t)a.cap * a.r;
+    for (int i = threadIdx.x; i < nz; i += 256) {
+      float z = 0.f;
+      for (int sp = 0; sp < a.S; ++sp) z += zp[sp * zstride + i];
+      s_z[i] = z;
+    }
+    __syncthreads();
+  }
+  if (n0 >= a.N) return;  // never taken (N is a multiple of every column tile width)
   const int e = a.block_expert[blk];
   const int m = lane & 15, kq = lane >> 4;
   const int K = a.K;
@@ -168,7 +206,6 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs a) {
 #undef MOELORA_COMPUTE
 
   // Epilogue: lane holds weight rows n0 + 16*rt + 4*kq + v (v < 4) for token row (lane % 16).
-  const int64_t zstride = a.cap * a.r;
   if (SPLIT) {
     if (up_wave) {
 #pragma unroll
@@ -183,37 +220,37 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs a) {
     const int p = a.sorted_pairs[row];
     if (p < 0) continue;
     const int ad = sanitize_adapter(a.adapter_ids[p / a.k], a.nA);
-    const float* zrow = a.zpart + (size_t)row * a.r;
+    const float* zrow = s_z + (nt * 16 + m) * a.r;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const int nb = n0 + 16 * rt + 4 * kq;
       if (GATEUP) {
-        float g[4], u[4];
+        float gu[2][4];  // gate, up
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          g[v] = acc[rt][nt][v];
-          u[v] = SPLIT ? s_up[((wave & 1) * NT + nt) * 64 + lane][v] : acc[NW - RT + rt][nt][v];
+          gu[0][v] = acc[rt][nt][v];
+          gu[1][v] = SPLIT ? s_up[((wave & 1) * NT + nt) * 64 + lane][v] : acc[NW - RT + rt][nt][v];
         }
         if (ad >= 0) {
           const uint16_t* bg = a.Bw + (((size_t)ad * a.E + e) * 2 * N + nb) * a.r;
-          lora_expand4(zrow, zstride, a.S, bg, a.r, g);
-          lora_expand4(zrow, zstride, a.S, bg + N * a.r, a.r, u);
+          const uint16_t* const bb[2] = {bg, bg + N * a.r};
+          lora_expand<2>(zrow, bb, a.r, gu);
         }
         float hv[4];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) hv[v] = g[v] / (1.f + __expf(-g[v])) * u[v];
+        for (int v = 0; v < 4; ++v) hv[v] = gu[0][v] / (1.f + __expf(-gu[0][v])) * gu[1][v];
         u32x2 packed = {pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
         *reinterpret_cast<u32x2*>(a.act_out + (size_t)row * N + nb) = packed;
       } else {
-        float d[4];
+        float d[1][4];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) d[v] = acc[rt][nt][v];
+        for (int v = 0; v < 4; ++v) d[0][v] = acc[rt][nt][v];
         if (ad >= 0 && zsplit == 0) {
-          const uint16_t* bd = a.Bw + (((size_t)ad * a.E + e) * N + nb) * a.r;
-          lora_expand4(zrow, zstride, a.S, bd, a.r, d);
+          const uint16_t* const bd[1] = {a.Bw + (((size_t)ad * a.E + e) * N + nb) * a.r};
+          lora_expand<1>(zrow, bd, a.r, d);
         }
         *reinterpret_cast<f32x4*>(a.d_out + zsplit * a.d_split_stride + (size_t)p * N + nb) =
-            f32x4{d[0], d[1], d[2], d[3]};
+            f32x4{d[0][0], d[0][1], d[0][2], d[0][3]};
       }
     }
   }

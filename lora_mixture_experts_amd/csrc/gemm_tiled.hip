@@ -71,8 +71,8 @@ __device__ __forceinline__ void tiled_store(const GemmArgs& a, f32x16 (&acc)[FM]
 // each run the tile's columns of B[adapter][expert] (BN rows x r, r-contiguous) are loaded
 // straight into LDS, up to as many runs at once as fit, with one wait per batch, and every
 // 32-row group the run overlaps adds (z restricted to the run's rows) x B over K = r. Each
-// wavefront first loads the z rows of its groups (summing the split-K parts) and keeps them as
-// bf16 high and low parts in registers.
+// wavefront first loads the z rows of its groups and keeps them as bf16 high and low parts in
+// registers.
 template <bool GATEUP, int BM, int BN, int WM, int WN, int FM, int FN, uint32_t LDS_BYTES>
 __device__ __forceinline__ void lora_expand_lds(const GemmArgs& a, f32x16 (&acc)[FM][FN],
                                                 uint16_t* lds, int row0, int wm, int wn,
@@ -127,9 +127,9 @@ __device__ __forceinline__ void lora_expand_lds(const GemmArgs& a, f32x16 (&acc)
     if (lane == 0) *s_n = nrun;
   }
 
-  // z of this wavefront's rows: fp32 sum of the split-K parts, kept as bf16 high and low parts.
-  // Loaded half the groups at a time (the fp32 sums of all groups at once would not fit beside
-  // the accumulators).
+  // z of this wavefront's rows (the sum of the shrink's split parts), kept as bf16 high and low
+  // parts. Loaded half the groups at a time (the fp32 values of all groups at once would not
+  // fit beside the accumulators).
   u32x4 zh[FM][MAXSL], zl[FM][MAXSL];
   constexpr int GH = FM > 1 ? FM / 2 : 1;
 #pragma unroll
@@ -142,7 +142,7 @@ __device__ __forceinline__ void lora_expand_lds(const GemmArgs& a, f32x16 (&acc)
 #pragma unroll
         for (int t = 0; t < 8; ++t) zf[i][sl][t] = 0.f;
     const int64_t zstride = a.cap * r;
-    for (int sp = 0; sp < a.S; ++sp) {
+    for (int sp = 0; sp < a.S; ++sp) {  // split-K parts of the shrink, in order
 #pragma unroll
       for (int i = 0; i < GH; ++i) {
         const float* zr =

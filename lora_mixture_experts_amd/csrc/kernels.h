@@ -29,7 +29,7 @@ inline size_t align_list_ints(int T, int k, int E) {
   return 3 * (size_t)T * k + (size_t)T + 16 * (size_t)E;
 }
 
-// LoRA shrink z = X A^T for the rows of the sorted layout (split-K partial sums).
+// LoRA shrink z = X A^T for the rows of the sorted layout.
 struct ShrinkArgs {
   const uint16_t* X;  // gather: x [T][K]; otherwise act [cap][K]
   uint32_t x_bytes;   // size of X (< 2 GiB)
@@ -38,9 +38,10 @@ struct ShrinkArgs {
   const int* n_blocks;
   int bm;
   const int* adapter_ids;
-  int k, nA, E, r, K, S;
+  int k, nA, E, r, K;
   const uint16_t* Aw;  // [nA][E][r][K]
-  float* zpart;        // [S][cap][r]
+  int S;               // K splits over workgroups
+  float* zpart;        // [S][cap][r]; written for the rows that carry an adapter
   int64_t cap;
 };
 
@@ -51,7 +52,7 @@ struct GemmArgs {
   uint32_t x_bytes;    // size of X (< 2 GiB)
   const uint16_t* W;   // gate_up: W1 [E][2I][h]; down: W2 [E][h][I]
   const uint16_t* Bw;  // gate_up: B1 [nA][E][2I][r]; down: B2 [nA][E][h][r]
-  const float* zpart;  // [S][cap][r]
+  const float* zpart;  // [S][cap][r] LoRA shrink output, as S split-K parts
   int S;
   int64_t cap;
   const int* sorted_pairs;

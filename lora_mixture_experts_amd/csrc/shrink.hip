@@ -76,7 +76,10 @@ __global__ __launch_bounds__(256) void lora_shrink_kernel(ShrinkArgs a) {
               : (uint32_t)((GATHER ? (size_t)(p_m / a.k) : (size_t)(row0 + m)) * K * 2);
 
   for (int run = 0; run < s_nrun; ++run) {
-    const int lo = s_lo[run], hi = s_hi[run], ad = s_rad[run];
+    const int lo = s_lo[run], hi = s_hi[run];
+    // uniform: the A descriptor must live in scalar registers (from a value the compiler cannot
+    // prove uniform it would build a per-lane loop around every load)
+    const int ad = __builtin_amdgcn_readfirstlane(s_rad[run]);
     // rows outside the run read zeros without touching memory
     const uint32_t xo = (m >= lo && m < hi) ? x_row_off : kOutOfRange;
     const __amdgpu_buffer_rsrc_t ar =
