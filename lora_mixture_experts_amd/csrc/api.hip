@@ -1,5 +1,6 @@
 // C ABI of libmoelora: argument validation, workspace carve-up and the launch sequence of the
 // fused MoE + multi-LoRA layer (declared in include/moelora.h).
+#include <algorithm>
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
@@ -77,7 +78,7 @@ size_t align_lds_plan(int T, int k, int E, int nA, AlignArgs* a) {
 
 // GEMM path from the mean rows per expert (known on the host; per-expert counts are not):
 // the skinny path streams weights once per 16/32-row block, the tiled path stages tiles in LDS
-// for MFMA-bound row counts. MOELORA_PATH=skinny|skinny1|skinny2 forces the skinny path (and
+// for MFMA-bound row counts. MOELORA_PATH=skinny|skinny1|skinny2|skinny4 forces the skinny path (and
 // its row-block size) for experiments.
 struct PathPlan {
   bool tiled;
@@ -109,6 +110,7 @@ PathPlan pick_path(int64_t P, int E, int h, int I) {
     if (env && !strcmp(env, "skinny")) forced = 1;
     if (env && !strcmp(env, "skinny1")) forced = 3;
     if (env && !strcmp(env, "skinny2")) forced = 4;
+    if (env && !strcmp(env, "skinny4")) forced = 5;
     const char* tenv = getenv("MOELORA_TILED");
     if (tenv) {
       auto parse = [](const char* str, TiledConfig* c) {
@@ -127,9 +129,9 @@ PathPlan pick_path(int64_t P, int E, int h, int I) {
     }
   }
   if (forced == 1) pl.tiled = false;
-  if (forced == 3 || forced == 4) {
+  if (forced >= 3 && forced <= 5) {
     pl.tiled = false;
-    pl.nt = forced == 3 ? 1 : 2;
+    pl.nt = forced == 3 ? 1 : (forced == 4 ? 2 : 4);
   }
   if (forced == 2) {
     pl.tiled = true;
@@ -339,7 +341,10 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   const int64_t max_rows = P + (int64_t)E * (bm - 1);
   const int max_blocks = (int)((max_rows + bm - 1) / bm);
   const int tiles16 = max_blocks * (bm / 16);
-  const int s1 = pick_splits(tiles16, h), s2 = pick_splits(tiles16, I);
+  // Split the shrink's K by the tiles that can hold pairs (at most P/16 plus one partial tile per
+  // expert), not by the padded grid: padding tiles exit at once.
+  const int64_t live_tiles = std::min<int64_t>(tiles16, (P + 15) / 16 + E);
+  const int s1 = pick_splits(live_tiles, h), s2 = pick_splits(live_tiles, I);
   const size_t lds = align_lds_plan(T, topk, E, nA, &al);
   if (launch_align(al, lds, stream) != hipSuccess) return MOELORA_EHIP;
   if (!mark(ev, 2, stream)) return MOELORA_EHIP;

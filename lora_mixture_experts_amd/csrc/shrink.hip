@@ -11,12 +11,12 @@
 // tile belong to one expert and are sorted by adapter, so the adapters of a tile form
 // contiguous runs; each run is one 16 x r x K MFMA product against A[adapter][expert] in which
 // only the run's rows load x (the other rows read zeros through out-of-range buffer offsets,
-// at no memory traffic, and their outputs are dropped). The shrink streams A (r x K per run),
-// so all four wavefronts share every run: each takes a quarter of the split's K range, with
-// the loads of its next 128-wide K step in flight while the current one is multiplied, and
-// the four partial products are added in LDS in wavefront order. The partial sums of split s
-// go to zpart[s]; consumers add the S parts in order, so the result does not depend on
-// scheduling.
+// at no memory traffic, and their outputs are dropped). The shrink streams A (r x K per run).
+// With one or two runs the four wavefronts share each run, splitting the split's K range;
+// with more they take whole runs in parallel. A wavefront keeps the loads of its next 128-wide
+// K step in flight while the current one is multiplied; the partial products of wavefronts
+// sharing a run are added in LDS in wavefront order. The partial sums of split s go to
+// zpart[s]; consumers add the S parts in order, so the result does not depend on scheduling.
 #include "common.h"
 #include "kernels.h"
 
@@ -58,13 +58,21 @@ __global__ __launch_bounds__(256) void lora_shrink_kernel(ShrinkArgs a) {
   }
   __syncthreads();
 
+  const int nrun = s_nrun;
+  if (nrun == 0) return;
+  // ng groups of gs wavefronts (ng: the smallest power of two >= min(nrun, 4)); a group takes
+  // every ng-th run and its members split the run's K range of this split
+  const int ng = nrun >= 3 ? 4 : nrun;
+  const int gs = 4 / ng;
+  const int grp = wave / gs, mem = wave % gs;
+
   const int K = a.K, r = a.r;
   const int nks = K / 128;
   const int per = (nks + a.S - 1) / a.S;
   const int ks0 = min(nks, s * per), ks1 = min(nks, ks0 + per);
-  // this wavefront's quarter of the split (contiguous 128-wide steps)
-  const int wper = (ks1 - ks0 + 3) / 4;
-  const int w0 = min(ks1, ks0 + wave * wper), w1 = min(ks1, w0 + wper);
+  // this wavefront's share of the split (contiguous 128-wide steps)
+  const int wper = (ks1 - ks0 + gs - 1) / gs;
+  const int w0 = min(ks1, ks0 + mem * wper), w1 = min(ks1, w0 + wper);
   const int m = lane & 15, kq = lane >> 4;
 
   __shared__ f32x4 s_part[4][NCT][64];  // [wave][column tile][lane]
@@ -75,12 +83,16 @@ __global__ __launch_bounds__(256) void lora_shrink_kernel(ShrinkArgs a) {
       p_m < 0 ? kOutOfRange
               : (uint32_t)((GATHER ? (size_t)(p_m / a.k) : (size_t)(row0 + m)) * K * 2);
 
-  for (int run = 0; run < s_nrun; ++run) {
-    const int lo = s_lo[run], hi = s_hi[run];
+  // every group runs the same number of rounds, so the barriers below are uniform
+  const int rounds = (nrun + ng - 1) / ng;
+  for (int round = 0; round < rounds; ++round) {
+    const int run = round * ng + grp;
+    const bool active = run < nrun;
+    const int lo = active ? s_lo[run] : 0, hi = active ? s_hi[run] : 0;
     // uniform: the A descriptor must live in scalar registers (from a value the compiler cannot
     // prove uniform it would build a per-lane loop around every load)
-    const int ad = __builtin_amdgcn_readfirstlane(s_rad[run]);
-    // rows outside the run read zeros without touching memory
+    const int ad = __builtin_amdgcn_readfirstlane(active ? s_rad[run] : 0);
+    // rows outside the run (all rows, for an idle group) read zeros without touching memory
     const uint32_t xo = (m >= lo && m < hi) ? x_row_off : kOutOfRange;
     const __amdgpu_buffer_rsrc_t ar =
         make_rsrc(a.Aw + ((size_t)ad * a.E + e) * (size_t)r * K, (uint32_t)((size_t)r * K * 2));
@@ -89,7 +101,7 @@ __global__ __launch_bounds__(256) void lora_shrink_kernel(ShrinkArgs a) {
 #pragma unroll
     for (int c = 0; c < NCT; ++c) {
       const int q = c * 16 + m;
-      ao[c] = q < r ? (uint32_t)((size_t)q * K * 2) : kOutOfRange;
+      ao[c] = (active && q < r) ? (uint32_t)((size_t)q * K * 2) : kOutOfRange;
     }
     f32x4 acc[NCT];
 #pragma unroll
@@ -130,27 +142,37 @@ __global__ __launch_bounds__(256) void lora_shrink_kernel(ShrinkArgs a) {
       }
       if (i < n) mma(xa0, bw0);
     }
-    // partial of this wavefront -> LDS; the sum over the four wavefronts in order
+    // acc[c] holds rows 4*(lane/16)+v of column q = 16c + lane%16
+    auto store = [&](int c, f32x4 t) {
+      const int q = c * 16 + m;
+      if (q < r) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int row = 4 * kq + v;
+          if (row >= lo && row < hi) a.zpart[((size_t)s * a.cap + row0 + row) * r + q] = t[v];
+        }
+      }
+    };
+    if (gs == 1) {
+      if (active) {
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) store(c, acc[c]);
+      }
+      continue;
+    }
+    // partials of the group's wavefronts -> LDS; its first wavefront adds them in order
 #pragma unroll
     for (int c = 0; c < NCT; ++c) s_part[wave][c][lane] = acc[c];
     __syncthreads();
-    if (wave == 0) {
+    if (active && mem == 0) {
 #pragma unroll
       for (int c = 0; c < NCT; ++c) {
-        const int q = c * 16 + m;
-        if (q < r) {
-          const f32x4 t = s_part[0][c][lane] + s_part[1][c][lane] + s_part[2][c][lane] +
-                          s_part[3][c][lane];
-          // acc[c] holds rows 4*(lane/16)+v of column q
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int row = 4 * kq + v;
-            if (row >= lo && row < hi) a.zpart[((size_t)s * a.cap + row0 + row) * r + q] = t[v];
-          }
-        }
+        f32x4 t = s_part[wave][c][lane];
+        for (int j = 1; j < gs; ++j) t += s_part[wave + j][c][lane];
+        store(c, t);
       }
     }
-    __syncthreads();  // s_part is reused by the next run
+    __syncthreads();  // s_part is reused by the next round
   }
 }
 
