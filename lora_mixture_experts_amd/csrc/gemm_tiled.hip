@@ -184,9 +184,11 @@ __device__ __forceinline__ void lora_expand_lds(const GemmArgs& a, f32x16 (&acc)
   if (nrun == 0) return;
 
   // B tile of one run in LDS: BN rows (the tile's weight rows) x r, the 16-byte chunk index
-  // XOR-swizzled by the row (rows of r/8 chunks; 1 KB load blocks of 512/r rows).
+  // XOR-swizzled by the row (rows of r/8 chunks; 1 KB load blocks of 512/r rows). A fragment
+  // read takes 16 consecutive rows at one chunk per 256-byte pass of the 64 LDS banks, so rows
+  // 16/cpr apart must land in different slots.
   const int cpr = r / 8, rpb = 512 / r;
-  const int rsh = 8 / cpr;  // rows per swizzle step
+  const int rsh = 16 / cpr;  // rows per swizzle step
   auto swz = [&](int row, int c) { return c ^ ((row / rsh) & (cpr - 1)); };
   const uint32_t run_bytes = (uint32_t)BN * r * 2;
   const int rb = (int)((LDS_BYTES - TABLE_BYTES) / run_bytes);  // runs per batch (>= 3)
@@ -276,11 +278,12 @@ __global__ __launch_bounds__(256, 1) void tiled_gemm_kernel(GemmArgs a, int n_ti
   const size_t w_rows = GATEUP ? 2 * N : N;  // weight rows of one expert
 
   // byte offsets of the chunk each lane loads at K step 0 (padding rows: out of range, zeros)
-  const int chunk = Pipe::load_chunk(lane);
   uint32_t xo[NA], wo[NB];
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
-    const int srow = row0 + Pipe::load_row(i, wave, lane);
+    const int row = Pipe::load_row(i, wave, lane);
+    const int chunk = Pipe::load_chunk(row, lane);
+    const int srow = row0 + row;
     const int p = a.sorted_pairs[srow];
     xo[i] = p < 0 ? kOutOfRange
                   : (uint32_t)((GATEUP ? (size_t)(p / a.k) : (size_t)srow) * K * 2) + 16u * chunk;
@@ -288,6 +291,7 @@ __global__ __launch_bounds__(256, 1) void tiled_gemm_kernel(GemmArgs a, int n_ti
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     const int row = Pipe::load_row(i, wave, lane);
+    const int chunk = Pipe::load_chunk(row, lane);
     size_t wrow;
     if (GATEUP) {
       const int g = row / WN, rr = row % WN;

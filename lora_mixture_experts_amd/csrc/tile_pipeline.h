@@ -70,18 +70,20 @@ struct TilePipe {
   static_assert(FM + FN <= 15, "one sub-step of fragment reads must fit the LDS counter");
   static_assert((NST - 1) * PER < 64, "in-flight loads must fit vmcnt");
 
-  // Slot of chunk c in tile row r (XOR swizzle; 8 consecutive rows hit 8 distinct 16-byte bank
-  // groups for any fixed chunk).
+  // Slot of chunk c in tile row r (XOR swizzle). The LDS has 64 banks of 4 bytes and serves a
+  // 16-byte-per-lane read 16 lanes (256 bytes) at a time; the 16 lanes of a fragment read hold
+  // 16 consecutive rows at one chunk, so rows that share their 256-byte bank alignment
+  // (every 2nd row at 128 bytes per row, every 4th at 64) must land in different slots.
   __device__ static __forceinline__ int swz(int r, int c) {
-    return BK == 64 ? (c ^ (r & 7)) : (c ^ ((r >> 1) & 3));
+    return BK == 64 ? (c ^ ((r >> 1) & 7)) : (c ^ ((r >> 2) & 3));
   }
   // Tile row and K chunk that lane `lane` of wavefront `wave` loads in its i-th block of A
-  // (rows of B likewise): the lane fills slot lane % CPR of row lane / CPR of the block.
+  // (rows of B likewise): the lane fills slot lane % CPR of row lane / CPR of the block, so it
+  // fetches the chunk that the swizzle puts in that slot of that (tile) row.
   __device__ static __forceinline__ int load_row(int i, int wave, int lane) {
     return (i * 4 + wave) * RPB + lane / CPR;
   }
-  __device__ static __forceinline__ int load_chunk(int lane) {
-    const int row = lane / CPR;  // block-relative; blocks start at multiples of RPB
+  __device__ static __forceinline__ int load_chunk(int row, int lane) {
     return swz(row, lane % CPR);
   }
 
