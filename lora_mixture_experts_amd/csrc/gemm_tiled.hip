@@ -248,7 +248,7 @@ __device__ __forceinline__ void lora_expand_lds(const GemmArgs& a, f32x16 (&acc)
 
 template <bool GATEUP, int BM, int BN, int WM, int WN, int BK, int NST>
 __global__ __launch_bounds__(256, 1) void tiled_gemm_kernel(GemmArgs a, int n_tiles_n,
-                                                            int grid_total) {
+                                                            int /*grid_total*/) {
   using Pipe = TilePipe<BM, BN, WM, WN, BK, NST>;
   constexpr int FM = Pipe::FM, FN = Pipe::FN, NA = Pipe::NA, NB = Pipe::NB;
   static_assert(!GATEUP || FN % 2 == 0, "gate_up needs gate and up halves per wave");
@@ -259,18 +259,27 @@ __global__ __launch_bounds__(256, 1) void tiled_gemm_kernel(GemmArgs a, int n_ti
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / Pipe::WAVES_N, wn = wave % Pipe::WAVES_N;
 
-  // Tile order. Hardware workgroup ids go round-robin over the 8 XCDs, so each XCD is given a
-  // contiguous range of logical tiles; the workgroups an XCD runs at once then cover a group of
-  // GROUP_M row blocks x GROUP_N column tiles, and every token tile and weight tile fetched
-  // into that XCD's L2 serves several workgroups.
-  constexpr int GROUP_M = 8, GROUP_N = 8;
+  // Tile order. The live tiles (n_blocks row blocks x n_tiles_n column tiles; the grid is
+  // sized for the largest n_blocks) are numbered column group by column group, row group by row
+  // group, in groups of up to 8 row blocks x 8 column tiles. Hardware workgroup ids go
+  // round-robin over the 8 XCDs, so each XCD is given an equal contiguous range of that
+  // numbering: the workgroups it runs at once cover a few groups, every token tile and weight
+  // tile fetched into its L2 serves several of them, and no XCD gets more tiles than another.
+  const int nblk = *a.n_blocks;
+  const int live = nblk * n_tiles_n;
+  const int per_xcd = (live + 7) >> 3;
   const int hw = blockIdx.x;
-  const int logical = (hw & 7) * (grid_total >> 3) + (hw >> 3);
-  const int groups_m = (a.n_blocks_max + GROUP_M - 1) / GROUP_M;
-  const int grp = logical / (GROUP_M * GROUP_N), within = logical % (GROUP_M * GROUP_N);
-  const int blk = (grp % groups_m) * GROUP_M + within % GROUP_M;
-  const int ntile = (grp / groups_m) * GROUP_N + within / GROUP_M;
-  if (ntile >= n_tiles_n || blk >= a.n_blocks_max || blk >= *a.n_blocks) return;
+  const int slot = hw >> 3;
+  const int t = (hw & 7) * per_xcd + slot;
+  if (slot >= per_xcd || t >= live) return;
+  const int cg = t / (nblk * 8);                 // column group (all but the last are 8 wide)
+  const int cols = min(8, n_tiles_n - cg * 8);
+  const int u = t - cg * nblk * 8;
+  const int rg = u / (8 * cols);                 // row group (all but the last are 8 tall)
+  const int rows = min(8, nblk - rg * 8);
+  const int w = u - rg * 8 * cols;
+  const int blk = rg * 8 + w % rows;
+  const int ntile = cg * 8 + w / rows;
   const int e = a.block_expert[blk];
   const int K = a.K;
   const size_t N = (size_t)a.N;
