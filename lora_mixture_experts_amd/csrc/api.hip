@@ -14,7 +14,7 @@ using namespace moelora;
 namespace {
 
 constexpr int kMaxBM = 256;      // largest row block any GEMM path uses
-constexpr int kMaxDownSplit = 2;  // K splits of the skinny down GEMM
+constexpr int kMaxDownSplit = 2;  // K splits of the down GEMM
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 int64_t round_up64(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
@@ -394,7 +394,12 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   g.K = h;
   g.N = I;
   SkinnyPlan plan = pick_skinny(nt, h, I);
-  if (path.tiled) plan.ksplit = 1;
+  if (path.tiled) {
+    // tiled down: split K in two when the tiles would fill the chip fewer than four times (the
+    // last, partial round of 256x256 tiles then costs a large share of the time)
+    const int64_t est_tiles = (int64_t)((P + path.bm - 1) / path.bm + E) * (h / path.tc_dn.bn);
+    plan.ksplit = est_tiles < 4 * 256 ? kMaxDownSplit : 1;
+  }
   g.ksplit = 1;
   g.d_split_stride = P * (int64_t)h;
   const hipError_t gu_err = path.tiled ? launch_tiled(path.tc, true, g, stream)

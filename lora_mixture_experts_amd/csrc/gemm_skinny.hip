@@ -107,9 +107,11 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs a) {
 
   // The LoRA shrink leaves z as S split-K parts; the block's z rows are added up once, in split
   // order, into LDS for the epilogue (rows without an adapter hold values nobody reads). Only
-  // K split 0 of down adds the LoRA term.
+  // K split 0 of down adds the LoRA term. Run after the first weight loads are issued, so the
+  // two latencies overlap. (The grid covers N exactly: every wavefront has columns.)
   __shared__ __attribute__((aligned(16))) float s_z[BMZ * 64];
-  if (zsplit == 0) {
+  auto z_prologue = [&]() {
+    if (zsplit != 0) return;
     const int nz = BMZ * a.r;
     const float* zp = a.zpart + (size_t)blk * BMZ * a.r;
     const size_t zstride = (size_t)a.cap * a.r;
@@ -119,8 +121,7 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs a) {
       s_z[i] = z;
     }
     __syncthreads();
-  }
-  if (n0 >= a.N) return;  // never taken (N is a multiple of every column tile width)
+  };
   const int e = a.block_expert[blk];
   const int m = lane & 15, kq = lane >> 4;
   const int K = a.K;
@@ -180,6 +181,7 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs a) {
           acc[w][nt] = mfma16(W_[w][j], X_[nt][j], acc[w][nt]);                \
   } while (0)
   const int nsteps = ks1 - ks0;
+  if (!PIPE || nsteps == 0) z_prologue();
   if (!PIPE) {
     for (int i = 0; i < nsteps; ++i) {
       const int kb = (ks0 + i) * KS + kq * (8 * P);
@@ -189,6 +191,7 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs a) {
   } else if (nsteps > 0) {
     const int kb0 = ks0 * KS + kq * (8 * P);
     MOELORA_LOAD(wa, xa, kb0);
+    z_prologue();
     for (int i = 0; i < nsteps; i += 2) {
       // sched_barrier(0) keeps the compiler from interleaving the phases (which would bring
       // the waits for the in-flight set back in front of the MFMAs)
@@ -260,7 +263,8 @@ hipError_t launch_skinny(const SkinnyConfig& c, bool gateup, const GemmArgs& a, 
                          hipStream_t stream) {
   const bool split = gateup && c.split;
   const int cols_per_wg = split ? 32 : 4 * 16 * c.rt;
-  const int grid_x = (a.N + cols_per_wg - 1) / cols_per_wg;
+  if (a.N % cols_per_wg != 0) return hipErrorInvalidValue;  // every wavefront has columns
+  const int grid_x = a.N / cols_per_wg;
   if (grid_x <= 0 || grid_y <= 0) return hipSuccess;
   dim3 grid(grid_x, grid_y, gateup ? 1 : a.ksplit), block(256);
 #define MOELORA_SKINNY(NT_, P_, RT_, PIPE_)                                                       \

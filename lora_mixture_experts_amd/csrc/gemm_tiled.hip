@@ -31,11 +31,11 @@
 namespace moelora {
 
 // Store of a finished tile: SiLU-and-mul (gate_up, into act) or the plain store (down, into the
-// pair's row of D). Lane l holds rows 8*(v/4) + 4*(l/32) + (v%4) of each 32-row group and
+// pair's row of the K split's part of D). Lane l holds rows 8*(v/4) + 4*(l/32) + (v%4) of each 32-row group and
 // column (l % 32) of each 32-column fragment.
 template <bool GATEUP, int BN, int WM, int WN, int FM, int FN>
 __device__ __forceinline__ void tiled_store(const GemmArgs& a, f32x16 (&acc)[FM][FN], int row0,
-                                            int wm, int wn, int ntile, int lane) {
+                                            int wm, int wn, int ntile, int ks, int lane) {
   const size_t N = (size_t)a.N;
   const int fr = lane & 31, fg = lane >> 5;
   // column of fragment jn: gate_up act column (gate and up halves share it); down output column
@@ -60,7 +60,8 @@ __device__ __forceinline__ void tiled_store(const GemmArgs& a, f32x16 (&acc)[FM]
         }
       } else {
 #pragma unroll
-        for (int jn = 0; jn < FN; ++jn) a.d_out[(size_t)p * N + col_of(jn)] = acc[i][jn][v];
+        for (int jn = 0; jn < FN; ++jn)
+          a.d_out[ks * a.d_split_stride + (size_t)p * N + col_of(jn)] = acc[i][jn][v];
       }
     }
   }
@@ -265,13 +266,17 @@ __global__ __launch_bounds__(256, 1) void tiled_gemm_kernel(GemmArgs a, int n_ti
   // round-robin over the 8 XCDs, so each XCD is given an equal contiguous range of that
   // numbering: the workgroups it runs at once cover a few groups, every token tile and weight
   // tile fetched into its L2 serves several of them, and no XCD gets more tiles than another.
+  // (down may also split K: split ks of every tile comes after all tiles of split ks - 1)
   const int nblk = *a.n_blocks;
-  const int live = nblk * n_tiles_n;
+  const int tiles = nblk * n_tiles_n;
+  const int live = tiles * (GATEUP ? 1 : a.ksplit);
   const int per_xcd = (live + 7) >> 3;
   const int hw = blockIdx.x;
   const int slot = hw >> 3;
-  const int t = (hw & 7) * per_xcd + slot;
-  if (slot >= per_xcd || t >= live) return;
+  const int tk = (hw & 7) * per_xcd + slot;
+  if (slot >= per_xcd || tk >= live) return;
+  const int ks = GATEUP ? 0 : tk / tiles;        // K split
+  const int t = tk - ks * tiles;
   const int cg = t / (nblk * 8);                 // column group (all but the last are 8 wide)
   const int cols = min(8, n_tiles_n - cg * 8);
   const int u = t - cg * nblk * 8;
@@ -282,6 +287,8 @@ __global__ __launch_bounds__(256, 1) void tiled_gemm_kernel(GemmArgs a, int n_ti
   const int ntile = cg * 8 + w / rows;
   const int e = a.block_expert[blk];
   const int K = a.K;
+  const int kspan = GATEUP ? K : K / a.ksplit;  // this split's K range: [ks * kspan, +kspan)
+  const uint32_t kbyte0 = (uint32_t)ks * kspan * 2;
   const size_t N = (size_t)a.N;
   const int row0 = blk * BM;
   const size_t w_rows = GATEUP ? 2 * N : N;  // weight rows of one expert
@@ -295,7 +302,8 @@ __global__ __launch_bounds__(256, 1) void tiled_gemm_kernel(GemmArgs a, int n_ti
     const int srow = row0 + row;
     const int p = a.sorted_pairs[srow];
     xo[i] = p < 0 ? kOutOfRange
-                  : (uint32_t)((GATEUP ? (size_t)(p / a.k) : (size_t)srow) * K * 2) + 16u * chunk;
+                  : (uint32_t)((GATEUP ? (size_t)(p / a.k) : (size_t)srow) * K * 2) + kbyte0 +
+                        16u * chunk;
   }
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
@@ -309,7 +317,7 @@ __global__ __launch_bounds__(256, 1) void tiled_gemm_kernel(GemmArgs a, int n_ti
     } else {
       wrow = (size_t)ntile * BN + row;
     }
-    wo[i] = (uint32_t)(wrow * K * 2) + 16u * chunk;
+    wo[i] = (uint32_t)(wrow * K * 2) + kbyte0 + 16u * chunk;
   }
   const u32x4 xr = buffer_desc(a.X, a.x_bytes);
   const u32x4 wr = buffer_desc(a.W + (size_t)e * w_rows * K, (uint32_t)(w_rows * K * 2));
@@ -322,11 +330,13 @@ __global__ __launch_bounds__(256, 1) void tiled_gemm_kernel(GemmArgs a, int n_ti
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  Pipe::run(acc, xr, xo, wr, wo, lds, K, wave, lane);
+  Pipe::run(acc, xr, xo, wr, wo, lds, kspan, wave, lane);
 
-  lora_expand_lds<GATEUP, BM, BN, WM, WN, FM, FN, Pipe::LDS_BYTES>(a, acc, lds, row0, wm, wn,
-                                                                    ntile, e, wave, lane);
-  tiled_store<GATEUP, BN, WM, WN, FM, FN>(a, acc, row0, wm, wn, ntile, lane);
+  // the LoRA term goes into K split 0 only (the combine adds the splits)
+  if (ks == 0)
+    lora_expand_lds<GATEUP, BM, BN, WM, WN, FM, FN, Pipe::LDS_BYTES>(a, acc, lds, row0, wm, wn,
+                                                                      ntile, e, wave, lane);
+  tiled_store<GATEUP, BN, WM, WN, FM, FN>(a, acc, row0, wm, wn, ntile, ks, lane);
 }
 
 template <bool GATEUP, int BM, int BN, int WM, int WN, int BK, int NST>
@@ -351,11 +361,12 @@ hipError_t launch_tiled_t(const GemmArgs& a, int n_tiles_n, int total, hipStream
 hipError_t launch_tiled(const TiledConfig& c, bool gateup, const GemmArgs& a, hipStream_t stream) {
   const int cols = gateup ? 2 * a.N : a.N;
   if (cols % c.bn != 0) return hipErrorInvalidValue;
+  const int splits = gateup ? 1 : a.ksplit;
+  if (splits < 1 || (a.K / splits) % c.bk != 0 || a.K % splits != 0) return hipErrorInvalidValue;
   const int n_tiles_n = cols / c.bn;
-  // grouped order (8 x 8 tiles per group, see the kernel), padded to whole groups and to a
-  // multiple of the 8 XCDs
-  const int gm = (a.n_blocks_max + 7) / 8, gn = (n_tiles_n + 7) / 8;
-  int total = gm * gn * 64;
+  // one workgroup per (row block, column tile, K split) for the largest row-block count,
+  // rounded up to a multiple of the 8 XCDs
+  int total = a.n_blocks_max * n_tiles_n * splits;
   total = (total + 7) / 8 * 8;
   if (total <= 0) return hipSuccess;
 #define MOELORA_TILED(BM_, BN_, WM_, WN_, BK_, NST_)                                       \
