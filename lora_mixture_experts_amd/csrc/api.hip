@@ -95,12 +95,16 @@ PathPlan pick_path(int64_t P, int E, int h, int I) {
   pl.nt = mean <= 12.0 ? 1 : (mean <= 24.0 ? 2 : 4);
   // Row-block size against padding: an expert wastes up to bm - 1 rows, so the 256-row tile
   // (most MFMA work per loaded byte) only pays once experts hold several hundred rows.
-  const TiledConfig t64{64, 128, 32, 64, 64, 2}, t128{128, 128, 64, 64, 64, 2},
-      t256{256, 256, 128, 128, 64, 2};
+  // 128- and 256-row tiles run eight wavefronts (two per SIMD): one wavefront's LDS waits and
+  // barriers are covered by the other's MFMAs
+  const TiledConfig t64{64, 128, 32, 64, 64, 2, 4}, t64w{64, 256, 32, 64, 64, 2, 8},
+      t128{128, 128, 32, 64, 64, 2, 8}, t256{256, 256, 64, 128, 64, 2, 8};
   const bool fits256 = (2 * I) % 256 == 0 && h % 256 == 0;
   pl.tc = mean < 192.0 ? t64 : (mean < 768.0 || !fits256 ? t128 : t256);
   pl.tc_dn = pl.tc;
-  // MOELORA_TILED="bm,bn,wm,wn,bk,nst[;bm,bn,wm,wn,bk,nst]" forces the tiles of gate_up (and of
+  // 64-row blocks: gate_up (2I wide) takes 256 columns per tile with eight wavefronts
+  if (mean < 192.0) pl.tc = t64w;
+  // MOELORA_TILED="bm,bn,wm,wn,bk,nst[,nw][;...]" forces the tiles of gate_up (and of
   // down when a second set with the same bm follows) for experiments
   static int forced = -1;  // -1 unread, 0 none, 1 skinny, 2 tiled, 3/4 skinny with 1/2 tiles
   static TiledConfig ft, ftd;
@@ -114,9 +118,10 @@ PathPlan pick_path(int64_t P, int E, int h, int I) {
     const char* tenv = getenv("MOELORA_TILED");
     if (tenv) {
       auto parse = [](const char* str, TiledConfig* c) {
-        int v[6] = {0, 0, 0, 0, 64, 2};
-        const int n = sscanf(str, "%d,%d,%d,%d,%d,%d", &v[0], &v[1], &v[2], &v[3], &v[4], &v[5]);
-        *c = TiledConfig{v[0], v[1], v[2], v[3], v[4], v[5]};
+        int v[7] = {0, 0, 0, 0, 64, 2, 4};
+        const int n = sscanf(str, "%d,%d,%d,%d,%d,%d,%d", &v[0], &v[1], &v[2], &v[3], &v[4], &v[5],
+                             &v[6]);
+        *c = TiledConfig{v[0], v[1], v[2], v[3], v[4], v[5], v[6]};
         return n >= 4;
       };
       if (parse(tenv, &ft)) {

@@ -74,7 +74,8 @@ __device__ __forceinline__ void tiled_store(const GemmArgs& a, f32x16 (&acc)[FM]
 // 32-row group the run overlaps adds (z restricted to the run's rows) x B over K = r. Each
 // wavefront first loads the z rows of its groups and keeps them as bf16 high and low parts in
 // registers.
-template <bool GATEUP, int BM, int BN, int WM, int WN, int FM, int FN, uint32_t LDS_BYTES>
+template <bool GATEUP, int BM, int BN, int WM, int WN, int FM, int FN, uint32_t LDS_BYTES,
+          int NWAVES>
 __device__ __forceinline__ void lora_expand_lds(const GemmArgs& a, f32x16 (&acc)[FM][FN],
                                                 uint16_t* lds, int row0, int wm, int wn,
                                                 int ntile, int e, int wave, int lane) {
@@ -206,7 +207,7 @@ __device__ __forceinline__ void lora_expand_lds(const GemmArgs& a, f32x16 (&acc)
 
   for (int b0 = 0; b0 < nrun; b0 += rb) {
     const int nb = min(rb, nrun - b0);
-    for (int blk = wave; blk < nb * bpr; blk += 4) {
+    for (int blk = wave; blk < nb * bpr; blk += NWAVES) {
       const int kk = blk / bpr, bi = blk % bpr;
       const int ad = __builtin_amdgcn_readfirstlane(s_ad[b0 + kk]);
       const int row = bi * rpb + lane / cpr;
@@ -247,10 +248,10 @@ __device__ __forceinline__ void lora_expand_lds(const GemmArgs& a, f32x16 (&acc)
   }
 }
 
-template <bool GATEUP, int BM, int BN, int WM, int WN, int BK, int NST>
-__global__ __launch_bounds__(256, 1) void tiled_gemm_kernel(GemmArgs a, int n_tiles_n,
+template <bool GATEUP, int BM, int BN, int WM, int WN, int BK, int NST, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void tiled_gemm_kernel(GemmArgs a, int n_tiles_n,
                                                             int /*grid_total*/) {
-  using Pipe = TilePipe<BM, BN, WM, WN, BK, NST>;
+  using Pipe = TilePipe<BM, BN, WM, WN, BK, NST, true, NW>;
   constexpr int FM = Pipe::FM, FN = Pipe::FN, NA = Pipe::NA, NB = Pipe::NB;
   static_assert(!GATEUP || FN % 2 == 0, "gate_up needs gate and up halves per wave");
 
@@ -334,16 +335,17 @@ __global__ __launch_bounds__(256, 1) void tiled_gemm_kernel(GemmArgs a, int n_ti
 
   // the LoRA term goes into K split 0 only (the combine adds the splits)
   if (ks == 0)
-    lora_expand_lds<GATEUP, BM, BN, WM, WN, FM, FN, Pipe::LDS_BYTES>(a, acc, lds, row0, wm, wn,
-                                                                      ntile, e, wave, lane);
+    lora_expand_lds<GATEUP, BM, BN, WM, WN, FM, FN, Pipe::LDS_BYTES, NW>(a, acc, lds, row0, wm,
+                                                                          wn, ntile, e, wave,
+                                                                          lane);
   tiled_store<GATEUP, BN, WM, WN, FM, FN>(a, acc, row0, wm, wn, ntile, ks, lane);
 }
 
-template <bool GATEUP, int BM, int BN, int WM, int WN, int BK, int NST>
+template <bool GATEUP, int BM, int BN, int WM, int WN, int BK, int NST, int NW>
 hipError_t launch_tiled_t(const GemmArgs& a, int n_tiles_n, int total, hipStream_t stream) {
-  constexpr int lds_bytes = TilePipe<BM, BN, WM, WN, BK, NST>::LDS_BYTES;
+  constexpr int lds_bytes = TilePipe<BM, BN, WM, WN, BK, NST, true, NW>::LDS_BYTES;
   static_assert(lds_bytes <= kLdsBytes, "LDS stages must fit");
-  auto kern = tiled_gemm_kernel<GATEUP, BM, BN, WM, WN, BK, NST>;
+  auto kern = tiled_gemm_kernel<GATEUP, BM, BN, WM, WN, BK, NST, NW>;
   static bool attr_set[64] = {};
   int dev = 0;
   hipError_t err = hipGetDevice(&dev);
@@ -354,7 +356,7 @@ hipError_t launch_tiled_t(const GemmArgs& a, int n_tiles_n, int total, hipStream
     if (err != hipSuccess) return err;
     attr_set[dev] = true;
   }
-  hipLaunchKernelGGL(kern, dim3(total), dim3(256), lds_bytes, stream, a, n_tiles_n, total);
+  hipLaunchKernelGGL(kern, dim3(total), dim3(64 * NW), lds_bytes, stream, a, n_tiles_n, total);
   return hipGetLastError();
 }
 
@@ -369,19 +371,20 @@ hipError_t launch_tiled(const TiledConfig& c, bool gateup, const GemmArgs& a, hi
   int total = a.n_blocks_max * n_tiles_n * splits;
   total = (total + 7) / 8 * 8;
   if (total <= 0) return hipSuccess;
-#define MOELORA_TILED(BM_, BN_, WM_, WN_, BK_, NST_)                                       \
-  if (c.bm == BM_ && c.bn == BN_ && c.wm == WM_ && c.wn == WN_ && c.bk == BK_ && c.nst == NST_) \
-    return gateup                                                                           \
-        ? launch_tiled_t<true, BM_, BN_, WM_, WN_, BK_, NST_>(a, n_tiles_n, total, stream)  \
-        : launch_tiled_t<false, BM_, BN_, WM_, WN_, BK_, NST_>(a, n_tiles_n, total, stream);
-  MOELORA_TILED(64, 128, 32, 64, 64, 2)
-  MOELORA_TILED(128, 128, 64, 64, 64, 2)
-  MOELORA_TILED(256, 256, 128, 128, 64, 2)
-  MOELORA_TILED(64, 128, 32, 64, 64, 3)
-  MOELORA_TILED(128, 128, 64, 64, 32, 4)
-  MOELORA_TILED(256, 256, 128, 128, 32, 4)
-  MOELORA_TILED(256, 256, 128, 128, 32, 5)
-  MOELORA_TILED(256, 128, 128, 64, 64, 3)
+#define MOELORA_TILED(BM_, BN_, WM_, WN_, BK_, NST_, NW_)                                   \
+  if (c.bm == BM_ && c.bn == BN_ && c.wm == WM_ && c.wn == WN_ && c.bk == BK_ && c.nst == NST_ && \
+      c.nw == NW_)                                                                              \
+    return gateup                                                                               \
+        ? launch_tiled_t<true, BM_, BN_, WM_, WN_, BK_, NST_, NW_>(a, n_tiles_n, total, stream) \
+        : launch_tiled_t<false, BM_, BN_, WM_, WN_, BK_, NST_, NW_>(a, n_tiles_n, total, stream);
+  MOELORA_TILED(64, 128, 32, 64, 64, 2, 4)
+  MOELORA_TILED(128, 128, 64, 64, 64, 2, 4)
+  MOELORA_TILED(256, 256, 128, 128, 64, 2, 4)
+  MOELORA_TILED(128, 128, 32, 64, 64, 2, 8)
+  MOELORA_TILED(256, 256, 64, 128, 64, 2, 8)
+  MOELORA_TILED(256, 256, 128, 64, 64, 2, 8)
+  MOELORA_TILED(256, 256, 64, 128, 32, 5, 8)
+  MOELORA_TILED(64, 256, 32, 64, 64, 2, 8)
 #undef MOELORA_TILED
   return hipErrorInvalidValue;
 }

@@ -69,10 +69,11 @@ struct GemmArgs {
   int n_blocks_max;   // row blocks the grid is sized for (>= *n_blocks)
 };
 
-// Tile shape of the LDS-staged GEMM: four wavefronts of WM x WN each; NST LDS stages of BK k.
+// Tile shape of the LDS-staged GEMM: nw wavefronts of WM x WN each; NST LDS stages of BK k.
 struct TiledConfig {
   int bm, bn, wm, wn;
   int bk, nst;
+  int nw = 4;
 };
 
 // Tile shape of the skinny (few rows per expert) GEMM.

@@ -1,7 +1,7 @@
 // Main loop of the LDS-tiled expert GEMM: operand tiles are loaded from HBM straight into a
 // ring of LDS stages and multiplied on 32x32x16 bf16 MFMAs. Internal to libmoelora.
 //
-// C[m][n] += sum_k A[m][k] B[n][k] for a BM x BN tile, four wavefronts of WM x WN each.
+// C[m][n] += sum_k A[m][k] B[n][k] for a BM x BN tile, NWAVES wavefronts of WM x WN each.
 // Both operands are K-contiguous, so every MFMA fragment (32 rows x 8 consecutive k per lane)
 // is one 16-byte LDS read. A stage holds BK k of both tiles, row-major, BK k per row, with the
 // 16-byte chunk index XOR-swizzled by the row so that fragment reads are free of bank
@@ -51,22 +51,23 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int NST, bool SPREAD = true>
+template <int BM, int BN, int WM, int WN, int BK, int NST, bool SPREAD = true, int NWAVES = 4>
 struct TilePipe {
   static_assert(BK == 32 || BK == 64, "K step of 32 or 64");
   static_assert(NST >= 2, "at least two LDS stages");
   static constexpr int WAVES_N = BN / WN;
-  static_assert((BM / WM) * WAVES_N == 4, "four wavefronts per workgroup");
+  static_assert((BM / WM) * WAVES_N == NWAVES, "WM x WN wavefront tiles cover the tile");
   static constexpr int FM = WM / 32, FN = WN / 32;
   static constexpr int CPR = BK / 8;               // 16-byte chunks per tile row
   static constexpr int RPB = 64 / CPR;             // tile rows per 1 KB load block
-  static constexpr int NA = BM / RPB / 4;          // load blocks per wavefront and stage (A)
-  static constexpr int NB = BN / RPB / 4;          // (B)
+  static constexpr int NA = BM / RPB / NWAVES;     // load blocks per wavefront and stage (A)
+  static constexpr int NB = BN / RPB / NWAVES;     // (B)
   static constexpr int PER = NA + NB;              // loads per wavefront and stage
   static constexpr int SUB = BK / 16;              // MFMA sub-steps per stage
   static constexpr uint32_t STAGE_BYTES = (BM + BN) * BK * 2;
   static constexpr uint32_t LDS_BYTES = NST * STAGE_BYTES;
-  static_assert(NA * RPB * 4 == BM && NB * RPB * 4 == BN, "tiles must split into load blocks");
+  static_assert(NA * RPB * NWAVES == BM && NB * RPB * NWAVES == BN,
+                "tiles must split into load blocks");
   static_assert(FM + FN <= 15, "one sub-step of fragment reads must fit the LDS counter");
   static_assert((NST - 1) * PER < 64, "in-flight loads must fit vmcnt");
 
@@ -81,7 +82,7 @@ struct TilePipe {
   // (rows of B likewise): the lane fills slot lane % CPR of row lane / CPR of the block, so it
   // fetches the chunk that the swizzle puts in that slot of that (tile) row.
   __device__ static __forceinline__ int load_row(int i, int wave, int lane) {
-    return (i * 4 + wave) * RPB + lane / CPR;
+    return (i * NWAVES + wave) * RPB + lane / CPR;
   }
   __device__ static __forceinline__ int load_chunk(int row, int lane) {
     return swz(row, lane % CPR);
@@ -98,9 +99,9 @@ struct TilePipe {
       const uint32_t sa = lds0 + stage * STAGE_BYTES + wave * 1024;
       const uint32_t sb = sa + BM * BK * 2;
 #pragma unroll
-      for (int i = 0; i < NA; ++i) lds_dma16(xr, xo[i], soff, sa + i * 4096);
+      for (int i = 0; i < NA; ++i) lds_dma16(xr, xo[i], soff, sa + i * NWAVES * 1024);
 #pragma unroll
-      for (int i = 0; i < NB; ++i) lds_dma16(wr, wo[i], soff, sb + i * 4096);
+      for (int i = 0; i < NB; ++i) lds_dma16(wr, wo[i], soff, sb + i * NWAVES * 1024);
     };
     const int fr = lane & 31, fg = lane >> 5;
     auto read_frags = [&](int stage, int j, u32x4* af, u32x4* bf) {
@@ -148,8 +149,8 @@ struct TilePipe {
 #pragma unroll
         for (int d = 0; d < PER; ++d) {
           if ((d * NM) / PER != t) continue;
-          if (d < NA) lds_dma16(xr, xo[d], soff, sa + d * 4096);
-          else lds_dma16(wr, wo[d - NA], soff, sb + (d - NA) * 4096);
+          if (d < NA) lds_dma16(xr, xo[d], soff, sa + d * NWAVES * 1024);
+          else lds_dma16(wr, wo[d - NA], soff, sb + (d - NA) * NWAVES * 1024);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
