@@ -154,7 +154,8 @@ PathPlan pick_path(int64_t P, int E, int h, int I) {
 
 bool skinny_instantiated(const SkinnyConfig& c, bool gateup) {
   static const int have[][5] = {{1, 4, 1, 1, 0}, {1, 4, 1, 0, 0}, {1, 4, 2, 1, 0}, {1, 4, 2, 0, 0},
-                                {1, 8, 1, 1, 0}, {1, 8, 1, 0, 0}, {2, 4, 1, 1, 0}, {2, 8, 1, 1, 0},
+                                {1, 8, 1, 1, 0}, {1, 8, 1, 0, 0}, {2, 4, 1, 1, 0}, {2, 4, 2, 1, 0},
+                                {2, 8, 1, 1, 0},
                                 {4, 4, 1, 1, 0}, {1, 4, 1, 1, 1}, {1, 4, 1, 0, 1}, {1, 8, 1, 1, 1},
                                 {1, 8, 1, 0, 1}};
   if (c.split && !gateup) return false;
@@ -173,10 +174,11 @@ struct SkinnyPlan {
 
 SkinnyPlan pick_skinny(int nt, int h, int I) {
   SkinnyPlan pl;
-  // measured on decode (16 experts, ~8 rows each): gate_up keeps gate and up rows in one
-  // wavefront; down streams two row tiles per wavefront and splits K in two
+  // measured on decode (16 experts, ~8 rows each) and FG (128 experts, 16 rows each): gate_up
+  // keeps gate and up rows in one wavefront; down streams two row tiles per wavefront (and on
+  // 16-row blocks splits K in two)
   pl.gu = SkinnyConfig{nt, 4, 1, 1, 0};
-  pl.dn = SkinnyConfig{nt, 4, nt == 1 ? 2 : 1, 1, 0};
+  pl.dn = SkinnyConfig{nt, 4, nt <= 2 ? 2 : 1, 1, 0};
   pl.ksplit = nt == 1 ? 2 : 1;
   static int ov[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   static bool parsed = false;
@@ -404,6 +406,13 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
     // last, partial round of 256x256 tiles then costs a large share of the time)
     const int64_t est_tiles = (int64_t)((P + path.bm - 1) / path.bm + E) * (h / path.tc_dn.bn);
     plan.ksplit = est_tiles < 4 * 256 ? kMaxDownSplit : 1;
+    // MOELORA_DOWN_SPLIT=1|2 overrides it (experiments)
+    static int down_split = -1;
+    if (down_split < 0) {
+      const char* env = getenv("MOELORA_DOWN_SPLIT");
+      down_split = env ? atoi(env) : 0;
+    }
+    if (down_split == 1 || down_split == 2) plan.ksplit = down_split;
   }
   g.ksplit = 1;
   g.d_split_stride = P * (int64_t)h;

@@ -290,6 +290,7 @@ hipError_t launch_skinny(const SkinnyConfig& c, bool gateup, const GemmArgs& a, 
   MOELORA_SKINNY(1, 8, 1, true)
   MOELORA_SKINNY(1, 8, 1, false)
   MOELORA_SKINNY(2, 4, 1, true)
+  MOELORA_SKINNY(2, 4, 2, true)
   MOELORA_SKINNY(2, 8, 1, true)
   MOELORA_SKINNY(4, 4, 1, true)
   MOELORA_SKINNY_SPLIT(1, 4, true)
