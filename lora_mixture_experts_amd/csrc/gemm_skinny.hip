@@ -97,11 +97,27 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs a) {
   constexpr int BM = 16 * NT;
   constexpr int KS = 32 * P;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n0 = SPLIT ? (blockIdx.x * 2 + (wave & 1)) * 16 : (blockIdx.x * 4 + wave) * 16 * RT;
+  // Work order: the live (row block, column tile) items are numbered in groups of G consecutive
+  // row blocks, column tile by column tile, and every XCD (hardware workgroup ids go
+  // round-robin over the 8) gets an equal contiguous share. With G = 1 (the default) an XCD
+  // takes whole row blocks: their token rows stay in its L2 while the column tiles pass and
+  // it streams consecutive weight rows of one expert.
+  const int ncol = a.n_col_tiles;
+  const int nblk = *a.n_blocks;
+  const int live = nblk * ncol;
+  const int per_xcd = (live + 7) >> 3;
+  const int slot = blockIdx.x >> 3;
+  const int t = (blockIdx.x & 7) * per_xcd + slot;
+  if (slot >= per_xcd || t >= live) return;
+  const int G = a.blk_group;  // row blocks per group
+  const int sg = t / (G * ncol);
+  const int rows_g = min(G, nblk - sg * G);
+  const int u = t - sg * G * ncol;
+  const int blk = sg * G + u % rows_g;
+  const int ctile = u / rows_g;
+  const int n0 = SPLIT ? (ctile * 2 + (wave & 1)) * 16 : (ctile * 4 + wave) * 16 * RT;
   const bool up_wave = SPLIT && wave >= 2;
   __shared__ f32x4 s_up[SPLIT ? 2 * 64 * NT : 1];
-  const int blk = blockIdx.y;
-  if (blk >= *a.n_blocks) return;
   const int zsplit = blockIdx.z;
   constexpr int BMZ = 16 * NT;
 
@@ -264,9 +280,13 @@ hipError_t launch_skinny(const SkinnyConfig& c, bool gateup, const GemmArgs& a, 
   const bool split = gateup && c.split;
   const int cols_per_wg = split ? 32 : 4 * 16 * c.rt;
   if (a.N % cols_per_wg != 0) return hipErrorInvalidValue;  // every wavefront has columns
-  const int grid_x = a.N / cols_per_wg;
-  if (grid_x <= 0 || grid_y <= 0) return hipSuccess;
-  dim3 grid(grid_x, grid_y, gateup ? 1 : a.ksplit), block(256);
+  const int ncol = a.N / cols_per_wg;
+  if (ncol <= 0 || grid_y <= 0) return hipSuccess;
+  if (ncol != a.n_col_tiles) return hipErrorInvalidValue;
+  // one workgroup per (row block, column tile) for the largest block count, in a 1-D grid
+  // rounded up to the 8 XCDs (the kernel maps its id onto the live items)
+  const int total = ((grid_y * ncol) + 7) / 8 * 8;
+  dim3 grid(total, 1, gateup ? 1 : a.ksplit), block(256);
 #define MOELORA_SKINNY(NT_, P_, RT_, PIPE_)                                                       \
   if (c.nt == NT_ && c.p == P_ && c.rt == RT_ && c.pipe == PIPE_ && !split) {                     \
     if (gateup)                                                                                   \
