@@ -232,12 +232,15 @@ bool moelora_make_layout(int T, int h, int I, int E, int nA, int r, int topk, Mo
   L->expert_off = take(4 * (size_t)(E + 1));
   L->n_blocks = take(4);
   L->block_expert = take(4 * (size_t)(L->cap / 16 + 1));
+  L->block_seg = take(4 * (size_t)(L->cap / 16 + 1));
+  L->pair_row = take(4 * (size_t)P);
   L->seg_table = take(16 * (size_t)P);
   L->n_seg = take(4);
   L->z1 = take(4 * (size_t)kMaxSplit * L->cap * r);
   L->z2 = take(4 * (size_t)kMaxSplit * L->cap * r);
+  L->zhl = take(2 * 2 * (size_t)L->cap * r);
   L->act = take(2 * (size_t)L->cap * I);
-  L->dpair = take(4 * (size_t)kMaxDownSplit * P * h);
+  L->dpair = take(4 * (size_t)kMaxDownSplit * L->cap * h);
   L->align_cnt = take(4 * (size_t)E * (nA + 1));
   L->align_start = take(4 * (size_t)E * (nA + 1));
   L->align_lists = take(4 * align_list_ints(T, topk, E));
@@ -312,6 +315,8 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   int* sorted = (int*)(ws + L.sorted);
   int* n_blocks = (int*)(ws + L.n_blocks);
   int* block_expert = (int*)(ws + L.block_expert);
+  int* block_seg = (int*)(ws + L.block_seg);
+  int* pair_row = (int*)(ws + L.pair_row);
   float* z1 = (float*)(ws + L.z1);
   float* z2 = (float*)(ws + L.z2);
   uint16_t* act = (uint16_t*)(ws + L.act);
@@ -341,6 +346,8 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   al.n_seg = (int*)(ws + L.n_seg);
   al.flags = (int*)(ws + L.flags);
   al.block_expert = block_expert;
+  al.block_seg = block_seg;
+  al.pair_row = pair_row;
   al.n_blocks = n_blocks;
   al.g_cnt = (int*)(ws + L.align_cnt);
   al.g_start = (int*)(ws + L.align_start);
@@ -372,6 +379,9 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   g.cap = L.cap;
   g.sorted_pairs = sorted;
   g.block_expert = block_expert;
+  g.block_seg = block_seg;
+  g.seg_table = al.seg_table;
+  g.n_seg = al.n_seg;
   g.n_blocks = n_blocks;
   g.adapter_ids = adapter_ids;
   g.k = topk;
@@ -391,6 +401,10 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   sh.zpart = z1;
   sh.cap = L.cap;
   if (launch_shrink(true, sh, tiles16, stream) != hipSuccess) return MOELORA_EHIP;
+  uint16_t* zhl = (uint16_t*)(ws + L.zhl);
+  if (path.tiled && launch_zfinal(z1, s1, L.cap, r, n_blocks, bm, (int64_t)max_blocks * bm, zhl,
+                                  stream) != hipSuccess)
+    return MOELORA_EHIP;
   if (!mark(ev, 3, stream)) return MOELORA_EHIP;
   g.X = (const uint16_t*)x;
   g.x_bytes = (uint32_t)((size_t)T * h * 2);
@@ -398,6 +412,7 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   g.Bw = (const uint16_t*)B1;
   g.zpart = z1;
   g.S = s1;
+  g.zhl = zhl;
   g.K = h;
   g.N = I;
   SkinnyPlan plan = pick_skinny(nt, h, I);
@@ -415,7 +430,7 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
     if (down_split == 1 || down_split == 2) plan.ksplit = down_split;
   }
   g.ksplit = 1;
-  g.d_split_stride = P * (int64_t)h;
+  g.d_split_stride = L.cap * (int64_t)h;
   {
     // MOELORA_SKINNY_GROUP overrides the skinny kernels' row blocks per group (experiments)
     static int grp = -1;
@@ -439,6 +454,9 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   sh.S = s2;
   sh.zpart = z2;
   if (launch_shrink(false, sh, tiles16, stream) != hipSuccess) return MOELORA_EHIP;
+  if (path.tiled && launch_zfinal(z2, s2, L.cap, r, n_blocks, bm, (int64_t)max_blocks * bm, zhl,
+                                  stream) != hipSuccess)
+    return MOELORA_EHIP;
   if (!mark(ev, 5, stream)) return MOELORA_EHIP;
   g.X = act;
   g.x_bytes = (uint32_t)((size_t)L.cap * I * 2);
@@ -456,8 +474,8 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   if (!mark(ev, 6, stream)) return MOELORA_EHIP;
 
   // weighted top-k combine -> y (bf16)
-  if (launch_combine(dpair, plan.ksplit, P * (int64_t)h, topk_w, T, topk, h, (uint16_t*)y, stream) !=
-      hipSuccess)
+  if (launch_combine(dpair, plan.ksplit, L.cap * (int64_t)h, pair_row, topk_w, T, topk, h,
+                     (uint16_t*)y, stream) != hipSuccess)
     return MOELORA_EHIP;
   if (!mark(ev, 7, stream)) return MOELORA_EHIP;
   return MOELORA_OK;
@@ -531,6 +549,8 @@ int moe_lora_route_align(const float* router_logits, const int32_t* adapter_ids,
   al.n_seg = n_seg;
   al.flags = (int*)(ws + L.flags);
   al.block_expert = nullptr;
+  al.block_seg = nullptr;
+  al.pair_row = nullptr;
   al.n_blocks = nullptr;
   al.g_cnt = (int*)(ws + L.align_cnt);
   al.g_start = (int*)(ws + L.align_start);

@@ -1,6 +1,7 @@
-// Weighted top-k combine: y[t] = sum_j w[t][j] * D[t*k + j], summed in slot order in fp32, then
-// rounded once to bf16 (round-to-nearest-even). D may arrive as ksplit partial buffers (split-K of
-// the down GEMM); they are added in split order first.
+// Weighted top-k combine: y[t] = sum_j w[t][j] * D[row(t*k + j)], summed in slot order in fp32,
+// then rounded once to bf16 (round-to-nearest-even). D holds the down GEMM's output rows in the
+// sorted (expert, adapter) order; pair_row maps a pair to its row. D may arrive as ksplit partial
+// buffers (split-K of the down GEMM); they are added in split order first.
 //
 // Page "vLLM MoE LoRA SageMaker Bedrock", section "Entendendo os Modelos MoE": the outputs of
 // the experts a token was sent to are aggregated. Each thread owns four consecutive features of
@@ -12,6 +13,7 @@ namespace moelora {
 
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ D, int ksplit,
                                                       int64_t split_stride,
+                                                      const int* __restrict__ pair_row,
                                                       const float* __restrict__ topk_w, int T,
                                                       int k, int h, uint16_t* __restrict__ y) {
   const int h4 = h >> 2;
@@ -22,9 +24,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < k; ++j) {
     const float w = topk_w[(size_t)t * k + j];
-    f32x4 d = *reinterpret_cast<const f32x4*>(D + ((size_t)t * k + j) * h + c);
+    const size_t row = (size_t)pair_row[(size_t)t * k + j];
+    f32x4 d = *reinterpret_cast<const f32x4*>(D + row * h + c);
     for (int z = 1; z < ksplit; ++z)
-      d += *reinterpret_cast<const f32x4*>(D + z * split_stride + ((size_t)t * k + j) * h + c);
+      d += *reinterpret_cast<const f32x4*>(D + z * split_stride + row * h + c);
 #pragma unroll
     for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(w, d[v], acc[v]);
   }
@@ -32,12 +35,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   *reinterpret_cast<u32x2*>(y + (size_t)t * h + c) = packed;
 }
 
-hipError_t launch_combine(const float* D, int ksplit, int64_t split_stride, const float* topk_w,
-                          int T, int k, int h, uint16_t* y, hipStream_t stream) {
+hipError_t launch_combine(const float* D, int ksplit, int64_t split_stride, const int* pair_row,
+                          const float* topk_w, int T, int k, int h, uint16_t* y,
+                          hipStream_t stream) {
   const int64_t n = (int64_t)T * (h / 4);
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, D,
-                     ksplit, split_stride, topk_w, T, k, h, y);
+                     ksplit, split_stride, pair_row, topk_w, T, k, h, y);
   return hipGetLastError();
 }
 

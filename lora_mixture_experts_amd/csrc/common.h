@@ -82,8 +82,8 @@ __device__ __forceinline__ int sanitize_adapter(int a, int nA) {
 // Workspace layout (host side). Every region starts on a 256-byte boundary.
 // ------------------------------------------------------------------------------------------
 struct MoeLoraLayout {
-  size_t topk_ids, topk_w, tok_flags, flags, sorted, expert_off, n_blocks, block_expert,
-      seg_table, n_seg, z1, z2, act, dpair, align_cnt, align_start, align_lists;
+  size_t topk_ids, topk_w, tok_flags, flags, sorted, expert_off, n_blocks, block_expert, block_seg,
+      pair_row, seg_table, n_seg, z1, z2, zhl, act, dpair, align_cnt, align_start, align_lists;
   size_t total;
   int64_t cap;     // rows of the sorted layout at the largest row-block size
   int max_bm;      // largest row-block size any path uses

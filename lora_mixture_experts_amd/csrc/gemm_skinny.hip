@@ -21,7 +21,7 @@
 // gate_up: a wave owns act columns [n0, n0+16): gate rows n0.. and up rows I+n0..; the
 //   epilogue adds z1 B1 to both, applies SiLU-and-mul and stores act (bf16) at the sorted row.
 // down:    a wave owns output features [n0, n0+16) of W2; the epilogue adds z2 B2 and stores
-//   the fp32 expert output at the pair's row of D (pair order t*k + j).
+//   the fp32 expert output at the sorted row of D (the combine finds a pair's row).
 #include "common.h"
 #include "kernels.h"
 
@@ -268,7 +268,7 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs a) {
           const uint16_t* const bd[1] = {a.Bw + (((size_t)ad * a.E + e) * N + nb) * a.r};
           lora_expand<1>(zrow, bd, a.r, d);
         }
-        *reinterpret_cast<f32x4*>(a.d_out + zsplit * a.d_split_stride + (size_t)p * N + nb) =
+        *reinterpret_cast<f32x4*>(a.d_out + zsplit * a.d_split_stride + (size_t)row * N + nb) =
             f32x4{d[0][0], d[0][1], d[0][2], d[0][3]};
       }
     }

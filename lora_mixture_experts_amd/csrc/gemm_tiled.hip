@@ -30,9 +30,11 @@
 
 namespace moelora {
 
-// Store of a finished tile: SiLU-and-mul (gate_up, into act) or the plain store (down, into the
-// pair's row of the K split's part of D). Lane l holds rows 8*(v/4) + 4*(l/32) + (v%4) of each 32-row group and
-// column (l % 32) of each 32-column fragment.
+// Store of a finished tile at its rows of the sorted layout: SiLU-and-mul (gate_up, into act) or
+// the plain store (down, into the K split's part of D). Padding rows hold zeros (their token rows
+// were loaded as zeros and carry no adapter) and are stored like the others, so the store needs
+// no per-row lookup. Lane l holds rows 8*(v/4) + 4*(l/32) + (v%4) of each 32-row group and column
+// (l % 32) of each 32-column fragment.
 template <bool GATEUP, int BN, int WM, int WN, int FM, int FN>
 __device__ __forceinline__ void tiled_store(const GemmArgs& a, f32x16 (&acc)[FM][FN], int row0,
                                             int wm, int wn, int ntile, int ks, int lane) {
@@ -45,145 +47,55 @@ __device__ __forceinline__ void tiled_store(const GemmArgs& a, f32x16 (&acc)[FM]
   };
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
-    const int grow0 = row0 + wm * WM + i * 32;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int srow = grow0 + 8 * (v / 4) + 4 * fg + (v % 4);
-      const int p = a.sorted_pairs[srow];
-      if (p < 0) continue;
+      const size_t srow = (size_t)row0 + wm * WM + i * 32 + 8 * (v / 4) + 4 * fg + (v % 4);
       if (GATEUP) {
 #pragma unroll
         for (int jn = 0; jn < FN / 2; ++jn) {
           const float g = acc[i][jn][v], u = acc[i][jn + FN / 2][v];
           const float hv = g / (1.f + __expf(-g)) * u;
-          a.act_out[(size_t)srow * N + col_of(jn)] = (uint16_t)f32_to_bf16_bits(hv);
+          a.act_out[srow * N + col_of(jn)] = (uint16_t)f32_to_bf16_bits(hv);
         }
       } else {
 #pragma unroll
         for (int jn = 0; jn < FN; ++jn)
-          a.d_out[ks * a.d_split_stride + (size_t)p * N + col_of(jn)] = acc[i][jn][v];
+          a.d_out[ks * a.d_split_stride + srow * N + col_of(jn)] = acc[i][jn][v];
       }
     }
   }
 }
 
-// LoRA expand of a whole tile through LDS (used after the LDS-staged main loop, whose LDS is
-// free by then). The tile's rows are sorted by adapter, so they form runs of one adapter; for
-// each run the tile's columns of B[adapter][expert] (BN rows x r, r-contiguous) are loaded
-// straight into LDS, up to as many runs at once as fit, with one wait per batch, and every
-// 32-row group the run overlaps adds (z restricted to the run's rows) x B over K = r. Each
-// wavefront first loads the z rows of its groups and keeps them as bf16 high and low parts in
-// registers.
+// Lane of the n-th set bit of a wavefront-uniform mask.
+__device__ __forceinline__ int nth_set_bit(uint64_t m, int n) {
+  for (int i = 0; i < n; ++i) m &= m - 1;
+  return __builtin_ctzll(m);
+}
+
+// LoRA expand of a whole tile, after the main loop (its LDS stages are free by then). The rows of
+// a tile are sorted by adapter, so the segments of the segment table that overlap it are runs of
+// one adapter; they start at the block's first segment, and lane j of every wavefront takes
+// segment first + j clipped to the tile (64 at a time), so no table is built. For each run with
+// an adapter the tile's columns of B[adapter][expert] (BN rows x r, r-contiguous) are loaded
+// straight into LDS, up to as many runs at once as fit, with one wait per batch, and every 32-row
+// group the run overlaps adds (z restricted to the run's rows) x B over K = r. z (the sum of the
+// shrink's split parts as bf16 high and low planes) is loaded while the first batch is in
+// flight.
 template <bool GATEUP, int BM, int BN, int WM, int WN, int FM, int FN, uint32_t LDS_BYTES,
           int NWAVES>
-__device__ __forceinline__ void lora_expand_lds(const GemmArgs& a, f32x16 (&acc)[FM][FN],
-                                                uint16_t* lds, int row0, int wm, int wn,
-                                                int ntile, int e, int wave, int lane) {
+__device__ __forceinline__ void lora_expand_segs(const GemmArgs& a, f32x16 (&acc)[FM][FN],
+                                                 uint16_t* lds, int blk, int row0, int wm, int wn,
+                                                 int ntile, int e, int wave, int lane) {
   constexpr int MAXSL = 4;  // 16-wide slices of r (r <= 64)
-  constexpr uint32_t TABLE_BYTES = ((5 * BM + 1) * 4 + 1023) / 1024 * 1024;
-  static_assert(LDS_BYTES >= TABLE_BYTES + BN * 64 * 2, "the B tile of one run must fit");
+  static_assert(LDS_BYTES >= BN * 64 * 2, "the B tile of one run must fit");
+  const int first = a.block_seg[blk];
+  if (first < 0) return;
+  const int nseg = *a.n_seg;
   const int r = a.r;
   const size_t N = (size_t)a.N;
   const size_t w_rows = GATEUP ? 2 * N : N;
   const int fr = lane & 31, fg = lane >> 5;
-  int* cp_t = reinterpret_cast<int*>(lds);  // change points of the row adapter
-  int* cp_ad = cp_t + BM;
-  int* s_lo = cp_ad + BM;  // runs with an adapter: tile rows [lo, hi)
-  int* s_hi = s_lo + BM;
-  int* s_ad = s_hi + BM;
-  int* s_n = s_ad + BM;
   const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
-
-  __syncthreads();  // every wavefront is done with the main loop's stages
-  if (wave == 0) {
-    int ncp = 0, prev = -2;
-    for (int t0 = 0; t0 < BM; t0 += 64) {
-      const int t = t0 + lane;
-      const int p = a.sorted_pairs[row0 + t];
-      const int ad = p >= 0 ? sanitize_adapter(a.adapter_ids[p / a.k], a.nA) : -1;
-      int before = __shfl(ad, (lane + 63) & 63);
-      if (lane == 0) before = prev;
-      const bool cp = ad != before;
-      const uint64_t m = __ballot(cp);
-      if (cp) {
-        const int pos = ncp + __popcll(m & lanemask_lt());
-        cp_t[pos] = t;
-        cp_ad[pos] = ad;
-      }
-      ncp += __popcll(m);
-      prev = __shfl(ad, 63);
-    }
-    int nrun = 0;
-    for (int j0 = 0; j0 < ncp; j0 += 64) {
-      const int j = j0 + lane;
-      const bool run = j < ncp && cp_ad[j] >= 0;
-      const uint64_t m = __ballot(run);
-      if (run) {
-        const int pos = nrun + __popcll(m & lanemask_lt());
-        s_lo[pos] = cp_t[j];
-        s_hi[pos] = j + 1 < ncp ? cp_t[j + 1] : BM;
-        s_ad[pos] = cp_ad[j];
-      }
-      nrun += __popcll(m);
-    }
-    if (lane == 0) *s_n = nrun;
-  }
-
-  // z of this wavefront's rows (the sum of the shrink's split parts), kept as bf16 high and low
-  // parts. Loaded half the groups at a time (the fp32 values of all groups at once would not
-  // fit beside the accumulators).
-  u32x4 zh[FM][MAXSL], zl[FM][MAXSL];
-  constexpr int GH = FM > 1 ? FM / 2 : 1;
-#pragma unroll
-  for (int i0 = 0; i0 < FM; i0 += GH) {
-    float zf[GH][MAXSL][8];
-#pragma unroll
-    for (int i = 0; i < GH; ++i)
-#pragma unroll
-      for (int sl = 0; sl < MAXSL; ++sl)
-#pragma unroll
-        for (int t = 0; t < 8; ++t) zf[i][sl][t] = 0.f;
-    const int64_t zstride = a.cap * r;
-    for (int sp = 0; sp < a.S; ++sp) {  // split-K parts of the shrink, in order
-#pragma unroll
-      for (int i = 0; i < GH; ++i) {
-        const float* zr =
-            a.zpart + sp * zstride + (size_t)(row0 + wm * WM + (i0 + i) * 32 + fr) * r;
-#pragma unroll
-        for (int sl = 0; sl < MAXSL; ++sl) {
-          const int q = 16 * sl + 8 * fg;
-          if (q < r) {
-            const f32x4 lo = *reinterpret_cast<const f32x4*>(zr + q);
-            const f32x4 hi = *reinterpret_cast<const f32x4*>(zr + q + 4);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              zf[i][sl][t] += lo[t];
-              zf[i][sl][4 + t] += hi[t];
-            }
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < GH; ++i)
-#pragma unroll
-      for (int sl = 0; sl < MAXSL; ++sl) {
-        uint32_t hb[8], lb[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          hb[t] = f32_to_bf16_bits(zf[i][sl][t]);
-          lb[t] = f32_to_bf16_bits(zf[i][sl][t] - __uint_as_float(hb[t] << 16));
-        }
-        zh[i0 + i][sl] = u32x4{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16),
-                               hb[4] | (hb[5] << 16), hb[6] | (hb[7] << 16)};
-        zl[i0 + i][sl] = u32x4{lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16),
-                               lb[4] | (lb[5] << 16), lb[6] | (lb[7] << 16)};
-      }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  __syncthreads();  // run table visible
-  const int nrun = *s_n;
-  if (nrun == 0) return;
 
   // B tile of one run in LDS: BN rows (the tile's weight rows) x r, the 16-byte chunk index
   // XOR-swizzled by the row (rows of r/8 chunks; 1 KB load blocks of 512/r rows). A fragment
@@ -193,8 +105,8 @@ __device__ __forceinline__ void lora_expand_lds(const GemmArgs& a, f32x16 (&acc)
   const int rsh = 16 / cpr;  // rows per swizzle step
   auto swz = [&](int row, int c) { return c ^ ((row / rsh) & (cpr - 1)); };
   const uint32_t run_bytes = (uint32_t)BN * r * 2;
-  const int rb = (int)((LDS_BYTES - TABLE_BYTES) / run_bytes);  // runs per batch (>= 3)
-  const int bpr = BN / rpb;                                      // load blocks per run
+  const int rb = (int)(LDS_BYTES / run_bytes);  // runs per batch (>= 2)
+  const int bpr = BN / rpb;                     // load blocks per run
   auto wrow_of_tile_row = [&](int row) -> size_t {
     if (GATEUP) {
       const int g = row / WN, rr = row % WN;
@@ -203,41 +115,103 @@ __device__ __forceinline__ void lora_expand_lds(const GemmArgs& a, f32x16 (&acc)
     }
     return (size_t)ntile * BN + row;
   };
-  const uint16_t* btile = lds + TABLE_BYTES / 2;
 
-  for (int b0 = 0; b0 < nrun; b0 += rb) {
-    const int nb = min(rb, nrun - b0);
-    for (int blk = wave; blk < nb * bpr; blk += NWAVES) {
-      const int kk = blk / bpr, bi = blk % bpr;
-      const int ad = __builtin_amdgcn_readfirstlane(s_ad[b0 + kk]);
-      const int row = bi * rpb + lane / cpr;
-      const int chunk = swz(row, lane % cpr);
-      const u32x4 br = buffer_desc(a.Bw + ((size_t)ad * a.E + e) * w_rows * r,
-                                   (uint32_t)(w_rows * r * 2));
-      lds_dma16(br, (uint32_t)(wrow_of_tile_row(row) * r * 2) + 16u * chunk, 0u,
-                lds0 + TABLE_BYTES + kk * run_bytes + bi * 1024);
+  // z of this wavefront's rows as bf16 high and low parts (one load each per 32-row group and
+  // 16-wide slice of r)
+  u32x4 zh[FM][MAXSL], zl[FM][MAXSL];
+  auto load_z = [&]() {
+    const uint16_t* zhp = a.zhl;
+    const uint16_t* zlp = a.zhl + (size_t)a.cap * r;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const size_t zrow = (size_t)(row0 + wm * WM + i * 32 + fr) * r;
+#pragma unroll
+      for (int sl = 0; sl < MAXSL; ++sl) {
+        const int q = 16 * sl + 8 * fg;
+        const u32x4 zero{0u, 0u, 0u, 0u};
+        zh[i][sl] = q < r ? *reinterpret_cast<const u32x4*>(zhp + zrow + q) : zero;
+        zl[i][sl] = q < r ? *reinterpret_cast<const u32x4*>(zlp + zrow + q) : zero;
+      }
     }
+  };
+
+  // lane j: segment c0 + j, clipped to the tile (segments from the block's first one on start
+  // inside the tile until one starts past it)
+  int c0 = first, lo = 0, hi = 0, ad = -1;
+  uint64_t in_mask = 0, runs = 0, batch = 0;
+  int nb = 0;
+  auto chunk = [&]() {
+    const int sj = c0 + lane;
+    bool in = false;
+    lo = hi = 0;
+    ad = -1;
+    if (sj < nseg) {
+      const u32x4 sg = *reinterpret_cast<const u32x4*>(a.seg_table + 4 * (size_t)sj);
+      const int st = (int)sg[2], cnt = (int)sg[3];
+      in = st < row0 + BM;
+      lo = max(st - row0, 0);
+      hi = min(st + cnt - row0, BM);
+      ad = sanitize_adapter((int)sg[1], a.nA);
+    }
+    in_mask = __ballot(in);
+    runs = __ballot(in && ad >= 0);
+  };
+  // the next chunk with runs with an adapter, if any
+  auto next_runs = [&]() {
+    while (!runs && (in_mask >> 63)) {
+      c0 += 64;
+      chunk();
+    }
+  };
+  // the next batch (the lowest rb runs left), its B tiles loaded into LDS
+  auto issue_batch = [&]() {
+    batch = 0;
+    nb = 0;
+    while (runs && nb < rb) {
+      batch |= runs & (~runs + 1);
+      runs &= runs - 1;
+      ++nb;
+    }
+    for (int bl = wave; bl < nb * bpr; bl += NWAVES) {
+      const int kk = bl / bpr, bi = bl % bpr;
+      const int adk = __builtin_amdgcn_readlane(ad, nth_set_bit(batch, kk));
+      const int row = bi * rpb + lane / cpr;
+      const int ch = swz(row, lane % cpr);
+      const u32x4 br = buffer_desc(a.Bw + ((size_t)adk * a.E + e) * w_rows * r,
+                                   (uint32_t)(w_rows * r * 2));
+      lds_dma16(br, (uint32_t)(wrow_of_tile_row(row) * r * 2) + 16u * ch, 0u,
+                lds0 + kk * run_bytes + bi * 1024);
+    }
+  };
+
+  chunk();
+  next_runs();
+  if (!runs) return;
+  issue_batch();
+  load_z();  // while the first batch is in flight
+  while (true) {
     wait_vmcnt<0>();
     __syncthreads();
     for (int kk = 0; kk < nb; ++kk) {
-      const int lo = s_lo[b0 + kk], hi = s_hi[b0 + kk];
-      const uint16_t* bt = btile + kk * (run_bytes / 2);
+      const int j = nth_set_bit(batch, kk);
+      const int rlo = __builtin_amdgcn_readlane(lo, j), rhi = __builtin_amdgcn_readlane(hi, j);
+      const uint16_t* bt = lds + kk * (run_bytes / 2);
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int g0 = wm * WM + i * 32;
-        if (lo >= g0 + 32 || hi <= g0) continue;
-        const bool in = g0 + fr >= lo && g0 + fr < hi;
+        if (rlo >= g0 + 32 || rhi <= g0) continue;
+        const bool inr = g0 + fr >= rlo && g0 + fr < rhi;
 #pragma unroll
         for (int sl = 0; sl < MAXSL; ++sl) {
           if (16 * sl >= r) continue;
           const int c = 2 * sl + fg;
           const u32x4 zero{0u, 0u, 0u, 0u};
-          const u32x4 za = in ? zh[i][sl] : zero, zb = in ? zl[i][sl] : zero;
+          const u32x4 za = inr ? zh[i][sl] : zero, zb = inr ? zl[i][sl] : zero;
 #pragma unroll
           for (int jn = 0; jn < FN; ++jn) {
             const int n = wn * WN + jn * 32 + fr;
-            const u32x4 bv = 8 * c < r ? *reinterpret_cast<const u32x4*>(bt + n * r + 8 * swz(n, c))
-                                       : zero;
+            const u32x4 bv =
+                8 * c < r ? *reinterpret_cast<const u32x4*>(bt + n * r + 8 * swz(n, c)) : zero;
             acc[i][jn] = mfma32(za, bv, acc[i][jn]);
             acc[i][jn] = mfma32(zb, bv, acc[i][jn]);
           }
@@ -245,6 +219,9 @@ __device__ __forceinline__ void lora_expand_lds(const GemmArgs& a, f32x16 (&acc)
       }
     }
     __syncthreads();  // the next batch overwrites the B tiles
+    next_runs();
+    if (!runs) break;
+    issue_batch();
   }
 }
 
@@ -333,11 +310,13 @@ __global__ __launch_bounds__(64 * NW, 1) void tiled_gemm_kernel(GemmArgs a, int 
 
   Pipe::run(acc, xr, xo, wr, wo, lds, kspan, wave, lane);
 
+  __syncthreads();  // every wavefront is done with the main loop's LDS stages
+
   // the LoRA term goes into K split 0 only (the combine adds the splits)
   if (ks == 0)
-    lora_expand_lds<GATEUP, BM, BN, WM, WN, FM, FN, Pipe::LDS_BYTES, NW>(a, acc, lds, row0, wm,
-                                                                          wn, ntile, e, wave,
-                                                                          lane);
+    lora_expand_segs<GATEUP, BM, BN, WM, WN, FM, FN, Pipe::LDS_BYTES, NW>(a, acc, lds, blk, row0,
+                                                                           wm, wn, ntile, e, wave,
+                                                                           lane);
   tiled_store<GATEUP, BN, WM, WN, FM, FN>(a, acc, row0, wm, wn, ntile, ks, lane);
 }
 

@@ -16,6 +16,9 @@ struct AlignArgs {
   int* n_seg;           // [1]
   int* flags;           // [1]
   int* block_expert;    // [padded total / block_m] or nullptr
+  int* block_seg;       // [padded total / block_m]: segment holding the block's first row, or -1
+                        // (a block of padding rows); written when block_expert is
+  int* pair_row;        // [T*k]: sorted row of each pair, or nullptr
   int* n_blocks;        // [1] or nullptr
   int* g_cnt;           // [E*(nA+1)] global scratch when the tables do not fit in LDS
   int* g_start;         // [E*(nA+1)]
@@ -52,18 +55,22 @@ struct GemmArgs {
   uint32_t x_bytes;    // size of X (< 2 GiB)
   const uint16_t* W;   // gate_up: W1 [E][2I][h]; down: W2 [E][h][I]
   const uint16_t* Bw;  // gate_up: B1 [nA][E][2I][r]; down: B2 [nA][E][h][r]
-  const float* zpart;  // [S][cap][r] LoRA shrink output, as S split-K parts
+  const float* zpart;  // [S][cap][r] LoRA shrink output, as S split-K parts (skinny)
   int S;
+  const uint16_t* zhl;  // [2][cap][r] the parts' sum as bf16 high and low planes (tiled)
   int64_t cap;
   const int* sorted_pairs;
   const int* block_expert;
+  const int* block_seg;  // first segment of each row block (or -1), see AlignArgs
+  const int* seg_table;  // [n_seg][4]: expert, adapter, first sorted row, rows
+  const int* n_seg;
   const int* n_blocks;
   const int* adapter_ids;
   int k, nA, E, r;
   int K;  // reduction length
   int N;  // gate_up: I (act columns); down: h
   uint16_t* act_out;  // gate_up: [cap][I]
-  float* d_out;       // down: [ksplit][T*k][h] partial sums
+  float* d_out;       // down: [ksplit][cap][h] partial sums, rows in sorted order
   int ksplit;         // down: K splits (gridDim.z); gate_up: 1
   int64_t d_split_stride;
   int n_blocks_max;   // row blocks the grid is sized for (>= *n_blocks)
@@ -92,11 +99,14 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int* topk_ids,
                         int* tok_flags, hipStream_t stream);
 hipError_t launch_align(const AlignArgs& a, size_t dyn_lds, hipStream_t stream);
 hipError_t launch_shrink(bool gather, const ShrinkArgs& a, int tiles, hipStream_t stream);
+hipError_t launch_zfinal(const float* zpart, int S, int64_t cap, int r, const int* n_blocks,
+                         int bm, int64_t max_rows, uint16_t* zhl, hipStream_t stream);
 hipError_t launch_skinny(const SkinnyConfig& c, bool gateup, const GemmArgs& a, int grid_y,
                          hipStream_t stream);
 hipError_t launch_tiled(const TiledConfig& c, bool gateup, const GemmArgs& a, hipStream_t stream);
-hipError_t launch_combine(const float* D, int ksplit, int64_t split_stride, const float* topk_w,
-                          int T, int k, int h, uint16_t* y, hipStream_t stream);
+hipError_t launch_combine(const float* D, int ksplit, int64_t split_stride, const int* pair_row,
+                          const float* topk_w, int T, int k, int h, uint16_t* y,
+                          hipStream_t stream);
 
 constexpr int kAlignThreads = 1024;
 constexpr int kAlignStaticLds = 17 * 1024;  // >= the align kernel's static LDS (16.7 KB)

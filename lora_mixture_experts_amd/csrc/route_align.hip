@@ -103,8 +103,8 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
 //            expert (stable), an (expert, wavefront) scan turns the ranks into positions
 //   phase D  count pairs per bucket b = e*(nA+1) + (a+1), one wavefront per expert list
 //   phase 2  exclusive scans: padded segment starts, expert offsets, segment table
-//   phase 3  padding slots (-1) and the row-block -> expert table
-//   phase 4  scatter pair ids; inside a bucket pairs keep token order
+//   phase 3  padding slots (-1) and the row-block -> expert (and first segment) tables
+//   phase 4  scatter pair ids (and each pair's row); inside a bucket pairs keep token order
 // Within a wavefront, lanes with equal key are found by one ballot per key bit, so the rank of
 // a pair among equal-key pairs of earlier lanes is an exact popcount. Every table lives in LDS
 // when it fits and in the workspace otherwise.
@@ -324,6 +324,11 @@ __global__ __launch_bounds__(1024) void align_kernel(AlignArgs a) {
         row[1] = (b - e * nb1) - 1;
         row[2] = st;
         row[3] = c;
+        // row blocks whose first row lies in this segment (with its padding) start at it
+        if (a.block_seg)
+          for (int bb = (st + block_m - 1) / block_m; bb * block_m < st + round_up_i(c, seg_pad);
+               ++bb)
+            a.block_seg[bb] = nz;
         ++nz;
       }
     }
@@ -350,8 +355,11 @@ __global__ __launch_bounds__(1024) void align_kernel(AlignArgs a) {
     }
     for (int s = s_off[e] + s_sexp[e] + lane; s < s_off[e + 1]; s += 64) a.sorted_pairs[s] = -1;
     if (a.block_expert)
-      for (int bb = s_off[e] / block_m + lane; bb < s_off[e + 1] / block_m; bb += 64)
+      for (int bb = s_off[e] / block_m + lane; bb < s_off[e + 1] / block_m; bb += 64) {
         a.block_expert[bb] = e;
+        // a block that starts on a padding row holds padding rows only
+        if (a.block_seg && bb * block_m >= s_off[e] + s_sexp[e]) a.block_seg[bb] = -1;
+      }
   }
   __syncthreads();
   for (int i = tid; i < nb; i += bd) cnt[i] = 0;
@@ -370,7 +378,11 @@ __global__ __launch_bounds__(1024) void align_kernel(AlignArgs a) {
       if (valid && (eq & lanemask_lt()) == 0ull) cur = atomicAdd(&cnt[e * nb1 + key], (int)__popcll(eq));
       const int src = valid ? (__ffsll((unsigned long long)eq) - 1) : lane;
       cur = __shfl(cur, src);
-      if (valid) a.sorted_pairs[start[e * nb1 + key] + cur + (int)__popcll(eq & lanemask_lt())] = p;
+      if (valid) {
+        const int pos = start[e * nb1 + key] + cur + (int)__popcll(eq & lanemask_lt());
+        a.sorted_pairs[pos] = p;
+        if (a.pair_row) a.pair_row[p] = pos;
+      }
     }
   }
 }
