@@ -374,6 +374,7 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   sh.nA = nA;
   sh.E = E;
   sh.r = r;
+  sh.xcd_ranges = path.tiled ? 1 : 0;
 
   GemmArgs g;
   g.cap = L.cap;

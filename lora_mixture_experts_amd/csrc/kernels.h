@@ -46,6 +46,7 @@ struct ShrinkArgs {
   int S;               // K splits over workgroups
   float* zpart;        // [S][cap][r]; written for the rows that carry an adapter
   int64_t cap;
+  int xcd_ranges;      // 1: each XCD takes a contiguous range of the work order (long runs)
 };
 
 // Base GEMM of one projection for the rows of the sorted layout, with the LoRA expand (and

@@ -26,10 +26,23 @@ namespace moelora {
 template <bool GATHER, int NCT>
 __global__ __launch_bounds__(256) void lora_shrink_kernel(ShrinkArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int row0 = blockIdx.x * 16;
-  const int s = blockIdx.y;
-  const int nblk = *a.n_blocks;
-  if (row0 >= nblk * a.bm) return;
+  // Work order: the live (16-row tile, split) items, split by split, tile by tile. Hardware
+  // workgroup ids go round-robin over the 8 XCDs. With long adapter runs (xcd_ranges) each XCD is
+  // given an equal contiguous range of that order instead, so that neighbouring tiles of one run
+  // and split run on one XCD and share the A slab of their K range in its L2; with short runs
+  // the round-robin spreads the costlier tiles (many runs) evenly.
+  const int live16 = *a.n_blocks * a.bm / 16;
+  const int live = live16 * a.S;
+  int item = blockIdx.x;
+  if (a.xcd_ranges) {
+    const int per_xcd = (live + 7) >> 3;
+    const int slot = blockIdx.x >> 3;
+    if (slot >= per_xcd) return;
+    item = (blockIdx.x & 7) * per_xcd + slot;
+  }
+  if (item >= live) return;
+  const int s = item / live16;
+  const int row0 = (item - s * live16) * 16;
   const int e = a.block_expert[row0 / a.bm];
 
   // adapter runs of the tile: run_lo[i]..run_hi[i] share adapter run_ad[i]
@@ -224,7 +237,8 @@ hipError_t launch_zfinal(const float* zpart, int S, int64_t cap, int r, const in
 
 hipError_t launch_shrink(bool gather, const ShrinkArgs& a, int tiles, hipStream_t stream) {
   if (tiles <= 0) return hipSuccess;
-  dim3 grid(tiles, a.S);
+  // (tile, split) items for the largest row-block count, rounded up to a multiple of the 8 XCDs
+  dim3 grid((unsigned)(((int64_t)tiles * a.S + 7) / 8 * 8));
 #define MOELORA_SHRINK(NCT_)                                                           \
   if (gather)                                                                          \
     hipLaunchKernelGGL((lora_shrink_kernel<true, NCT_>), grid, dim3(256), 0, stream, a); \

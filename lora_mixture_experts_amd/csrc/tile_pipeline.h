@@ -14,10 +14,6 @@
 
 #include "common.h"
 
-#ifndef MOELORA_PIPE_INTERLEAVE
-#define MOELORA_PIPE_INTERLEAVE 0
-#endif
-
 namespace moelora {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -49,23 +45,13 @@ __device__ __forceinline__ u32x4 buffer_desc(const void* base, uint32_t bytes) {
   return u32x4{(uint32_t)b, (uint32_t)(b >> 32) & 0xffffu, bytes, 0x00020000u};
 }
 
-// A 4-byte load per lane into LDS (lane l at lds_addr + 4 l), used to pull lines into L2.
-__device__ __forceinline__ void lds_dma4(u32x4 rsrc, uint32_t voff, uint32_t soff,
-                                         uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, %3 offen lds"
-               :
-               : "v"(voff), "s"(rsrc), "s"(lds_addr), "s"(soff)
-               : "memory", "m0");
-}
-
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int NST, bool SPREAD = true, int NWAVES = 4,
-          int PFD = 0>
+template <int BM, int BN, int WM, int WN, int BK, int NST, bool SPREAD = true, int NWAVES = 4>
 struct TilePipe {
   static_assert(BK == 32 || BK == 64, "K step of 32 or 64");
   static_assert(NST >= 2, "at least two LDS stages");
@@ -79,20 +65,11 @@ struct TilePipe {
   static constexpr int PER = NA + NB;              // loads per wavefront and stage
   static constexpr int SUB = BK / 16;              // MFMA sub-steps per stage
   static constexpr uint32_t STAGE_BYTES = (BM + BN) * BK * 2;
-  // L2 prefetch (PFD > 0): after the refill of step s, the rows of step s + PFD are touched
-  // with one 4-byte load per 64 bytes, landing in a 256-byte LDS sink that nothing reads, so
-  // that the refill of that step finds them in L2. NPA + NPB such loads per wavefront and step.
-  static constexpr int SPR = BK * 2 / 64;  // 64-byte pieces per tile row and step
-  static constexpr int NPA = PFD > 0 ? (NA * RPB * SPR + 63) / 64 : 0;
-  static constexpr int NPB = PFD > 0 ? (NB * RPB * SPR + 63) / 64 : 0;
-  static constexpr int NPF = NPA + NPB;
-  static constexpr uint32_t SINK = NST * STAGE_BYTES;
-  static constexpr uint32_t kPfNone = kOutOfRange;  // no piece: reads zeros, no traffic
-  static constexpr uint32_t LDS_BYTES = NST * STAGE_BYTES + (PFD > 0 ? 256 : 0);
+  static constexpr uint32_t LDS_BYTES = NST * STAGE_BYTES;
   static_assert(NA * RPB * NWAVES == BM && NB * RPB * NWAVES == BN,
                 "tiles must split into load blocks");
   static_assert(FM + FN <= 15, "one sub-step of fragment reads must fit the LDS counter");
-  static_assert((NST - 1) * (PER + NPF) + NPF < 64, "in-flight loads must fit vmcnt");
+  static_assert((NST - 1) * PER < 64, "in-flight loads must fit vmcnt");
 
   // Slot of chunk c in tile row r (XOR swizzle). The LDS has 64 banks of 4 bytes and serves a
   // 16-byte-per-lane read 16 lanes (256 bytes) at a time; the 16 lanes of a fragment read hold
@@ -125,33 +102,6 @@ struct TilePipe {
       for (int i = 0; i < NA; ++i) lds_dma16(xr, xo[i], soff, sa + i * NWAVES * 1024);
 #pragma unroll
       for (int i = 0; i < NB; ++i) lds_dma16(wr, wo[i], soff, sb + i * NWAVES * 1024);
-    };
-    // prefetch offsets: piece q*64 + lane of the wavefront's A (B) rows, from the load offsets
-    // of the lane that loads chunk slot 0 of that row
-    uint32_t pfa[NPA > 0 ? NPA : 1], pfb[NPB > 0 ? NPB : 1];
-    auto pf_offsets = [&](const uint32_t* off, int nblk, uint32_t* pf, int npf) {
-      for (int q = 0; q < npf; ++q) {
-        const int piece = q * 64 + lane, rl = piece / SPR, half = piece % SPR;
-        const int i = rl / RPB, r = rl % RPB;
-        uint32_t v = kPfNone;
-        for (int b = 0; b < nblk; ++b) {
-          const uint32_t o = (uint32_t)__shfl((int)off[b], r * CPR);
-          if (b == i) v = o;
-        }
-        const int row = (i * NWAVES + wave) * RPB + r;
-        pf[q] = (i < nblk && v < kPfNone) ? v - 16u * swz(row, 0) + 64u * half : kPfNone;
-      }
-    };
-    if (PFD > 0) {
-      pf_offsets(xo, NA, pfa, NPA);
-      pf_offsets(wo, NB, pfb, NPB);
-    }
-    auto prefetch = [&](int ks) {
-      const uint32_t soff = (uint32_t)ks * BK * 2;
-#pragma unroll
-      for (int q = 0; q < NPA; ++q) lds_dma4(xr, pfa[q], soff, lds0 + SINK);
-#pragma unroll
-      for (int q = 0; q < NPB; ++q) lds_dma4(wr, pfb[q], soff, lds0 + SINK);
     };
     const int fr = lane & 31, fg = lane >> 5;
     auto read_frags = [&](int stage, int j, u32x4* af, u32x4* bf) {
@@ -186,7 +136,6 @@ struct TilePipe {
       }
     };
 
-    const int nks_all = K / BK;
     // The last sub-step's MFMAs with the refill loads of step ks_load spread between them (one
     // load after MFMA floor(d * NM / PER)), so that issuing them does not stall the MFMA pipe.
     auto mfmas_with_loads = [&](const u32x4* af, const u32x4* bf, int ks_load, int st) {
@@ -205,18 +154,14 @@ struct TilePipe {
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (PFD > 0) prefetch(min(ks_load + PFD, nks_all - 1));
     };
 
     const int nks = K / BK;
     // prologue: steps 0 .. NST-1 in flight, wait for step 0
 #pragma unroll
-    for (int s = 0; s < NST; ++s) {
+    for (int s = 0; s < NST; ++s)
       if (s < nks) issue(s, s);
-      // (every stage load is followed by NPF prefetch loads, as in the loop below)
-      if (PFD > 0) prefetch(min(NST + s, nks - 1));
-    }
-    if (nks >= NST) wait_vmcnt<(NST - 1) * (PER + NPF) + NPF>();
+    if (nks >= NST) wait_vmcnt<(NST - 1) * PER>();
     else wait_vmcnt<0>();
     __syncthreads();
 
@@ -237,16 +182,14 @@ struct TilePipe {
         const u32x4* bc = (j & 1) ? bf1 : bf0;
         if (j < SUB - 1) {
           read_frags(stage, j + 1, an, bn);
-#if !MOELORA_PIPE_INTERLEAVE
           __builtin_amdgcn_sched_barrier(0);
-#endif
           mfmas_interleaved(ac, bc, true);
           __builtin_amdgcn_sched_barrier(0);
           continue;
         }
         // Step ks + 1 has landed once only the loads of steps ks + 2 .. ks + NST - 1 are
         // outstanding (everything, near the end, where the refills re-load the last step).
-        if (ks + NST - 1 < nks) wait_vmcnt<(NST - 2) * (PER + NPF) + NPF>();
+        if (ks + NST - 1 < nks) wait_vmcnt<(NST - 2) * PER>();
         else wait_vmcnt<0>();
         __syncthreads();
         const int ks_load = ks + NST < nks ? ks + NST : nks - 1;
@@ -256,7 +199,6 @@ struct TilePipe {
           mfmas_with_loads(ac, bc, ks_load, stage);
         } else {
           issue(ks_load, stage);
-          if (PFD > 0) prefetch(min(ks_load + PFD, nks - 1));
           read_frags(next, 0, an, bn);
           __builtin_amdgcn_sched_barrier(0);
           mfmas_interleaved(ac, bc, true);
@@ -273,9 +215,7 @@ struct TilePipe {
       const u32x4* ac = (j & 1) ? af1 : af0;
       const u32x4* bc = (j & 1) ? bf1 : bf0;
       if (j < SUB - 1) read_frags(stage, j + 1, an, bn);
-#if !MOELORA_PIPE_INTERLEAVE
       __builtin_amdgcn_sched_barrier(0);
-#endif
       mfmas_interleaved(ac, bc, j < SUB - 1);
       __builtin_amdgcn_sched_barrier(0);
     }
