@@ -56,16 +56,21 @@ int check_device() {
 }
 
 // Where the align kernel keeps its lists and tables: LDS when they fit, else the workspace.
+// With both in LDS the tables overlay the lists' rank scratch (dead by the time the tables are
+// used), so only the expert lists, the adapters and the larger of the two take room.
 size_t align_lds_plan(int T, int k, int E, int nA, AlignArgs* a) {
   const size_t budget = (size_t)(kLdsBytes - kAlignStaticLds);
+  const size_t P = (size_t)T * k;
   const size_t tables = 2 * sizeof(int) * (size_t)E * (nA + 1);
   const size_t lists = sizeof(int) * align_list_ints(T, k, E);
+  const size_t scratch = lists - sizeof(int) * (P + (size_t)T);
+  const size_t both = sizeof(int) * (P + (size_t)T) + std::max(scratch, tables);
   a->tables_in_lds = 0;
   a->lists_in_lds = 0;
   size_t used = 0;
-  if (lists + tables <= budget) {
+  if (both <= budget) {
     a->tables_in_lds = a->lists_in_lds = 1;
-    used = lists + tables;
+    used = both;
   } else if (lists <= budget) {
     a->lists_in_lds = 1;
     used = lists;

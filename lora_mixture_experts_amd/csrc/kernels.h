@@ -5,6 +5,10 @@
 
 namespace moelora {
 
+constexpr int kAlignThreads = 1024;
+constexpr int kAlignStaticLds = 17 * 1024;  // >= the align kernel's static LDS (16.7 KB)
+constexpr int kLdsBytes = 160 * 1024;
+
 struct AlignArgs {
   const int* topk_ids;     // [T*k]
   const int* adapter_ids;  // [T]
@@ -27,9 +31,10 @@ struct AlignArgs {
   int lists_in_lds;
 };
 
-// ints of the align kernel's list scratch (staged ids, ranks, expert lists, adapters, counts)
+// ints of the align kernel's lists: expert lists [T*k] and adapters [T], then the rank scratch
+// (staged ids [T*k], ranks [T*k], per-wavefront counts [16][E])
 inline size_t align_list_ints(int T, int k, int E) {
-  return 3 * (size_t)T * k + (size_t)T + 16 * (size_t)E;
+  return 3 * (size_t)T * k + (size_t)T + (kAlignThreads / 64) * (size_t)E;
 }
 
 // LoRA shrink z = X A^T for the rows of the sorted layout.
@@ -108,9 +113,5 @@ hipError_t launch_tiled(const TiledConfig& c, bool gateup, const GemmArgs& a, hi
 hipError_t launch_combine(const float* D, int ksplit, int64_t split_stride, const int* pair_row,
                           const float* topk_w, int T, int k, int h, uint16_t* y,
                           hipStream_t stream);
-
-constexpr int kAlignThreads = 1024;
-constexpr int kAlignStaticLds = 17 * 1024;  // >= the align kernel's static LDS (16.7 KB)
-constexpr int kLdsBytes = 160 * 1024;
 
 }  // namespace moelora

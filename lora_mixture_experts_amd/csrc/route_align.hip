@@ -178,35 +178,45 @@ __global__ __launch_bounds__(1024) void align_kernel(AlignArgs a) {
   __shared__ int s_estart[kMaxExperts + 1];
   __shared__ int s_red[72];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwaves = blockDim.x >> 6;
-  const int bd = blockDim.x;
+  constexpr int nwaves = kAlignThreads / 64, bd = kAlignThreads;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.T, k = a.k, E = a.E, nA = a.nA, P = T * k;
   const int nb1 = nA + 1, nb = E * nb1;
   const int seg_pad = a.seg_pad, block_m = a.block_m;
+  // p / k as a multiply by ceil(2^32 / k) and a shift: exact for p * k < 2^32
+  const uint64_t k_magic = ((1ull << 32) + k - 1) / k;
+  auto token_of = [&](int p) { return (int)(((uint64_t)(uint32_t)p * k_magic) >> 32); };
+  auto pad_to = [&](int c) { return seg_pad == 1 ? c : round_up_i(c, seg_pad); };
 
-  // carve LDS (or the workspace): tables cnt/start [nb]; lists tk [P], rank [P], elist [P],
-  // ad [T], cnt_we [nwaves][E]
-  int* dyn = smem;
-  int* cnt;
-  int* start;
-  if (a.tables_in_lds) {
-    cnt = dyn;
-    start = dyn + nb;
-    dyn += 2 * nb;
-  } else {
-    cnt = a.g_cnt;
-    start = a.g_start;
+  // carve LDS (or the workspace): lists elist [P] and ad [T]; the rank scratch tk [P],
+  // rank [P], cnt_we [nwaves][E]; tables cnt/start [nb]. With everything in LDS the tables
+  // overlay the rank scratch, which is dead once the expert lists are built.
+  int *elist, *adl, *tk, *rank, *cnt_we, *cnt, *start;
+  {
+    int* dyn = smem;
+    if (a.tables_in_lds && a.lists_in_lds) {
+      elist = dyn;
+      adl = elist + P;
+      tk = adl + T;
+      cnt = tk;
+    } else {
+      if (a.tables_in_lds) {
+        cnt = dyn;
+        dyn += 2 * nb;
+      } else {
+        cnt = a.g_cnt;
+      }
+      elist = a.lists_in_lds ? dyn : a.g_lists;
+      adl = elist + P;
+      tk = adl + T;
+    }
+    rank = tk + P;
+    cnt_we = rank + P;
+    start = a.tables_in_lds ? cnt + nb : a.g_start;
   }
-  int* lists = a.lists_in_lds ? dyn : a.g_lists;
-  int* tk = lists;
-  int* rank = tk + P;
-  int* elist = rank + P;
-  int* adl = elist + P;
-  int* cnt_we = adl + T;
 
   // phase 0
   int fl_nonfinite = 0, fl_range = 0;
-  for (int i = tid; i < nb; i += bd) cnt[i] = 0;
   for (int i = tid; i < nwaves * E; i += bd) cnt_we[i] = 0;
   for (int i = tid; i < P; i += bd) tk[i] = a.topk_ids[i];
   for (int t = tid; t < T; t += bd) {
@@ -259,7 +269,13 @@ __global__ __launch_bounds__(1024) void align_kernel(AlignArgs a) {
     if (tid == 0) s_estart[E] = P;
   }
   __syncthreads();
-  for (int p = tid; p < P; p += bd) elist[cnt_we[(p / PP) * E + tk[p]] + rank[p]] = p;
+  {
+    const int p0 = wave * PP, p1 = min(P, p0 + PP);
+    for (int p = p0 + lane; p < p1; p += 64) elist[cnt_we[wave * E + tk[p]] + rank[p]] = p;
+  }
+  __syncthreads();
+  // (the rank scratch is dead from here on; the tables may overlay it)
+  for (int i = tid; i < nb; i += bd) cnt[i] = 0;
   __syncthreads();
 
   const int nbits = 32 - __clz(nA);  // bits of a key in [0, nA]
@@ -270,7 +286,7 @@ __global__ __launch_bounds__(1024) void align_kernel(AlignArgs a) {
     for (int base = s_estart[e]; base < i1; base += 64) {
       const int i = base + lane;
       const bool valid = i < i1;
-      const int key = valid ? adl[elist[i] / k] + 1 : 0;
+      const int key = valid ? adl[token_of(elist[i])] + 1 : 0;
       const uint64_t eq = match_key(valid, key, nbits);
       if (valid && (eq & lanemask_lt()) == 0ull) atomicAdd(&cnt[e * nb1 + key], (int)__popcll(eq));
     }
@@ -283,7 +299,7 @@ __global__ __launch_bounds__(1024) void align_kernel(AlignArgs a) {
   int sv = 0, sn = 0;
   for (int b = lo; b < hi; ++b) {
     const int c = cnt[b];
-    sv += round_up_i(c, seg_pad);
+    sv += pad_to(c);
     sn += c > 0;
   }
   int ev, en, totv, totn;
@@ -292,7 +308,7 @@ __global__ __launch_bounds__(1024) void align_kernel(AlignArgs a) {
     int run = ev;
     for (int b = lo; b < hi; ++b) {
       start[b] = run;
-      run += round_up_i(cnt[b], seg_pad);
+      run += pad_to(cnt[b]);
     }
   }
   __syncthreads();
@@ -372,7 +388,7 @@ __global__ __launch_bounds__(1024) void align_kernel(AlignArgs a) {
       const int i = base + lane;
       const bool valid = i < i1;
       const int p = valid ? elist[i] : 0;
-      const int key = valid ? adl[p / k] + 1 : 0;
+      const int key = valid ? adl[token_of(p)] + 1 : 0;
       const uint64_t eq = match_key(valid, key, nbits);
       int cur = 0;
       if (valid && (eq & lanemask_lt()) == 0ull) cur = atomicAdd(&cnt[e * nb1 + key], (int)__popcll(eq));
