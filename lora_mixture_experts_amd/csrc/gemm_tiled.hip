@@ -11,8 +11,7 @@
 //
 // C[m][n] = sum_k X[m][k] W[n][k] for the BM token rows of one row block of the sorted layout
 // (all of one expert) and BN output features. The main loop (TilePipe) loads both operand
-// tiles straight from HBM into a ring of LDS stages and runs 32x32x16 bf16 MFMAs on them (the
-// 16x16x32 form runs at half their rate on CDNA4).
+// tiles straight from HBM into a ring of LDS stages and runs 32x32x16 bf16 MFMAs on them.
 //
 // gate_up: the weight rows of each wave's column range are [gate i .. | up i ..] for the same
 // intermediate columns i, so each lane holds gate and up of the same act element and
