@@ -363,7 +363,23 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   // Split the shrink's K by the tiles that can hold pairs (at most P/16 plus one partial tile per
   // expert), not by the padded grid: padding tiles exit at once.
   const int64_t live_tiles = std::min<int64_t>(tiles16, (P + 15) / 16 + E);
-  const int s1 = pick_splits(live_tiles, h), s2 = pick_splits(live_tiles, I);
+  int s1 = pick_splits(live_tiles, h), s2 = pick_splits(live_tiles, I);
+  // On the tiled path (row blocks of >= 64 rows) the shrink takes 64 rows per workgroup where a
+  // sub-block holds few adapter runs, so that a run's A slab is fetched once per 64 rows; the
+  // 16-row shrink then takes the rest. Both use the same K splits, as many as either needs to
+  // fill the chip (MOELORA_SHRINK64=0 turns the 64-row shrink off, for experiments).
+  static int shrink64_env = -1;
+  if (shrink64_env < 0) {
+    const char* env = getenv("MOELORA_SHRINK64");
+    shrink64_env = env ? atoi(env) : 1;
+  }
+  const bool shrink64 = shrink64_env != 0 && path.tiled && r <= 64 && bm % 64 == 0;
+  const int n_sub_max = max_blocks * bm / 64;
+  if (shrink64) {
+    const int64_t live_sub = std::min<int64_t>(n_sub_max, (P + 63) / 64 + E);
+    s1 = std::max(s1, pick_splits(live_sub, h));
+    s2 = std::max(s2, pick_splits(live_sub, I));
+  }
   const size_t lds = align_lds_plan(T, topk, E, nA, &al);
   if (launch_align(al, lds, stream) != hipSuccess) return MOELORA_EHIP;
   if (!mark(ev, 2, stream)) return MOELORA_EHIP;
@@ -380,6 +396,9 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   sh.E = E;
   sh.r = r;
   sh.xcd_ranges = path.tiled ? 1 : 0;
+  sh.block_seg = block_seg;
+  sh.seg_table = al.seg_table;
+  sh.n_seg = al.n_seg;
 
   GemmArgs g;
   g.cap = L.cap;
@@ -406,6 +425,9 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   sh.S = s1;
   sh.zpart = z1;
   sh.cap = L.cap;
+  sh.after64 = shrink64 ? 1 : 0;
+  if (shrink64 && launch_shrink_tiled(true, sh, n_sub_max, stream) != hipSuccess)
+    return MOELORA_EHIP;
   if (launch_shrink(true, sh, tiles16, stream) != hipSuccess) return MOELORA_EHIP;
   uint16_t* zhl = (uint16_t*)(ws + L.zhl);
   if (path.tiled && launch_zfinal(z1, s1, L.cap, r, n_blocks, bm, (int64_t)max_blocks * bm, zhl,
@@ -452,13 +474,15 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   if (gu_err != hipSuccess) return MOELORA_EHIP;
   if (!mark(ev, 4, stream)) return MOELORA_EHIP;
 
-  // down: shrink z2 = act A2, then W2 GEMM + z2 B2 -> D (fp32, pair order)
+  // down: shrink z2 = act A2, then W2 GEMM + z2 B2 -> D (fp32, sorted rows)
   sh.X = act;
   sh.x_bytes = (uint32_t)((size_t)L.cap * I * 2);
   sh.Aw = (const uint16_t*)A2;
   sh.K = I;
   sh.S = s2;
   sh.zpart = z2;
+  if (shrink64 && launch_shrink_tiled(false, sh, n_sub_max, stream) != hipSuccess)
+    return MOELORA_EHIP;
   if (launch_shrink(false, sh, tiles16, stream) != hipSuccess) return MOELORA_EHIP;
   if (path.tiled && launch_zfinal(z2, s2, L.cap, r, n_blocks, bm, (int64_t)max_blocks * bm, zhl,
                                   stream) != hipSuccess)

@@ -43,6 +43,9 @@ struct ShrinkArgs {
   uint32_t x_bytes;   // size of X (< 2 GiB)
   const int* sorted_pairs;
   const int* block_expert;
+  const int* block_seg;  // (64-row shrink) first segment of each row block, or -1
+  const int* seg_table;  // (64-row shrink) [n_seg][4]
+  const int* n_seg;
   const int* n_blocks;
   int bm;
   const int* adapter_ids;
@@ -52,6 +55,7 @@ struct ShrinkArgs {
   float* zpart;        // [S][cap][r]; written for the rows that carry an adapter
   int64_t cap;
   int xcd_ranges;      // 1: each XCD takes a contiguous range of the work order (long runs)
+  int after64;         // 16-row shrink: only the sub-blocks the 64-row shrink leaves
 };
 
 // Base GEMM of one projection for the rows of the sorted layout, with the LoRA expand (and
@@ -105,6 +109,8 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int* topk_ids,
                         int* tok_flags, hipStream_t stream);
 hipError_t launch_align(const AlignArgs& a, size_t dyn_lds, hipStream_t stream);
 hipError_t launch_shrink(bool gather, const ShrinkArgs& a, int tiles, hipStream_t stream);
+hipError_t launch_shrink_tiled(bool gather, const ShrinkArgs& a, int n_sub_max,
+                               hipStream_t stream);
 hipError_t launch_zfinal(const float* zpart, int S, int64_t cap, int r, const int* n_blocks,
                          int bm, int64_t max_rows, uint16_t* zhl, hipStream_t stream);
 hipError_t launch_skinny(const SkinnyConfig& c, bool gateup, const GemmArgs& a, int grid_y,

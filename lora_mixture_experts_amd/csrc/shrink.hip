@@ -19,6 +19,7 @@
 // zpart[s]; consumers add the S parts in order, so the result does not depend on scheduling.
 #include "common.h"
 #include "kernels.h"
+#include "segments.h"
 
 namespace moelora {
 
@@ -44,6 +45,10 @@ __global__ __launch_bounds__(256) void lora_shrink_kernel(ShrinkArgs a) {
   const int s = item / live16;
   const int row0 = (item - s * live16) * 16;
   const int e = a.block_expert[row0 / a.bm];
+  // with the 64-row shrink, only the tiles of sub-blocks it leaves (many short runs)
+  if (a.after64 && count_runs64(a.block_seg, a.seg_table, *a.n_seg, a.nA, row0 / a.bm,
+                                row0 & ~63, kShrink64MaxRuns) <= kShrink64MaxRuns)
+    return;
 
   // adapter runs of the tile: run_lo[i]..run_hi[i] share adapter run_ad[i]
   __shared__ int s_pair[16], s_ad[16], s_nrun, s_lo[16], s_hi[16], s_rad[16];
