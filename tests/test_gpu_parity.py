@@ -157,6 +157,19 @@ def test_forward_all_adapters_off_and_on():
     assert np.abs(y_off.double().cpu().numpy() - ref_on).max() > 0.1 * np.abs(ref_on).max()
 
 
+def test_forward_tiled_mixed_run_lengths():
+    """Long adapter runs (64-row shrink) next to one adapter per token (16-row shrink) in the
+    same batch, on 256-row tiles: every sub-block is taken by exactly one of the two shrinks."""
+    w = Workload("tiled256_mixed", 2048, 256, 384, 4, 2, 40, 32, adapters="zipf_runs", run=128)
+    _say("forward tiled256_mixed")
+    inp = _small_inputs(w, 3, 10.0, no_adapter_every=0)
+    g = torch.Generator().manual_seed(3)
+    inp["adapter_ids"][w.T // 2:] = torch.randint(-1, w.n_adapters, (w.T - w.T // 2,), generator=g,
+                                                  dtype=torch.int32)
+    y = _run(inp, w.topk)
+    check_close(y, oracle_rows(inp, w.topk), what="tiled256_mixed")
+
+
 def test_forward_empty_batch():
     w = SMALL["tiny"].with_(T=0)
     inp = configs.make_inputs(w, 0)
