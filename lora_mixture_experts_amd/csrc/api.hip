@@ -243,6 +243,7 @@ bool moelora_make_layout(int T, int h, int I, int E, int nA, int r, int topk, Mo
   L->n_seg = take(4);
   L->z1 = take(4 * (size_t)kMaxSplit * L->cap * r);
   L->z2 = take(4 * (size_t)kMaxSplit * L->cap * r);
+  L->zsum = take(4 * (size_t)L->cap * r);
   L->zhl = take(2 * 2 * (size_t)L->cap * r);
   L->act = take(2 * (size_t)L->cap * I);
   L->dpair = take(4 * (size_t)kMaxDownSplit * L->cap * h);
@@ -429,17 +430,17 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   if (shrink64 && launch_shrink_tiled(true, sh, n_sub_max, stream) != hipSuccess)
     return MOELORA_EHIP;
   if (launch_shrink(true, sh, tiles16, stream) != hipSuccess) return MOELORA_EHIP;
-  uint16_t* zhl = (uint16_t*)(ws + L.zhl);
-  if (path.tiled && launch_zfinal(z1, s1, L.cap, r, n_blocks, bm, (int64_t)max_blocks * bm, zhl,
-                                  stream) != hipSuccess)
+  float* zsum = (float*)(ws + L.zsum);
+  uint16_t* zhl = path.tiled ? (uint16_t*)(ws + L.zhl) : nullptr;
+  if (launch_zfinal(z1, s1, L.cap, r, n_blocks, bm, (int64_t)max_blocks * bm, zsum, zhl, stream) !=
+      hipSuccess)
     return MOELORA_EHIP;
   if (!mark(ev, 3, stream)) return MOELORA_EHIP;
   g.X = (const uint16_t*)x;
   g.x_bytes = (uint32_t)((size_t)T * h * 2);
   g.W = (const uint16_t*)W1;
   g.Bw = (const uint16_t*)B1;
-  g.zpart = z1;
-  g.S = s1;
+  g.zsum = zsum;
   g.zhl = zhl;
   g.K = h;
   g.N = I;
@@ -484,16 +485,14 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   if (shrink64 && launch_shrink_tiled(false, sh, n_sub_max, stream) != hipSuccess)
     return MOELORA_EHIP;
   if (launch_shrink(false, sh, tiles16, stream) != hipSuccess) return MOELORA_EHIP;
-  if (path.tiled && launch_zfinal(z2, s2, L.cap, r, n_blocks, bm, (int64_t)max_blocks * bm, zhl,
-                                  stream) != hipSuccess)
+  if (launch_zfinal(z2, s2, L.cap, r, n_blocks, bm, (int64_t)max_blocks * bm, zsum, zhl, stream) !=
+      hipSuccess)
     return MOELORA_EHIP;
   if (!mark(ev, 5, stream)) return MOELORA_EHIP;
   g.X = act;
   g.x_bytes = (uint32_t)((size_t)L.cap * I * 2);
   g.W = (const uint16_t*)W2;
   g.Bw = (const uint16_t*)B2;
-  g.zpart = z2;
-  g.S = s2;
   g.K = I;
   g.N = h;
   g.ksplit = plan.ksplit;

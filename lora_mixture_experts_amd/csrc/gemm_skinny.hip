@@ -121,21 +121,17 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs a) {
   const int zsplit = blockIdx.z;
   constexpr int BMZ = 16 * NT;
 
-  // The LoRA shrink leaves z as S split-K parts; the block's z rows are added up once, in split
-  // order, into LDS for the epilogue (rows without an adapter hold values nobody reads). Only
-  // K split 0 of down adds the LoRA term. Run after the first weight loads are issued, so the
-  // two latencies overlap. (The grid covers N exactly: every wavefront has columns.)
+  // The block's z rows (the shrink's split parts already added) go into LDS for the epilogue
+  // (rows without an adapter hold values nobody reads). Only K split 0 of down adds the LoRA
+  // term. Run after the first weight loads are issued, so the two latencies overlap. (The grid
+  // covers N exactly: every wavefront has columns.)
   __shared__ __attribute__((aligned(16))) float s_z[BMZ * 64];
   auto z_prologue = [&]() {
     if (zsplit != 0) return;
     const int nz = BMZ * a.r;
-    const float* zp = a.zpart + (size_t)blk * BMZ * a.r;
-    const size_t zstride = (size_t)a.cap * a.r;
-    for (int i = threadIdx.x; i < nz; i += 256) {
-      float z = 0.f;
-      for (int sp = 0; sp < a.S; ++sp) z += zp[sp * zstride + i];
-      s_z[i] = z;
-    }
+    const float* zp = a.zsum + (size_t)blk * BMZ * a.r;
+    for (int i = threadIdx.x * 4; i < nz; i += 256 * 4)
+      *reinterpret_cast<f32x4*>(s_z + i) = *reinterpret_cast<const f32x4*>(zp + i);
     __syncthreads();
   };
   const int e = a.block_expert[blk];

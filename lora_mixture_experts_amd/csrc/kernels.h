@@ -65,9 +65,8 @@ struct GemmArgs {
   uint32_t x_bytes;    // size of X (< 2 GiB)
   const uint16_t* W;   // gate_up: W1 [E][2I][h]; down: W2 [E][h][I]
   const uint16_t* Bw;  // gate_up: B1 [nA][E][2I][r]; down: B2 [nA][E][h][r]
-  const float* zpart;  // [S][cap][r] LoRA shrink output, as S split-K parts (skinny)
-  int S;
-  const uint16_t* zhl;  // [2][cap][r] the parts' sum as bf16 high and low planes (tiled)
+  const float* zsum;    // skinny: [cap][r] LoRA shrink output (its split parts added)
+  const uint16_t* zhl;  // tiled: [2][cap][r] the same as bf16 high and low planes
   int64_t cap;
   const int* sorted_pairs;
   const int* block_expert;
@@ -112,7 +111,8 @@ hipError_t launch_shrink(bool gather, const ShrinkArgs& a, int tiles, hipStream_
 hipError_t launch_shrink_tiled(bool gather, const ShrinkArgs& a, int n_sub_max,
                                hipStream_t stream);
 hipError_t launch_zfinal(const float* zpart, int S, int64_t cap, int r, const int* n_blocks,
-                         int bm, int64_t max_rows, uint16_t* zhl, hipStream_t stream);
+                         int bm, int64_t max_rows, float* zsum, uint16_t* zhl,
+                         hipStream_t stream);
 hipError_t launch_skinny(const SkinnyConfig& c, bool gateup, const GemmArgs& a, int grid_y,
                          hipStream_t stream);
 hipError_t launch_tiled(const TiledConfig& c, bool gateup, const GemmArgs& a, hipStream_t stream);

@@ -194,35 +194,40 @@ __global__ __launch_bounds__(256) void lora_shrink_kernel(ShrinkArgs a) {
   }
 }
 
-// z for the LDS-tiled GEMMs: the S split parts of each row added in split order (as the skinny
-// GEMMs add them), then split into bf16 high and low parts (hi = bf16(z), lo = bf16(z - hi)),
-// written as two planes [cap][r]: the tiled epilogue then loads each z row once, with no sum.
-// One thread per 8 consecutive values of a row; rows past the live row blocks are skipped.
+// z for the GEMM epilogues: the S split parts of each row added in split order, once, into
+// zsum [cap][r] (fp32, read by the skinny GEMMs), so that every workgroup reading a row's z
+// loads it once instead of S times. For the LDS-tiled GEMMs (zhl != nullptr) the sum is also
+// split into bf16 high and low parts (hi = bf16(z), lo = bf16(z - hi)), written as two planes
+// [cap][r], which their epilogue loads straight into MFMA operands. One thread per 8
+// consecutive values of a row; rows past the live row blocks are skipped.
 __global__ __launch_bounds__(256) void zfinal_kernel(const float* __restrict__ zpart, int S,
                                                      int64_t cap, int r,
                                                      const int* __restrict__ n_blocks, int bm,
+                                                     float* __restrict__ zsum,
                                                      uint16_t* __restrict__ zhl) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int per_row = r / 8;
   const int64_t row = idx / per_row;
   if (row >= (int64_t)*n_blocks * bm) return;
   const int q = (int)(idx - row * per_row) * 8;
-  float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int sp = 0; sp < S; ++sp) {
+  f32x4 z0 = *reinterpret_cast<const f32x4*>(zpart + row * r + q);
+  f32x4 z1 = *reinterpret_cast<const f32x4*>(zpart + row * r + q + 4);
+  for (int sp = 1; sp < S; ++sp) {
     const float* src = zpart + (sp * cap + row) * r + q;
-    const f32x4 a = *reinterpret_cast<const f32x4*>(src);
-    const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      z[t] += a[t];
-      z[4 + t] += b[t];
-    }
+    z0 += *reinterpret_cast<const f32x4*>(src);
+    z1 += *reinterpret_cast<const f32x4*>(src + 4);
+  }
+  if (zhl == nullptr) {
+    *reinterpret_cast<f32x4*>(zsum + row * r + q) = z0;
+    *reinterpret_cast<f32x4*>(zsum + row * r + q + 4) = z1;
+    return;
   }
   uint32_t hb[8], lb[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
-    hb[t] = f32_to_bf16_bits(z[t]);
-    lb[t] = f32_to_bf16_bits(z[t] - __uint_as_float(hb[t] << 16));
+    const float z = t < 4 ? z0[t] : z1[t - 4];
+    hb[t] = f32_to_bf16_bits(z);
+    lb[t] = f32_to_bf16_bits(z - __uint_as_float(hb[t] << 16));
   }
   *reinterpret_cast<u32x4*>(zhl + row * r + q) =
       u32x4{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16), hb[6] | (hb[7] << 16)};
@@ -231,12 +236,13 @@ __global__ __launch_bounds__(256) void zfinal_kernel(const float* __restrict__ z
 }
 
 hipError_t launch_zfinal(const float* zpart, int S, int64_t cap, int r, const int* n_blocks,
-                         int bm, int64_t max_rows, uint16_t* zhl, hipStream_t stream) {
+                         int bm, int64_t max_rows, float* zsum, uint16_t* zhl,
+                         hipStream_t stream) {
   if (r % 8 != 0) return hipErrorInvalidValue;
   const int64_t n = max_rows * (r / 8);
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(zfinal_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, zpart,
-                     S, cap, r, n_blocks, bm, zhl);
+                     S, cap, r, n_blocks, bm, zsum, zhl);
   return hipGetLastError();
 }
 
