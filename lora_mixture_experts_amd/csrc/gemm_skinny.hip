@@ -157,11 +157,16 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs a) {
   // loads zeros without touching memory. Every load stays unconditional, which keeps the
   // compiler's count of outstanding loads exact, so the prefetch below overlaps the MFMAs.
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.X, a.x_bytes);
+  // (the pair and adapter of each token row are fetched here, for the epilogue: their latency
+  // hides behind the main loop)
   uint32_t xo[NT];
+  int pair[NT], adap[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int row = blk * BM + nt * 16 + m;
     const int p = a.sorted_pairs[row];
+    pair[nt] = p;
+    adap[nt] = p >= 0 ? sanitize_adapter(a.adapter_ids[p / a.k], a.nA) : -1;
     xo[nt] = p < 0 ? kOutOfRange : (uint32_t)((GATEUP ? (size_t)(p / a.k) : (size_t)row) * K * 2);
   }
 
@@ -232,9 +237,8 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs a) {
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int row = blk * BM + nt * 16 + m;
-    const int p = a.sorted_pairs[row];
-    if (p < 0) continue;
-    const int ad = sanitize_adapter(a.adapter_ids[p / a.k], a.nA);
+    if (pair[nt] < 0) continue;
+    const int ad = adap[nt];
     const float* zrow = s_z + (nt * 16 + m) * a.r;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
