@@ -158,8 +158,8 @@ PathPlan pick_path(int64_t P, int E, int h, int I) {
 }
 
 bool skinny_instantiated(const SkinnyConfig& c, bool gateup) {
-  static const int have[][5] = {{1, 4, 1, 1, 0}, {1, 4, 1, 0, 0}, {1, 4, 2, 1, 0}, {1, 4, 2, 0, 0},
-                                {1, 8, 1, 1, 0}, {1, 8, 1, 0, 0}, {2, 4, 1, 1, 0}, {2, 4, 2, 1, 0},
+  static const int have[][5] = {{1, 2, 1, 1, 0}, {1, 2, 2, 1, 0}, {1, 4, 1, 1, 0}, {1, 4, 1, 0, 0}, {1, 4, 2, 1, 0}, {1, 4, 2, 0, 0},
+                                {1, 8, 1, 1, 0}, {1, 8, 1, 0, 0}, {2, 2, 1, 1, 0}, {2, 2, 2, 1, 0}, {2, 4, 1, 1, 0}, {2, 4, 2, 1, 0},
                                 {2, 8, 1, 1, 0},
                                 {4, 4, 1, 1, 0}, {1, 4, 1, 1, 1}, {1, 4, 1, 0, 1}, {1, 8, 1, 1, 1},
                                 {1, 8, 1, 0, 1}};
@@ -181,9 +181,12 @@ SkinnyPlan pick_skinny(int nt, int h, int I) {
   SkinnyPlan pl;
   // measured on decode (16 experts, ~8 rows each) and FG (128 experts, 16 rows each): gate_up
   // keeps gate and up rows in one wavefront; down streams two row tiles per wavefront (and on
-  // 16-row blocks splits K in two)
-  pl.gu = SkinnyConfig{nt, 4, 1, 1, 0};
-  pl.dn = SkinnyConfig{nt, 4, nt <= 2 ? 2 : 1, 1, 0};
+  // 16-row blocks splits K in two). 64-wide K steps (two 16-byte loads per lane and row) leave
+  // registers for more workgroups per CU than 128-wide ones; on 32-row blocks (short K loops,
+  // many experts) gate_up also streams two row tiles per wavefront.
+  pl.gu = nt == 1 ? SkinnyConfig{nt, 2, 1, 1, 0}
+                  : (nt == 2 ? SkinnyConfig{nt, 2, 2, 1, 0} : SkinnyConfig{nt, 4, 1, 1, 0});
+  pl.dn = SkinnyConfig{nt, nt <= 2 ? 2 : 4, nt <= 2 ? 2 : 1, 1, 0};
   pl.ksplit = nt == 1 ? 2 : 1;
   static int ov[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   static bool parsed = false;

@@ -303,12 +303,16 @@ hipError_t launch_skinny(const SkinnyConfig& c, bool gateup, const GemmArgs& a, 
                        stream, a);                                                                \
     return hipGetLastError();                                                                     \
   }
+  MOELORA_SKINNY(1, 2, 1, true)
+  MOELORA_SKINNY(1, 2, 2, true)
   MOELORA_SKINNY(1, 4, 1, true)
   MOELORA_SKINNY(1, 4, 1, false)
   MOELORA_SKINNY(1, 4, 2, true)
   MOELORA_SKINNY(1, 4, 2, false)
   MOELORA_SKINNY(1, 8, 1, true)
   MOELORA_SKINNY(1, 8, 1, false)
+  MOELORA_SKINNY(2, 2, 1, true)
+  MOELORA_SKINNY(2, 2, 2, true)
   MOELORA_SKINNY(2, 4, 1, true)
   MOELORA_SKINNY(2, 4, 2, true)
   MOELORA_SKINNY(2, 8, 1, true)

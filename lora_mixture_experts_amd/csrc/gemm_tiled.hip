@@ -356,12 +356,8 @@ hipError_t launch_tiled(const TiledConfig& c, bool gateup, const GemmArgs& a, hi
         ? launch_tiled_t<true, BM_, BN_, WM_, WN_, BK_, NST_, NW_>(a, n_tiles_n, total, stream) \
         : launch_tiled_t<false, BM_, BN_, WM_, WN_, BK_, NST_, NW_>(a, n_tiles_n, total, stream);
   MOELORA_TILED(64, 128, 32, 64, 64, 2, 4)
-  MOELORA_TILED(128, 128, 64, 64, 64, 2, 4)
-  MOELORA_TILED(256, 256, 128, 128, 64, 2, 4)
   MOELORA_TILED(128, 128, 32, 64, 64, 2, 8)
   MOELORA_TILED(256, 256, 64, 128, 64, 2, 8)
-  MOELORA_TILED(256, 256, 128, 64, 64, 2, 8)
-  MOELORA_TILED(256, 256, 64, 128, 32, 5, 8)
   MOELORA_TILED(64, 256, 32, 64, 64, 2, 8)
 #undef MOELORA_TILED
   return hipErrorInvalidValue;
