@@ -96,6 +96,87 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
   }
 }
 
+// Route for up to 256 experts: the rank of each logit, the number of logits that beat it
+// (larger, or equal with a lower expert id), is its slot when it is below k, which is the same
+// selection as k rounds of arg-max. The wavefront stages the token's logits in LDS and every lane
+// counts, for its (up to VPL) logits, how many of the E staged ones beat it: broadcast reads, no
+// cross-lane reductions. Non-finite logits are flagged and take part as -infinity.
+template <int VPL>
+__global__ __launch_bounds__(256) void route_rank_kernel(const float* __restrict__ logits, int T,
+                                                         int E, int k, int* __restrict__ topk_ids,
+                                                         float* __restrict__ topk_w,
+                                                         int* __restrict__ tok_flags) {
+  __shared__ __attribute__((aligned(16))) float s_l[4][64 * VPL];
+  __shared__ float s_sel[4][kMaxTopk];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + w;
+  const bool active = t < T;  // (no early exit: every wavefront reaches the barriers)
+  const float* row = logits + (size_t)(active ? t : 0) * E;
+  float v[VPL];
+  bool bad = false;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int e = lane + 64 * i;
+    float f = -INFINITY;
+    if (active && e < E) {
+      f = row[e];
+      if (!__builtin_isfinite(f)) {
+        bad = true;
+        f = -INFINITY;
+      }
+    }
+    v[i] = f;
+    s_l[w][e] = f;  // (slots past E hold -infinity and are never counted)
+  }
+  __syncthreads();
+  int rank[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) rank[i] = 0;
+  const int e4 = (E + 3) & ~3;
+  for (int c = 0; c < e4; c += 4) {
+    const f32x4 o = *reinterpret_cast<const f32x4*>(&s_l[w][c]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int eo = c + j;
+      if (eo >= E) break;
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        const int e = lane + 64 * i;
+        rank[i] += (o[j] > v[i] || (o[j] == v[i] && eo < e)) ? 1 : 0;
+      }
+    }
+  }
+  const uint64_t anybad = __ballot(bad);
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int e = lane + 64 * i;
+    if (active && e < E && rank[i] < k) {
+      topk_ids[(size_t)t * k + rank[i]] = e;
+      s_sel[w][rank[i]] = v[i];
+    }
+  }
+  __syncthreads();
+  if (active && lane == 0) {
+    const float top = s_sel[w][0];
+    float ex[kMaxTopk];
+    float den = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxTopk; ++j) {
+      ex[j] = 0.f;
+      if (j >= k) continue;
+      ex[j] = (top == -INFINITY) ? 1.f : __expf(s_sel[w][j] - top);
+      den += ex[j];
+    }
+    const float inv = 1.f / den;
+#pragma unroll
+    for (int j = 0; j < kMaxTopk; ++j) {
+      if (j >= k) continue;
+      topk_w[(size_t)t * k + j] = ex[j] * inv;
+    }
+    tok_flags[t] = anybad ? 1 : 0;
+  }
+}
+
 // ------------------------------------------------------------------------------------------
 // Align: one workgroup of 1024 threads.
 //   phase 0  validate adapter ids (out of range -> flag, treated as -1), collect flags, stage
@@ -410,8 +491,19 @@ namespace moelora {
 hipError_t launch_route(const float* logits, int T, int E, int k, int* topk_ids, float* topk_w,
                         int* tok_flags, hipStream_t stream) {
   if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(route_topk_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, logits, T, E, k,
-                     topk_ids, topk_w, tok_flags);
+  const dim3 grid((T + 3) / 4), block(256);
+  if (E <= 64)
+    hipLaunchKernelGGL(route_rank_kernel<1>, grid, block, 0, stream, logits, T, E, k, topk_ids,
+                       topk_w, tok_flags);
+  else if (E <= 128)
+    hipLaunchKernelGGL(route_rank_kernel<2>, grid, block, 0, stream, logits, T, E, k, topk_ids,
+                       topk_w, tok_flags);
+  else if (E <= 256)
+    hipLaunchKernelGGL(route_rank_kernel<4>, grid, block, 0, stream, logits, T, E, k, topk_ids,
+                       topk_w, tok_flags);
+  else
+    hipLaunchKernelGGL(route_topk_kernel, grid, block, 0, stream, logits, T, E, k, topk_ids,
+                       topk_w, tok_flags);
   return hipGetLastError();
 }
 

@@ -63,7 +63,9 @@ def test_route_align_bit_exact(name, seg_pad, block_m):
     _route_align_case(w, configs.make_logits(w, 0), configs.make_adapter_ids(w, 0), seg_pad, block_m)
 
 
-@pytest.mark.parametrize("E,k,levels", [(8, 2, 2), (128, 8, 3), (16, 16, 1), (1, 1, 1)])
+# E up to 256 takes the rank-count routing kernel, larger E the arg-max rounds
+@pytest.mark.parametrize("E,k,levels", [(8, 2, 2), (128, 8, 3), (16, 16, 1), (1, 1, 1), (200, 5, 2),
+                                        (256, 16, 3), (300, 6, 2), (1000, 3, 4)])
 def test_route_align_ties_and_no_adapter(E, k, levels):
     w = Workload("ties", 300, 128, 128, E, k, 7, 8)
     rng = np.random.default_rng(E + k)
