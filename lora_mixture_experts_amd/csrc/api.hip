@@ -217,7 +217,11 @@ int pick_splits(int64_t tiles, int K) {
   int s = (int)((1024 + tiles - 1) / (tiles > 0 ? tiles : 1));
   s = s < 1 ? 1 : (s > kMaxSplit ? kMaxSplit : s);
   const int nks = K / 128;
-  return s > nks ? nks : s;
+  s = s > nks ? nks : s;
+  // the kernels give split j the 128-wide steps [j * per, (j + 1) * per), per = ceil(nks / s);
+  // fewer splits with the same per leave none of them empty
+  const int per = (nks + s - 1) / s;
+  return (nks + per - 1) / per;
 }
 
 }  // namespace
