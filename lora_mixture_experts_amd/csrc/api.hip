@@ -55,30 +55,19 @@ int check_device() {
   return known[dev] == 1 ? MOELORA_OK : MOELORA_EDEVICE;
 }
 
-// Where the align kernel keeps its lists and tables: LDS when they fit, else the workspace.
-// With both in LDS the tables overlay the lists' rank scratch (dead by the time the tables are
-// used), so only the expert lists, the adapters and the larger of the two take room.
+// Align kernel's LDS: its arrays (keys, two pair-id buffers, segment starts and deltas, with the
+// radix digit counts overlaying the segment region) when they fit, else the digit counts only
+// and the arrays go to the workspace. Returns the dynamic LDS bytes and fills the kernel's sizes.
 size_t align_lds_plan(int T, int k, int E, int nA, AlignArgs* a) {
   const size_t budget = (size_t)(kLdsBytes - kAlignStaticLds);
+  align_digits(E, nA, &a->digit_bits, &a->passes);
+  a->seg_cap = align_seg_cap(T, k, E, nA);
   const size_t P = (size_t)T * k;
-  const size_t tables = 2 * sizeof(int) * (size_t)E * (nA + 1);
-  const size_t lists = sizeof(int) * align_list_ints(T, k, E);
-  const size_t scratch = lists - sizeof(int) * (P + (size_t)T);
-  const size_t both = sizeof(int) * (P + (size_t)T) + std::max(scratch, tables);
-  a->tables_in_lds = 0;
-  a->lists_in_lds = 0;
-  size_t used = 0;
-  if (both <= budget) {
-    a->tables_in_lds = a->lists_in_lds = 1;
-    used = both;
-  } else if (lists <= budget) {
-    a->lists_in_lds = 1;
-    used = lists;
-  } else if (tables <= budget) {
-    a->tables_in_lds = 1;
-    used = tables;
-  }
-  return used;
+  const size_t counts = (size_t)(kAlignThreads / 64) << a->digit_bits;
+  const size_t seg_region = std::max(2 * (size_t)a->seg_cap, counts);
+  const size_t in_lds = sizeof(int) * (3 * P + seg_region);
+  a->lists_in_lds = in_lds <= budget ? 1 : 0;
+  return a->lists_in_lds ? in_lds : sizeof(int) * counts;
 }
 
 // GEMM path from the mean rows per expert (known on the host; per-expert counts are not):
@@ -254,9 +243,7 @@ bool moelora_make_layout(int T, int h, int I, int E, int nA, int r, int topk, Mo
   L->zhl = take(2 * 2 * (size_t)L->cap * r);
   L->act = take(2 * (size_t)L->cap * I);
   L->dpair = take(4 * (size_t)kMaxDownSplit * L->cap * h);
-  L->align_cnt = take(4 * (size_t)E * (nA + 1));
-  L->align_start = take(4 * (size_t)E * (nA + 1));
-  L->align_lists = take(4 * align_list_ints(T, topk, E));
+  L->align_lists = take(4 * align_list_ints(T, topk, E, nA));
   L->total = off;
   return true;
 }
@@ -362,8 +349,6 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   al.block_seg = block_seg;
   al.pair_row = pair_row;
   al.n_blocks = n_blocks;
-  al.g_cnt = (int*)(ws + L.align_cnt);
-  al.g_start = (int*)(ws + L.align_start);
   al.g_lists = (int*)(ws + L.align_lists);
   const int64_t max_rows = P + (int64_t)E * (bm - 1);
   const int max_blocks = (int)((max_rows + bm - 1) / bm);
@@ -588,8 +573,6 @@ int moe_lora_route_align(const float* router_logits, const int32_t* adapter_ids,
   al.block_seg = nullptr;
   al.pair_row = nullptr;
   al.n_blocks = nullptr;
-  al.g_cnt = (int*)(ws + L.align_cnt);
-  al.g_start = (int*)(ws + L.align_start);
   al.g_lists = (int*)(ws + L.align_lists);
   const size_t lds = align_lds_plan(d->T, topk, d->n_experts, d->n_adapters, &al);
   if (launch_align(al, lds, stream) != hipSuccess) return MOELORA_EHIP;

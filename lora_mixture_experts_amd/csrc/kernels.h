@@ -24,17 +24,33 @@ struct AlignArgs {
                         // (a block of padding rows); written when block_expert is
   int* pair_row;        // [T*k]: sorted row of each pair, or nullptr
   int* n_blocks;        // [1] or nullptr
-  int* g_cnt;           // [E*(nA+1)] global scratch when the tables do not fit in LDS
-  int* g_start;         // [E*(nA+1)]
-  int* g_lists;         // [3*T*k + T + 16*E] global scratch when the lists do not fit in LDS
-  int tables_in_lds;
+  int* g_lists;         // workspace for the arrays when they do not fit in LDS
   int lists_in_lds;
+  int digit_bits;  // radix digit width D (1..10)
+  int passes;      // digits of the bucket key (passes * D >= its bit width)
+  int seg_cap;     // min(T*k, E*(nA+1)) + 1: room for the segment starts (and deltas)
 };
 
-// ints of the align kernel's lists: expert lists [T*k] and adapters [T], then the rank scratch
-// (staged ids [T*k], ranks [T*k], per-wavefront counts [16][E])
-inline size_t align_list_ints(int T, int k, int E) {
-  return 3 * (size_t)T * k + (size_t)T + (kAlignThreads / 64) * (size_t)E;
+// Radix digits of the align kernel for E*(nA+1) buckets: as few passes of at most 10 bits as
+// the key width needs, the width spread evenly over them.
+inline void align_digits(int E, int nA, int* digit_bits, int* passes) {
+  const uint32_t nb = (uint32_t)E * (uint32_t)(nA + 1);
+  int bits = 0;
+  while (bits < 31 && (1u << bits) < nb) ++bits;
+  if (bits < 1) bits = 1;
+  *passes = (bits + 9) / 10;
+  *digit_bits = (bits + *passes - 1) / *passes;
+}
+
+inline int align_seg_cap(int T, int k, int E, int nA) {
+  const int64_t P = (int64_t)T * k, nb = (int64_t)E * (nA + 1);
+  return (int)((P < nb ? P : nb) + 1);
+}
+
+// ints of the align kernel's arrays: keys and two pair-id buffers [T*k] each, segment starts and
+// deltas [seg_cap] each
+inline size_t align_list_ints(int T, int k, int E, int nA) {
+  return 3 * (size_t)T * k + 2 * (size_t)align_seg_cap(T, k, E, nA);
 }
 
 // LoRA shrink z = X A^T for the rows of the sorted layout.

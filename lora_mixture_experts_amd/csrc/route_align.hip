@@ -178,17 +178,20 @@ __global__ __launch_bounds__(256) void route_rank_kernel(const float* __restrict
 }
 
 // ------------------------------------------------------------------------------------------
-// Align: one workgroup of 1024 threads.
-//   phase 0  validate adapter ids (out of range -> flag, treated as -1), collect flags, stage
-//   phase A  per-expert pair lists in token order: each wavefront ranks its slice of pairs by
-//            expert (stable), an (expert, wavefront) scan turns the ranks into positions
-//   phase D  count pairs per bucket b = e*(nA+1) + (a+1), one wavefront per expert list
-//   phase 2  exclusive scans: padded segment starts, expert offsets, segment table
-//   phase 3  padding slots (-1) and the row-block -> expert (and first segment) tables
-//   phase 4  scatter pair ids (and each pair's row); inside a bucket pairs keep token order
-// Within a wavefront, lanes with equal key are found by one ballot per key bit, so the rank of
-// a pair among equal-key pairs of earlier lanes is an exact popcount. Every table lives in LDS
-// when it fits and in the workspace otherwise.
+// Align: one workgroup of 1024 threads. Each pair p = t*k + j gets the bucket key
+// b = e*(nA+1) + (a+1) (e its expert, a its token's adapter, -1 for none), and the pairs are
+// sorted by key, stable in pair (= token) order, by least-significant-digit radix passes of D
+// bits (D <= 10, as few passes as the key width allows). A segment is a run of equal keys.
+//   phase 0  keys (adapter ids validated: out of range -> flag, treated as -1), flags
+//   passes   count digits per wavefront slice, exclusive scan in (digit, wavefront) order,
+//            then rank and scatter; the rank of a pair among the equal digits of earlier lanes
+//            of its 64-pair chunk is an exact popcount of a ballot match
+//   phase 1  segment starts (key changes) -> segment id of every sorted position
+//   phase 2  padded segment sizes scanned; each expert's region (the sum over its segments)
+//            padded to block_m; segment table, expert offsets, row block -> segment table
+//   phase 3  padding slots (-1), row block -> expert table; pair ids into their padded rows
+// Every step is a flat loop over pairs, segments or experts: the work is O(T*k + E) whatever
+// the number of adapters. The arrays live in LDS when they fit and in the workspace otherwise.
 // ------------------------------------------------------------------------------------------
 __device__ __forceinline__ uint64_t match_key(bool member, int key, int nbits) {
   uint64_t eq = __ballot(member);
@@ -202,20 +205,24 @@ __device__ __forceinline__ uint64_t match_key(bool member, int key, int nbits) {
 
 __device__ __forceinline__ int round_up_i(int v, int m) { return (v + m - 1) / m * m; }
 
+// Inclusive scan over the 64 lanes with DPP moves: shifts by 1, 2, 4 and 8 within each row of
+// 16 lanes, then the last lane of row 0 (2) is added to row 1 (3) and that of row 1 to rows 2
+// and 3. A lane whose DPP source is missing or masked off adds 0.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return x;
+}
+
 // Exclusive scan of (v0, v1) over the workgroup; red needs 2*32+2 ints.
 __device__ void block_excl_scan2(int v0, int v1, int& ex0, int& ex1, int& tot0, int& tot1,
                                  int* red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  int i0 = v0, i1 = v1;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int a0 = __shfl_up(i0, off);
-    const int a1 = __shfl_up(i1, off);
-    if (lane >= off) {
-      i0 += a0;
-      i1 += a1;
-    }
-  }
+  const int i0 = wave_incl_scan(v0), i1 = wave_incl_scan(v1);
   if (lane == 63) {
     red[wave] = i0;
     red[32 + wave] = i1;
@@ -224,16 +231,7 @@ __device__ void block_excl_scan2(int v0, int v1, int& ex0, int& ex1, int& tot0, 
   if (wave == 0) {
     const int w0 = lane < nw ? red[lane] : 0;
     const int w1 = lane < nw ? red[32 + lane] : 0;
-    int s0 = w0, s1 = w1;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int a0 = __shfl_up(s0, off);
-      const int a1 = __shfl_up(s1, off);
-      if (lane >= off) {
-        s0 += a0;
-        s1 += a1;
-      }
-    }
+    const int s0 = wave_incl_scan(w0), s1 = wave_incl_scan(w1);
     if (lane < nw) {
       red[lane] = s0 - w0;
       red[32 + lane] = s1 - w1;
@@ -253,204 +251,221 @@ __device__ void block_excl_scan2(int v0, int v1, int& ex0, int& ex1, int& tot0, 
 
 __global__ __launch_bounds__(1024) void align_kernel(AlignArgs a) {
   extern __shared__ int smem[];
-  __shared__ int s_ebase[kMaxExperts];
-  __shared__ int s_sexp[kMaxExperts];
+  __shared__ int s_g0[kMaxExperts];    // padded-size scan at the expert's first segment
+  __shared__ int s_sexp[kMaxExperts];  // padded rows of the expert's segments
   __shared__ int s_off[kMaxExperts + 1];
-  __shared__ int s_estart[kMaxExperts + 1];
   __shared__ int s_red[72];
 
   constexpr int nwaves = kAlignThreads / 64, bd = kAlignThreads;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.T, k = a.k, E = a.E, nA = a.nA, P = T * k;
-  const int nb1 = nA + 1, nb = E * nb1;
+  const int nb1 = nA + 1;
   const int seg_pad = a.seg_pad, block_m = a.block_m;
   // p / k as a multiply by ceil(2^32 / k) and a shift: exact for p * k < 2^32
   const uint64_t k_magic = ((1ull << 32) + k - 1) / k;
   auto token_of = [&](int p) { return (int)(((uint64_t)(uint32_t)p * k_magic) >> 32); };
   auto pad_to = [&](int c) { return seg_pad == 1 ? c : round_up_i(c, seg_pad); };
 
-  // carve LDS (or the workspace): lists elist [P] and ad [T]; the rank scratch tk [P],
-  // rank [P], cnt_we [nwaves][E]; tables cnt/start [nb]. With everything in LDS the tables
-  // overlay the rank scratch, which is dead once the expert lists are built.
-  int *elist, *adl, *tk, *rank, *cnt_we, *cnt, *start;
-  {
-    int* dyn = smem;
-    if (a.tables_in_lds && a.lists_in_lds) {
-      elist = dyn;
-      adl = elist + P;
-      tk = adl + T;
-      cnt = tk;
-    } else {
-      if (a.tables_in_lds) {
-        cnt = dyn;
-        dyn += 2 * nb;
-      } else {
-        cnt = a.g_cnt;
-      }
-      elist = a.lists_in_lds ? dyn : a.g_lists;
-      adl = elist + P;
-      tk = adl + T;
-    }
-    rank = tk + P;
-    cnt_we = rank + P;
-    start = a.tables_in_lds ? cnt + nb : a.g_start;
-  }
+  // key [P], v0 [P], v1 [P] (pair ids between passes), then the segment region: starts
+  // [seg_cap] and row deltas [seg_cap]. The digit counts [nwaves << D] overlay the segment
+  // region (unused until the passes are done) in LDS, or take LDS of their own when the arrays
+  // are in the workspace.
+  int* key = a.lists_in_lds ? smem : a.g_lists;
+  int* v0 = key + P;
+  int* v1 = v0 + P;
+  int* seg_lo = v1 + P;
+  int* delta = seg_lo + a.seg_cap;
+  int* cnt = a.lists_in_lds ? seg_lo : smem;
 
   // phase 0
+  // (loads in batches of 8 per thread, issued before any is used)
   int fl_nonfinite = 0, fl_range = 0;
-  for (int i = tid; i < nwaves * E; i += bd) cnt_we[i] = 0;
-  for (int i = tid; i < P; i += bd) tk[i] = a.topk_ids[i];
-  for (int t = tid; t < T; t += bd) {
-    int av = a.adapter_ids[t];
-    if (av < -1 || av >= nA) {
-      fl_range = 1;
-      av = -1;
+  for (int t0 = 0; t0 < T; t0 += 8 * bd) {
+    int f[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int t = t0 + u * bd + tid;
+      f[u] = t < T ? a.tok_flags[t] : 0;
     }
-    if (a.tok_flags[t]) fl_nonfinite = 1;
-    adl[t] = av;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) fl_nonfinite |= f[u] != 0;
+  }
+  for (int q0 = 0; q0 < P; q0 += 8 * bd) {
+    int ex[8], av[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int p = q0 + u * bd + tid;
+      ex[u] = p < P ? a.topk_ids[p] : 0;
+      av[u] = p < P ? a.adapter_ids[token_of(p)] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int p = q0 + u * bd + tid;
+      if (av[u] < -1 || av[u] >= nA) {
+        fl_range = 1;
+        av[u] = -1;
+      }
+      if (p < P) key[p] = ex[u] * nb1 + av[u] + 1;
+    }
+  }
+  for (int e = tid; e < E; e += bd) {
+    s_g0[e] = 0;
+    s_sexp[e] = 0;
   }
   fl_nonfinite = __syncthreads_or(fl_nonfinite);
   fl_range = __syncthreads_or(fl_range);
 
-  // phase A: stable rank of each pair among the pairs of its expert in this wavefront's slice
-  const int ebits = E > 1 ? 32 - __clz(E - 1) : 0;
+  // radix passes, least significant digit first; pass 0 reads the pairs in pair order
+  const int D = a.digit_bits, dmask = (1 << D) - 1, ncnt = nwaves << D;
   const int PP = (P + nwaves - 1) / nwaves;
-  {
-    const int p0 = wave * PP, p1 = min(P, p0 + PP);
+  const int p0 = min(P, wave * PP), p1 = min(P, p0 + PP);
+  const int* src = nullptr;
+  int* dst = v0;
+  for (int pass = 0; pass < a.passes; ++pass) {
+    const int shift = pass * D;
+    for (int i = tid; i < ncnt; i += bd) cnt[i] = 0;
+    __syncthreads();
+    // digits of the wavefront's slice (only this wavefront touches row cnt[wave]; the adds
+    // need no returned value, so they do not wait for each other)
     for (int base = p0; base < p1; base += 64) {
-      const int p = base + lane;
-      const bool valid = p < p1;
-      const int e = valid ? tk[p] : 0;
-      const uint64_t eq = match_key(valid, e, ebits);
-      int c = 0;
-      if (valid && (eq & lanemask_lt()) == 0ull) c = atomicAdd(&cnt_we[wave * E + e], (int)__popcll(eq));
-      const int src = valid ? (__ffsll((unsigned long long)eq) - 1) : lane;
-      c = __shfl(c, src);
-      if (valid) rank[p] = c + (int)__popcll(eq & lanemask_lt());
-    }
-  }
-  __syncthreads();
-  // exclusive scan of cnt_we in (expert, wavefront) order; expert e's list starts at s_estart[e]
-  {
-    const int n = nwaves * E;
-    const int per_t = (n + bd - 1) / bd;
-    const int lo = min(n, tid * per_t), hi = min(n, lo + per_t);
-    int sv = 0;
-    for (int i = lo; i < hi; ++i) sv += cnt_we[(i % nwaves) * E + i / nwaves];
-    int ex, d0, tot, d1;
-    block_excl_scan2(sv, 0, ex, d0, tot, d1, s_red);
-    int run = ex;
-    for (int i = lo; i < hi; ++i) {
-      const int idx = (i % nwaves) * E + i / nwaves;
-      const int c = cnt_we[idx];
-      if (i % nwaves == 0) s_estart[i / nwaves] = run;
-      cnt_we[idx] = run;
-      run += c;
-    }
-    if (tid == 0) s_estart[E] = P;
-  }
-  __syncthreads();
-  {
-    const int p0 = wave * PP, p1 = min(P, p0 + PP);
-    for (int p = p0 + lane; p < p1; p += 64) elist[cnt_we[wave * E + tk[p]] + rank[p]] = p;
-  }
-  __syncthreads();
-  // (the rank scratch is dead from here on; the tables may overlay it)
-  for (int i = tid; i < nb; i += bd) cnt[i] = 0;
-  __syncthreads();
-
-  const int nbits = 32 - __clz(nA);  // bits of a key in [0, nA]
-
-  // phase D: counts per (expert, adapter) bucket over each expert's list
-  for (int e = wave; e < E; e += nwaves) {
-    const int i1 = s_estart[e + 1];
-    for (int base = s_estart[e]; base < i1; base += 64) {
       const int i = base + lane;
-      const bool valid = i < i1;
-      const int key = valid ? adl[token_of(elist[i])] + 1 : 0;
-      const uint64_t eq = match_key(valid, key, nbits);
-      if (valid && (eq & lanemask_lt()) == 0ull) atomicAdd(&cnt[e * nb1 + key], (int)__popcll(eq));
+      const bool valid = i < p1;
+      const int p = valid ? (src ? src[i] : i) : 0;
+      const int dig = valid ? (key[p] >> shift) & dmask : 0;
+      const uint64_t eq = match_key(valid, dig, D);
+      if (valid && (eq & lanemask_lt()) == 0ull) atomicAdd(&cnt[(wave << D) + dig], (int)__popcll(eq));
     }
+    __syncthreads();
+    {
+      const int per_t = (ncnt + bd - 1) / bd;
+      const int lo = min(ncnt, tid * per_t), hi = min(ncnt, lo + per_t);
+      int sv = 0;
+      for (int j = lo; j < hi; ++j) sv += cnt[((j % nwaves) << D) + j / nwaves];
+      int ex, d0, tot, d1;
+      block_excl_scan2(sv, 0, ex, d0, tot, d1, s_red);
+      int run = ex;
+      for (int j = lo; j < hi; ++j) {
+        const int idx = ((j % nwaves) << D) + j / nwaves;
+        const int c = cnt[idx];
+        cnt[idx] = run;
+        run += c;
+      }
+    }
+    __syncthreads();
+    for (int base = p0; base < p1; base += 64) {
+      const int i = base + lane;
+      const bool valid = i < p1;
+      const int p = valid ? (src ? src[i] : i) : 0;
+      const int dig = valid ? (key[p] >> shift) & dmask : 0;
+      const uint64_t eq = match_key(valid, dig, D);
+      int c = 0;
+      if (valid && (eq & lanemask_lt()) == 0ull) c = atomicAdd(&cnt[(wave << D) + dig], (int)__popcll(eq));
+      c = __shfl(c, valid ? (__ffsll((unsigned long long)eq) - 1) : lane);
+      if (valid) dst[c + (int)__popcll(eq & lanemask_lt())] = p;
+    }
+    __syncthreads();
+    src = dst;
+    dst = dst == v0 ? v1 : v0;
+  }
+  const int* sorted = src ? src : v0;  // (no pass runs only when P == 0)
+  int* sid = dst;                      // the other buffer: segment of each sorted position
+
+  // phase 1: contiguous ranges of sorted positions per thread
+  int nseg;
+  {
+    const int per_t = (P + bd - 1) / bd;
+    const int lo = min(P, tid * per_t), hi = min(P, lo + per_t);
+    const int prev0 = lo > 0 ? key[sorted[lo - 1]] : -1;
+    int prev = prev0, ns = 0;
+    for (int i = lo; i < hi; ++i) {
+      const int kk = key[sorted[i]];
+      ns += kk != prev;
+      prev = kk;
+    }
+    int ex, d0, d1;
+    block_excl_scan2(ns, 0, ex, d0, nseg, d1, s_red);
+    int sg = ex - 1;
+    prev = prev0;
+    for (int i = lo; i < hi; ++i) {
+      const int kk = key[sorted[i]];
+      if (kk != prev) seg_lo[++sg] = i;
+      prev = kk;
+      sid[i] = sg;
+    }
+    if (tid == 0) seg_lo[nseg] = P;
   }
   __syncthreads();
 
-  // phase 2
-  const int per = (nb + bd - 1) / bd;
-  const int lo = min(nb, tid * per), hi = min(nb, lo + per);
-  int sv = 0, sn = 0;
-  for (int b = lo; b < hi; ++b) {
-    const int c = cnt[b];
-    sv += pad_to(c);
-    sn += c > 0;
-  }
-  int ev, en, totv, totn;
-  block_excl_scan2(sv, sn, ev, en, totv, totn, s_red);
+  // phase 2: contiguous ranges of segments per thread
+  const int per_s = (nseg + bd - 1) / bd;
+  const int slo = min(nseg, tid * per_s), shi = min(nseg, slo + per_s);
+  int gex;
   {
-    int run = ev;
-    for (int b = lo; b < hi; ++b) {
-      start[b] = run;
-      run += pad_to(cnt[b]);
+    int sum = 0;
+    for (int sg = slo; sg < shi; ++sg) sum += pad_to(seg_lo[sg + 1] - seg_lo[sg]);
+    int d0, gtot, d1;
+    block_excl_scan2(sum, 0, gex, d0, gtot, d1, s_red);
+    int g = gex;
+    int e_prev = slo > 0 ? key[sorted[seg_lo[slo - 1]]] / nb1 : -1;
+    for (int sg = slo; sg < shi; ++sg) {
+      const int e = key[sorted[seg_lo[sg]]] / nb1;
+      if (e != e_prev) s_g0[e] = g;
+      g += pad_to(seg_lo[sg + 1] - seg_lo[sg]);
+      const int e_next = sg + 1 < nseg ? key[sorted[seg_lo[sg + 1]]] / nb1 : -1;
+      if (e_next != e) s_sexp[e] = g;  // the end; the start is subtracted below
+      e_prev = e;
     }
   }
   __syncthreads();
-  for (int e = tid; e < E; e += bd) {
-    const int s0 = start[e * nb1];
-    const int s1 = (e + 1 < E) ? start[(e + 1) * nb1] : totv;
-    s_ebase[e] = s0;
-    s_sexp[e] = s1 - s0;
-  }
-  __syncthreads();
   {
-    const int len = (tid < E) ? round_up_i(s_sexp[tid], block_m) : 0;
-    int eo, dummy_ex, tot, dummy_tot;
-    block_excl_scan2(len, 0, eo, dummy_ex, tot, dummy_tot, s_red);
+    int len = 0;
+    if (tid < E) {
+      s_sexp[tid] -= s_g0[tid];
+      len = round_up_i(s_sexp[tid], block_m);
+    }
+    int eo, d0, tot, d1;
+    block_excl_scan2(len, 0, eo, d0, tot, d1, s_red);
     if (tid < E) s_off[tid] = eo;
     if (tid == 0) s_off[E] = tot;
   }
   __syncthreads();
   {
-    int nz = en;
-    for (int b = lo; b < hi; ++b) {
-      const int e = b / nb1;
-      const int c = cnt[b];
-      const int st = s_off[e] + start[b] - s_ebase[e];
-      start[b] = st;
-      if (c > 0) {
-        int* row = a.seg_table + 4 * nz;
-        row[0] = e;
-        row[1] = (b - e * nb1) - 1;
-        row[2] = st;
-        row[3] = c;
-        // row blocks whose first row lies in this segment (with its padding) start at it
-        if (a.block_seg)
-          for (int bb = (st + block_m - 1) / block_m; bb * block_m < st + round_up_i(c, seg_pad);
-               ++bb)
-            a.block_seg[bb] = nz;
-        ++nz;
-      }
+    int g = gex;
+    for (int sg = slo; sg < shi; ++sg) {
+      const int i0 = seg_lo[sg], c = seg_lo[sg + 1] - i0;
+      const int kk = key[sorted[i0]];
+      const int e = kk / nb1;
+      const int st = s_off[e] + g - s_g0[e];
+      int* row = a.seg_table + 4 * sg;
+      row[0] = e;
+      row[1] = kk - e * nb1 - 1;
+      row[2] = st;
+      row[3] = c;
+      // row blocks whose first row lies in this segment (with its padding) start at it
+      if (a.block_seg)
+        for (int bb = (st + block_m - 1) / block_m; bb * block_m < st + pad_to(c); ++bb)
+          a.block_seg[bb] = sg;
+      delta[sg] = st - i0;
+      g += pad_to(c);
     }
   }
   for (int e = tid; e <= E; e += bd) a.expert_offsets[e] = s_off[e];
   if (tid == 0) {
-    *a.n_seg = totn;
+    *a.n_seg = nseg;
     *a.flags = (fl_nonfinite ? 1 : 0) | (fl_range ? 2 : 0);
     if (a.n_blocks) *a.n_blocks = s_off[E] / block_m;
   }
   __syncthreads();
 
   // phase 3
-  for (int e = wave; e < E; e += nwaves) {
-    const int b0 = e * nb1;
-    if (seg_pad > 1) {
-      for (int q = lane; q < nb1; q += 64) {
-        const int c = cnt[b0 + q];
-        if (c > 0) {
-          const int st = start[b0 + q];
-          for (int s = st + c; s < st + round_up_i(c, seg_pad); ++s) a.sorted_pairs[s] = -1;
-        }
-      }
+  if (seg_pad > 1)
+    for (int sg = tid; sg < nseg; sg += bd) {
+      const int i0 = seg_lo[sg], c = seg_lo[sg + 1] - i0;
+      const int st = i0 + delta[sg];
+      for (int q = st + c; q < st + pad_to(c); ++q) a.sorted_pairs[q] = -1;
     }
-    for (int s = s_off[e] + s_sexp[e] + lane; s < s_off[e + 1]; s += 64) a.sorted_pairs[s] = -1;
+  for (int e = wave; e < E; e += nwaves) {
+    for (int q = s_off[e] + s_sexp[e] + lane; q < s_off[e + 1]; q += 64) a.sorted_pairs[q] = -1;
     if (a.block_expert)
       for (int bb = s_off[e] / block_m + lane; bb < s_off[e + 1] / block_m; bb += 64) {
         a.block_expert[bb] = e;
@@ -458,29 +473,11 @@ __global__ __launch_bounds__(1024) void align_kernel(AlignArgs a) {
         if (a.block_seg && bb * block_m >= s_off[e] + s_sexp[e]) a.block_seg[bb] = -1;
       }
   }
-  __syncthreads();
-  for (int i = tid; i < nb; i += bd) cnt[i] = 0;
-  __syncthreads();
-
-  // phase 4
-  for (int e = wave; e < E; e += nwaves) {
-    const int i1 = s_estart[e + 1];
-    for (int base = s_estart[e]; base < i1; base += 64) {
-      const int i = base + lane;
-      const bool valid = i < i1;
-      const int p = valid ? elist[i] : 0;
-      const int key = valid ? adl[token_of(p)] + 1 : 0;
-      const uint64_t eq = match_key(valid, key, nbits);
-      int cur = 0;
-      if (valid && (eq & lanemask_lt()) == 0ull) cur = atomicAdd(&cnt[e * nb1 + key], (int)__popcll(eq));
-      const int src = valid ? (__ffsll((unsigned long long)eq) - 1) : lane;
-      cur = __shfl(cur, src);
-      if (valid) {
-        const int pos = start[e * nb1 + key] + cur + (int)__popcll(eq & lanemask_lt());
-        a.sorted_pairs[pos] = p;
-        if (a.pair_row) a.pair_row[p] = pos;
-      }
-    }
+  for (int i = tid; i < P; i += bd) {
+    const int p = sorted[i];
+    const int pos = i + delta[sid[i]];
+    a.sorted_pairs[pos] = p;
+    if (a.pair_row) a.pair_row[p] = pos;
   }
 }
 
