@@ -27,58 +27,105 @@
 
 namespace moelora {
 
-__device__ __forceinline__ float dot8_bf16(const float* z, u32x4 v) {
-  float s = z[0] * bf16_lo(v.x);
-  s += z[1] * bf16_hi(v.x);
-  s += z[2] * bf16_lo(v.y);
-  s += z[3] * bf16_hi(v.y);
-  s += z[4] * bf16_lo(v.z);
-  s += z[5] * bf16_hi(v.z);
-  s += z[6] * bf16_lo(v.w);
-  s += z[7] * bf16_hi(v.w);
-  return s;
-}
-
-// out[b][v] += sum_q z[q] * B_b[v][q] for NB groups of 4 weight rows (gate_up: the gate and
-// the up rows) at Bb[b] + v*r; z is the row's shrink output (r floats). The loads of 16 rank
-// values of z and of every group are issued together before the products.
-template <int NB>
-__device__ __forceinline__ void lora_expand(const float* __restrict__ zrow,
-                                            const uint16_t* const (&Bb)[NB], int r,
-                                            float (&out)[NB][4]) {
-  for (int q0 = 0; q0 < r; q0 += 16) {
-    float z[16];
-    u32x4 bv[NB][4][2];
+// LoRA expand of the block, as MFMAs added onto the base accumulators: for every adapter run
+// (the distinct adapters of the block's live rows; the sorted layout keeps one expert's rows of
+// one adapter contiguous), acc[t][nt] += B_t z^T, where B_t holds the 16 weight rows of output
+// tile t (rows brow[t] .. +15 of the expert's B for the run's adapter, r ranks each) and z the
+// shrink output of the rows of token tile nt, zero outside the run. B_t is the A operand (lane:
+// row m, ranks 8*kq ..), z the B operand (lane: token row m, the same ranks), so the result lands
+// in the accumulator layout of the base product. z (fp32) enters as two bf16 parts, z = hi + lo
+// with lo = bf16(z - hi), which keeps about 16 of its mantissa bits. Up to RB runs' B fragments
+// are loaded before any of their MFMAs, so a block's runs cost a few memory round trips rather
+// than one per run.
+template <int NT, int NW, int RB>
+__device__ __forceinline__ void lora_mfma(f32x4 (&acc)[NW][NT], const int (&brow)[NW],
+                                          const uint16_t* __restrict__ bexp, size_t ad_stride,
+                                          int r, const float* s_z, const int (&adap)[NT],
+                                          int lane) {
+  const int m = lane & 15, kq = lane >> 4;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  for (int c0 = 0; c0 < r; c0 += 32) {
+    const int q = c0 + 8 * kq;  // this lane's 8 ranks
+    u32x4 zh[NT], zl[NT];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int q = q0 + 8 * c;
+    for (int nt = 0; nt < NT; ++nt) {
+      zh[nt] = zero;
+      zl[nt] = zero;
       if (q < r) {
-        const f32x4 lo = *reinterpret_cast<const f32x4*>(zrow + q);
-        const f32x4 hi = *reinterpret_cast<const f32x4*>(zrow + q + 4);
+        const float* zr = s_z + (nt * 16 + m) * r + q;
+        const f32x4 z0 = *reinterpret_cast<const f32x4*>(zr);
+        const f32x4 z1 = *reinterpret_cast<const f32x4*>(zr + 4);
+        const float z[8] = {z0[0], z0[1], z0[2], z0[3], z1[0], z1[1], z1[2], z1[3]};
+        float hi[8], lo[8];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          z[8 * c + t] = lo[t];
-          z[8 * c + 4 + t] = hi[t];
+        for (int i = 0; i < 8; ++i) {
+          hi[i] = __uint_as_float(f32_to_bf16_bits(z[i]) << 16);
+          lo[i] = z[i] - hi[i];
         }
-#pragma unroll
-        for (int g = 0; g < NB; ++g)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) bv[g][v][c] = ldg16(Bb[g] + (size_t)v * r + q);
-      } else {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) z[8 * c + t] = 0.f;
-#pragma unroll
-        for (int g = 0; g < NB; ++g)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) bv[g][v][c] = u32x4{0u, 0u, 0u, 0u};
+        zh[nt] = u32x4{pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3]),
+                       pack_bf16x2(hi[4], hi[5]), pack_bf16x2(hi[6], hi[7])};
+        zl[nt] = u32x4{pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]),
+                       pack_bf16x2(lo[4], lo[5]), pack_bf16x2(lo[6], lo[7])};
       }
     }
+    // rows of each token tile still to do (lanes 0-15 carry rows 0-15; the masks are uniform)
+    uint32_t todo[NT];
 #pragma unroll
-    for (int g = 0; g < NB; ++g)
+    for (int nt = 0; nt < NT; ++nt) todo[nt] = (uint32_t)__ballot(adap[nt] >= 0) & 0xffffu;
+    while (true) {
+      int rad[RB];
+      uint32_t rmask[RB][NT];
+      int nr = 0;
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
+      for (int i = 0; i < RB; ++i) {
+        int nt0 = -1;
 #pragma unroll
-        for (int c = 0; c < 2; ++c) out[g][v] += dot8_bf16(z + 8 * c, bv[g][v][c]);
+        for (int nt = NT - 1; nt >= 0; --nt)
+          if (todo[nt]) nt0 = nt;
+        if (nt0 < 0) break;
+        int adv = adap[0];
+#pragma unroll
+        for (int nt = 1; nt < NT; ++nt)
+          if (nt == nt0) adv = adap[nt];
+        const int ad = __builtin_amdgcn_readlane(adv, __builtin_ctz(todo[nt0]));
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const uint32_t mk = (uint32_t)__ballot(adap[nt] == ad) & todo[nt];
+          rmask[i][nt] = mk;
+          todo[nt] &= ~mk;
+        }
+        rad[i] = ad;
+        nr = i + 1;
+      }
+      if (nr == 0) break;
+      u32x4 bl[RB][NW];
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        if (i < nr) {
+          const uint16_t* ba = bexp + (size_t)rad[i] * ad_stride;
+#pragma unroll
+          for (int t = 0; t < NW; ++t)
+            bl[i][t] = q < r ? ldg16(ba + (size_t)(brow[t] + m) * r + q) : zero;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        if (i < nr) {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            if (rmask[i][nt]) {
+              const bool in = (rmask[i][nt] >> m) & 1u;
+              const u32x4 a_hi = in ? zh[nt] : zero, a_lo = in ? zl[nt] : zero;
+#pragma unroll
+              for (int t = 0; t < NW; ++t) {
+                acc[t][nt] = mfma16(bl[i][t], a_hi, acc[t][nt]);
+                acc[t][nt] = mfma16(bl[i][t], a_lo, acc[t][nt]);
+              }
+            }
+          }
+        }
+      }
+    }
   }
 }
 
@@ -226,6 +273,25 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs a) {
 #undef MOELORA_COMPUTE
 
   // Epilogue: lane holds weight rows n0 + 16*rt + 4*kq + v (v < 4) for token row (lane % 16).
+  // The LoRA term first (down: K split 0 only), onto the accumulators.
+  if (zsplit == 0) {
+    int brow[NW];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      if (SPLIT) {
+        brow[0] = (up_wave ? (int)N : 0) + n0;
+      } else if (GATEUP) {
+        brow[rt] = n0 + 16 * rt;
+        brow[NW - RT + rt] = (int)N + n0 + 16 * rt;
+      } else {
+        brow[rt] = n0 + 16 * rt;
+      }
+    }
+    const size_t rows_e = (GATEUP ? 2 : 1) * N;
+    constexpr int RB = NW >= 8 ? 1 : 8 / NW;
+    lora_mfma<NT, NW, RB>(acc, brow, a.Bw + (size_t)e * rows_e * a.r, (size_t)a.E * rows_e * a.r,
+                          a.r, s_z, adap, lane);
+  }
   if (SPLIT) {
     if (up_wave) {
 #pragma unroll
@@ -238,8 +304,6 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs a) {
   for (int nt = 0; nt < NT; ++nt) {
     const int row = blk * BM + nt * 16 + m;
     if (pair[nt] < 0) continue;
-    const int ad = adap[nt];
-    const float* zrow = s_z + (nt * 16 + m) * a.r;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const int nb = n0 + 16 * rt + 4 * kq;
@@ -250,11 +314,6 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs a) {
           gu[0][v] = acc[rt][nt][v];
           gu[1][v] = SPLIT ? s_up[((wave & 1) * NT + nt) * 64 + lane][v] : acc[NW - RT + rt][nt][v];
         }
-        if (ad >= 0) {
-          const uint16_t* bg = a.Bw + (((size_t)ad * a.E + e) * 2 * N + nb) * a.r;
-          const uint16_t* const bb[2] = {bg, bg + N * a.r};
-          lora_expand<2>(zrow, bb, a.r, gu);
-        }
         float hv[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) hv[v] = gu[0][v] / (1.f + __expf(-gu[0][v])) * gu[1][v];
@@ -264,10 +323,6 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs a) {
         float d[1][4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) d[0][v] = acc[rt][nt][v];
-        if (ad >= 0 && zsplit == 0) {
-          const uint16_t* const bd[1] = {a.Bw + (((size_t)ad * a.E + e) * N + nb) * a.r};
-          lora_expand<1>(zrow, bd, a.r, d);
-        }
         *reinterpret_cast<f32x4*>(a.d_out + zsplit * a.d_split_stride + (size_t)row * N + nb) =
             f32x4{d[0][0], d[0][1], d[0][2], d[0][3]};
       }
