@@ -126,14 +126,16 @@ __global__ __launch_bounds__(256) void lora_shrink_kernel(ShrinkArgs a) {
     for (int c = 0; c < NCT; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     u32x4 xa0[4], bw0[NCT][4], xa1[4], bw1[NCT][4];
+    // step ks covers k in [128 ks, 128 ks + 128); MFMA jj takes k = 32 jj + 8 kq .. + 8 from lane
+    // (m, kq), so each load instruction reads 64 contiguous bytes of every row it touches
     auto load = [&](int ks, u32x4* xa, u32x4 (*bw)[4]) {
-      const uint32_t kb = (uint32_t)(ks * 128 + kq * 32) * 2;
+      const uint32_t kb = (uint32_t)(ks * 128 + kq * 8) * 2;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) xa[jj] = bufld16(xr, xo + kb + 16u * jj);
+      for (int jj = 0; jj < 4; ++jj) xa[jj] = bufld16(xr, xo + kb + 64u * jj);
 #pragma unroll
       for (int c = 0; c < NCT; ++c)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) bw[c][jj] = bufld16(ar, ao[c] + kb + 16u * jj);
+        for (int jj = 0; jj < 4; ++jj) bw[c][jj] = bufld16(ar, ao[c] + kb + 64u * jj);
     };
     auto mma = [&](const u32x4* xa, const u32x4 (*bw)[4]) {
 #pragma unroll
