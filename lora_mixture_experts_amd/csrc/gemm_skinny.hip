@@ -288,7 +288,8 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs a) {
       }
     }
     const size_t rows_e = (GATEUP ? 2 : 1) * N;
-    constexpr int RB = NW >= 8 ? 1 : 8 / NW;
+    // runs per batch of B loads: fewer for down, whose register count sets its occupancy
+    constexpr int RB = (GATEUP ? 8 : 4) / NW > 0 ? (GATEUP ? 8 : 4) / NW : 1;
     lora_mfma<NT, NW, RB>(acc, brow, a.Bw + (size_t)e * rows_e * a.r, (size_t)a.E * rows_e * a.r,
                           a.r, s_z, adap, lane);
   }
