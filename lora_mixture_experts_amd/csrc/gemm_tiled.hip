@@ -239,7 +239,8 @@ __global__ __launch_bounds__(64 * NW, 1) void tiled_gemm_kernel(GemmArgs a, int 
 
   // Tile order. The live tiles (n_blocks row blocks x n_tiles_n column tiles; the grid is
   // sized for the largest n_blocks) are numbered column group by column group, row group by row
-  // group, in groups of up to 8 row blocks x 8 column tiles. Hardware workgroup ids go
+  // group, in groups of up to 4 row blocks x 4 column tiles (measured best of the shapes from
+  // 2x8 to 16x8 on prefill and both adapter-stress batches). Hardware workgroup ids go
   // round-robin over the 8 XCDs, so each XCD is given an equal contiguous range of that
   // numbering: the workgroups it runs at once cover a few groups, every token tile and weight
   // tile fetched into its L2 serves several of them, and no XCD gets more tiles than another.
@@ -254,14 +255,15 @@ __global__ __launch_bounds__(64 * NW, 1) void tiled_gemm_kernel(GemmArgs a, int 
   if (slot >= per_xcd || tk >= live) return;
   const int ks = GATEUP ? 0 : tk / tiles;        // K split
   const int t = tk - ks * tiles;
-  const int cg = t / (nblk * 8);                 // column group (all but the last are 8 wide)
-  const int cols = min(8, n_tiles_n - cg * 8);
-  const int u = t - cg * nblk * 8;
-  const int rg = u / (8 * cols);                 // row group (all but the last are 8 tall)
-  const int rows = min(8, nblk - rg * 8);
-  const int w = u - rg * 8 * cols;
-  const int blk = rg * 8 + w % rows;
-  const int ntile = cg * 8 + w / rows;
+  constexpr int GR = 4, GC = 4;                   // row blocks and column tiles per group
+  const int cg = t / (nblk * GC);                 // column group (all but the last GC wide)
+  const int cols = min(GC, n_tiles_n - cg * GC);
+  const int u = t - cg * nblk * GC;
+  const int rg = u / (GR * cols);                 // row group (all but the last GR tall)
+  const int rows = min(GR, nblk - rg * GR);
+  const int w = u - rg * GR * cols;
+  const int blk = rg * GR + w % rows;
+  const int ntile = cg * GC + w / rows;
   const int e = a.block_expert[blk];
   const int K = a.K;
   const int kspan = GATEUP ? K : K / a.ksplit;  // this split's K range: [ks * kspan, +kspan)
