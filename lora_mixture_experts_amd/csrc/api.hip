@@ -235,6 +235,7 @@ bool moelora_make_layout(int T, int h, int I, int E, int nA, int r, int topk, Mo
   L->block_expert = take(4 * (size_t)(L->cap / 16 + 1));
   L->block_seg = take(4 * (size_t)(L->cap / 16 + 1));
   L->pair_row = take(4 * (size_t)P);
+  L->sorted_ad = take(4 * (size_t)L->cap);
   L->seg_table = take(16 * (size_t)P);
   L->n_seg = take(4);
   L->z1 = take(4 * (size_t)kMaxSplit * L->cap * r);
@@ -317,6 +318,7 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   int* block_expert = (int*)(ws + L.block_expert);
   int* block_seg = (int*)(ws + L.block_seg);
   int* pair_row = (int*)(ws + L.pair_row);
+  int* sorted_ad = (int*)(ws + L.sorted_ad);
   float* z1 = (float*)(ws + L.z1);
   float* z2 = (float*)(ws + L.z2);
   uint16_t* act = (uint16_t*)(ws + L.act);
@@ -348,6 +350,7 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   al.block_expert = block_expert;
   al.block_seg = block_seg;
   al.pair_row = pair_row;
+  al.sorted_ad = sorted_ad;
   al.n_blocks = n_blocks;
   al.g_lists = (int*)(ws + L.align_lists);
   const int64_t max_rows = P + (int64_t)E * (bm - 1);
@@ -380,6 +383,7 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
 
   ShrinkArgs sh;
   sh.sorted_pairs = sorted;
+  sh.sorted_ad = sorted_ad;
   sh.block_expert = block_expert;
   sh.n_blocks = n_blocks;
   sh.bm = bm;
@@ -396,6 +400,7 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   GemmArgs g;
   g.cap = L.cap;
   g.sorted_pairs = sorted;
+  g.sorted_ad = sorted_ad;
   g.block_expert = block_expert;
   g.block_seg = block_seg;
   g.seg_table = al.seg_table;
@@ -572,6 +577,7 @@ int moe_lora_route_align(const float* router_logits, const int32_t* adapter_ids,
   al.block_expert = nullptr;
   al.block_seg = nullptr;
   al.pair_row = nullptr;
+  al.sorted_ad = nullptr;
   al.n_blocks = nullptr;
   al.g_lists = (int*)(ws + L.align_lists);
   const size_t lds = align_lds_plan(d->T, topk, d->n_experts, d->n_adapters, &al);

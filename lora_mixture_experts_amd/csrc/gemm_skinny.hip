@@ -213,7 +213,7 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs a) {
     const int row = blk * BM + nt * 16 + m;
     const int p = a.sorted_pairs[row];
     pair[nt] = p;
-    adap[nt] = p >= 0 ? sanitize_adapter(a.adapter_ids[p / a.k], a.nA) : -1;
+    adap[nt] = a.sorted_ad[row];
     xo[nt] = p < 0 ? kOutOfRange : (uint32_t)((GATEUP ? (size_t)(p / a.k) : (size_t)row) * K * 2);
   }
 

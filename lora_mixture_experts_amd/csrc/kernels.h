@@ -23,6 +23,8 @@ struct AlignArgs {
   int* block_seg;       // [padded total / block_m]: segment holding the block's first row, or -1
                         // (a block of padding rows); written when block_expert is
   int* pair_row;        // [T*k]: sorted row of each pair, or nullptr
+  int* sorted_ad;       // [>= padded total]: adapter of each sorted row (-1: none or padding),
+                        // or nullptr
   int* n_blocks;        // [1] or nullptr
   int* g_lists;         // workspace for the arrays when they do not fit in LDS
   int lists_in_lds;
@@ -58,6 +60,7 @@ struct ShrinkArgs {
   const uint16_t* X;  // gather: x [T][K]; otherwise act [cap][K]
   uint32_t x_bytes;   // size of X (< 2 GiB)
   const int* sorted_pairs;
+  const int* sorted_ad;  // adapter of each sorted row, -1 for none or padding
   const int* block_expert;
   const int* block_seg;  // (64-row shrink) first segment of each row block, or -1
   const int* seg_table;  // (64-row shrink) [n_seg][4]
@@ -70,7 +73,8 @@ struct ShrinkArgs {
   int S;               // K splits over workgroups
   float* zpart;        // [S][cap][r]; written for the rows that carry an adapter
   int64_t cap;
-  int xcd_ranges;      // 1: each XCD takes a contiguous range of the work order (long runs)
+  int xcd_ranges;      // 1: split-major order, each XCD a contiguous range of it (long runs);
+                       // 0: tile-major, the S splits of a 16-row tile on consecutive ids
   int after64;         // 16-row shrink: only the sub-blocks the 64-row shrink leaves
 };
 
@@ -85,6 +89,7 @@ struct GemmArgs {
   const uint16_t* zhl;  // tiled: [2][cap][r] the same as bf16 high and low planes
   int64_t cap;
   const int* sorted_pairs;
+  const int* sorted_ad;  // adapter of each sorted row, -1 for none or padding
   const int* block_expert;
   const int* block_seg;  // first segment of each row block (or -1), see AlignArgs
   const int* seg_table;  // [n_seg][4]: expert, adapter, first sorted row, rows

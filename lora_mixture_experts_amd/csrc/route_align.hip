@@ -189,7 +189,8 @@ __global__ __launch_bounds__(256) void route_rank_kernel(const float* __restrict
 //   phase 1  segment starts (key changes) -> segment id of every sorted position
 //   phase 2  padded segment sizes scanned; each expert's region (the sum over its segments)
 //            padded to block_m; segment table, expert offsets, row block -> segment table
-//   phase 3  padding slots (-1), row block -> expert table; pair ids into their padded rows
+//   phase 3  padding slots (-1), row block -> expert table; pair ids (and their adapters)
+//            into their padded rows
 // Every step is a flat loop over pairs, segments or experts: the work is O(T*k + E) whatever
 // the number of adapters. The arrays live in LDS when they fit and in the workspace otherwise.
 // ------------------------------------------------------------------------------------------
@@ -462,10 +463,16 @@ __global__ __launch_bounds__(1024) void align_kernel(AlignArgs a) {
     for (int sg = tid; sg < nseg; sg += bd) {
       const int i0 = seg_lo[sg], c = seg_lo[sg + 1] - i0;
       const int st = i0 + delta[sg];
-      for (int q = st + c; q < st + pad_to(c); ++q) a.sorted_pairs[q] = -1;
+      for (int q = st + c; q < st + pad_to(c); ++q) {
+        a.sorted_pairs[q] = -1;
+        if (a.sorted_ad) a.sorted_ad[q] = -1;
+      }
     }
   for (int e = wave; e < E; e += nwaves) {
-    for (int q = s_off[e] + s_sexp[e] + lane; q < s_off[e + 1]; q += 64) a.sorted_pairs[q] = -1;
+    for (int q = s_off[e] + s_sexp[e] + lane; q < s_off[e + 1]; q += 64) {
+      a.sorted_pairs[q] = -1;
+      if (a.sorted_ad) a.sorted_ad[q] = -1;
+    }
     if (a.block_expert)
       for (int bb = s_off[e] / block_m + lane; bb < s_off[e + 1] / block_m; bb += 64) {
         a.block_expert[bb] = e;
@@ -478,6 +485,7 @@ __global__ __launch_bounds__(1024) void align_kernel(AlignArgs a) {
     const int pos = i + delta[sid[i]];
     a.sorted_pairs[pos] = p;
     if (a.pair_row) a.pair_row[p] = pos;
+    if (a.sorted_ad) a.sorted_ad[pos] = key[p] % nb1 - 1;
   }
 }
 

@@ -27,52 +27,60 @@ namespace moelora {
 template <bool GATHER, int NCT>
 __global__ __launch_bounds__(256) void lora_shrink_kernel(ShrinkArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // Work order: the live (16-row tile, split) items, split by split, tile by tile. Hardware
-  // workgroup ids go round-robin over the 8 XCDs. With long adapter runs (xcd_ranges) each XCD is
-  // given an equal contiguous range of that order instead, so that neighbouring tiles of one run
-  // and split run on one XCD and share the A slab of their K range in its L2; with short runs
-  // the round-robin spreads the costlier tiles (many runs) evenly.
-  const int live16 = *a.n_blocks * a.bm / 16;
-  const int live = live16 * a.S;
-  int item = blockIdx.x;
+  // Work order. With long adapter runs (xcd_ranges) the live (16-row tile, split) items are
+  // numbered split by split, tile by tile, and each XCD (hardware workgroup ids go round-robin
+  // over the 8) is given an equal contiguous range, so that neighbouring tiles of one run and
+  // split run on one XCD and share the A slab of their K range in its L2. Otherwise the S splits
+  // of a tile take consecutive ids: the tile follows from the id alone, so the tile's rows are
+  // fetched together with the live row count instead of after it.
+  int s, row0;
   if (a.xcd_ranges) {
+    const int live16 = *a.n_blocks * a.bm / 16;
+    const int live = live16 * a.S;
     const int per_xcd = (live + 7) >> 3;
     const int slot = blockIdx.x >> 3;
     if (slot >= per_xcd) return;
-    item = (blockIdx.x & 7) * per_xcd + slot;
+    const int item = (blockIdx.x & 7) * per_xcd + slot;
+    if (item >= live) return;
+    s = item / live16;
+    row0 = (item - s * live16) * 16;
+  } else {
+    const int tile = blockIdx.x / a.S;
+    s = blockIdx.x - tile * a.S;
+    row0 = tile * 16;
+    if (row0 + 16 > a.cap) return;  // (ids of the grid's round-up to the 8 XCDs)
   }
-  if (item >= live) return;
-  const int s = item / live16;
-  const int row0 = (item - s * live16) * 16;
+  // rows, adapters and expert of the tile (a tile past the live rows reads stale entries of the
+  // sorted layout, inside its capacity, and leaves)
+  __shared__ int s_pair[16], s_ad[16], s_nrun, s_lo[16], s_hi[16], s_rad[16];
+  if (tid < 16) {
+    s_pair[tid] = a.sorted_pairs[row0 + tid];
+    s_ad[tid] = a.sorted_ad[row0 + tid];
+  }
   const int e = a.block_expert[row0 / a.bm];
+  if (!a.xcd_ranges && row0 >= *a.n_blocks * a.bm) return;
   // with the 64-row shrink, only the tiles of sub-blocks it leaves (many short runs)
   if (a.after64 && count_runs64(a.block_seg, a.seg_table, *a.n_seg, a.nA, row0 / a.bm,
                                 row0 & ~63, kShrink64MaxRuns) <= kShrink64MaxRuns)
     return;
-
-  // adapter runs of the tile: run_lo[i]..run_hi[i] share adapter run_ad[i]
-  __shared__ int s_pair[16], s_ad[16], s_nrun, s_lo[16], s_hi[16], s_rad[16];
-  if (tid < 16) {
-    const int p = a.sorted_pairs[row0 + tid];
-    s_pair[tid] = p;
-    s_ad[tid] = p >= 0 ? sanitize_adapter(a.adapter_ids[p / a.k], a.nA) : -1;
-  }
   __syncthreads();
-  if (tid == 0) {
-    int n = 0;
-    for (int i = 0; i < 16;) {
-      const int ad = s_ad[i];
-      int j = i + 1;
-      while (j < 16 && s_ad[j] == ad) ++j;
-      if (ad >= 0) {
-        s_lo[n] = i;
-        s_hi[n] = j;
-        s_rad[n] = ad;
-        ++n;
-      }
-      i = j;
+  // adapter runs of the tile: rows s_lo[i] .. s_hi[i] - 1 share adapter s_rad[i] (rows without
+  // an adapter belong to no run). A run starts where the adapter changes; lanes 0-15 of the
+  // first wavefront hold the rows.
+  if (wave == 0) {
+    const int ad = lane < 16 ? s_ad[lane] : -2;
+    const int prev = (lane >= 1 && lane < 16) ? s_ad[lane - 1] : -2;
+    const bool change = lane < 16 && (lane == 0 || ad != prev);
+    const uint64_t chg = __ballot(change);
+    const uint64_t starts = __ballot(change && ad >= 0);
+    if (change && ad >= 0) {
+      const int idx = (int)__popcll(starts & lanemask_lt());
+      const uint64_t later = chg & ~((2ull << lane) - 1ull);  // lane < 16
+      s_lo[idx] = lane;
+      s_hi[idx] = later ? (int)__ffsll((unsigned long long)later) - 1 : 16;
+      s_rad[idx] = ad;
     }
-    s_nrun = n;
+    if (lane == 0) s_nrun = (int)__popcll(starts);
   }
   __syncthreads();
 
