@@ -457,15 +457,6 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   }
   g.ksplit = 1;
   g.d_split_stride = L.cap * (int64_t)h;
-  {
-    // MOELORA_SKINNY_GROUP overrides the skinny kernels' row blocks per group (experiments)
-    static int grp = -1;
-    if (grp < 0) {
-      const char* env = getenv("MOELORA_SKINNY_GROUP");
-      grp = env ? atoi(env) : 0;
-    }
-    g.blk_group = grp >= 1 ? grp : 1;  // measured best on decode: block by block
-  }
   g.n_col_tiles = g.N / (plan.gu.split ? 32 : 64 * plan.gu.rt);
   const hipError_t gu_err = path.tiled ? launch_tiled(path.tc, true, g, stream)
                                        : launch_skinny(plan.gu, true, g, max_blocks, stream);

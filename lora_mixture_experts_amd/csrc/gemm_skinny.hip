@@ -144,11 +144,10 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs a) {
   constexpr int BM = 16 * NT;
   constexpr int KS = 32 * P;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // Work order: the live (row block, column tile) items are numbered in groups of G consecutive
-  // row blocks, column tile by column tile, and every XCD (hardware workgroup ids go
-  // round-robin over the 8) gets an equal contiguous share. With G = 1 (the default) an XCD
-  // takes whole row blocks: their token rows stay in its L2 while the column tiles pass and
-  // it streams consecutive weight rows of one expert.
+  // Work order: the live (row block, column tile) items are numbered column tile by column
+  // tile within each row block, and every XCD (hardware workgroup ids go round-robin over the
+  // 8) gets an equal contiguous share: it takes whole row blocks, whose token rows stay in its
+  // L2 while the column tiles pass, and streams consecutive weight rows of one expert.
   const int ncol = a.n_col_tiles;
   const int nblk = *a.n_blocks;
   const int live = nblk * ncol;
@@ -156,12 +155,27 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs a) {
   const int slot = blockIdx.x >> 3;
   const int t = (blockIdx.x & 7) * per_xcd + slot;
   if (slot >= per_xcd || t >= live) return;
-  const int G = a.blk_group;  // row blocks per group
-  const int sg = t / (G * ncol);
-  const int rows_g = min(G, nblk - sg * G);
-  const int u = t - sg * G * ncol;
-  const int blk = sg * G + u % rows_g;
-  const int ctile = u / rows_g;
+  const int blk = t / ncol;
+  const int ctile = t - blk * ncol;
+  // The block's expert and token rows (pair ids, adapters); the pair and adapter serve the
+  // epilogue too, so their latency hides behind the main loop. Token rows are read with buffer loads: a padding row (pair -1) gets an out-of-range
+  // offset and loads zeros without touching memory. Every load stays unconditional, which keeps
+  // the compiler's count of outstanding loads exact, so the prefetch below overlaps the MFMAs.
+  const int m = lane & 15, kq = lane >> 4;
+  const int K = a.K;
+  const int e = a.block_expert[blk];
+  uint32_t xo[NT];
+  int pair[NT], adap[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int row = blk * BM + nt * 16 + m;
+    const int p = a.sorted_pairs[row];
+    pair[nt] = p;
+    adap[nt] = a.sorted_ad[row];
+    xo[nt] = p < 0 ? kOutOfRange : (uint32_t)((GATEUP ? (size_t)(p / a.k) : (size_t)row) * K * 2);
+  }
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.X, a.x_bytes);
+
   const int n0 = SPLIT ? (ctile * 2 + (wave & 1)) * 16 : (ctile * 4 + wave) * 16 * RT;
   const bool up_wave = SPLIT && wave >= 2;
   __shared__ f32x4 s_up[SPLIT ? 2 * 64 * NT : 1];
@@ -181,9 +195,6 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs a) {
       *reinterpret_cast<f32x4*>(s_z + i) = *reinterpret_cast<const f32x4*>(zp + i);
     __syncthreads();
   };
-  const int e = a.block_expert[blk];
-  const int m = lane & 15, kq = lane >> 4;
-  const int K = a.K;
   const size_t N = (size_t)a.N;
   const int nks = K / KS;
   const int ks0 = (nks * zsplit) / a.ksplit, ks1 = (nks * (zsplit + 1)) / a.ksplit;
@@ -199,22 +210,6 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs a) {
     } else {
       wp[rt] = a.W + ((size_t)e * N + n0 + 16 * rt + m) * K;
     }
-  }
-  // Token rows, read with buffer loads: a padding row (pair -1) gets an out-of-range offset and
-  // loads zeros without touching memory. Every load stays unconditional, which keeps the
-  // compiler's count of outstanding loads exact, so the prefetch below overlaps the MFMAs.
-  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.X, a.x_bytes);
-  // (the pair and adapter of each token row are fetched here, for the epilogue: their latency
-  // hides behind the main loop)
-  uint32_t xo[NT];
-  int pair[NT], adap[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int row = blk * BM + nt * 16 + m;
-    const int p = a.sorted_pairs[row];
-    pair[nt] = p;
-    adap[nt] = a.sorted_ad[row];
-    xo[nt] = p < 0 ? kOutOfRange : (uint32_t)((GATEUP ? (size_t)(p / a.k) : (size_t)row) * K * 2);
   }
 
   f32x4 acc[NW][NT];

@@ -105,7 +105,6 @@ struct GemmArgs {
   int64_t d_split_stride;
   int n_blocks_max;   // row blocks the grid is sized for (>= *n_blocks)
   int n_col_tiles;    // skinny: column tiles of one row block (N / columns per workgroup)
-  int blk_group;      // skinny: row blocks per group of the work order (>= 1)
 };
 
 // Tile shape of the LDS-staged GEMM: nw wavefronts of WM x WN each; NST LDS stages of BK k.
