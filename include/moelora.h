@@ -89,10 +89,12 @@ int moe_lora_forward(const void *x, const float *router_logits, const void *W1, 
 #define MOELORA_N_STAGES 7
 
 /* moe_lora_forward for measurement: additionally records stage_events[i] (caller-created
- * hipEvent_t handles, MOELORA_N_STAGES + 1 of them) on `stream` right before stage i and
+ * hipEvent_t handles, an array of MOELORA_N_STAGES + 1) on `stream` right before stage i and
  * stage_events[MOELORA_N_STAGES] after the last stage, so the elapsed time between events i
- * and i+1 is stage i. Same results and errors as moe_lora_forward; MOELORA_ENULL when
- * stage_events or one of its entries is NULL. With T = 0 no event is recorded. */
+ * and i+1 is stage i. A NULL entry is not recorded (each record adds a gap between launches,
+ * so a caller timing one stage passes only its two events). Same results and errors as
+ * moe_lora_forward; MOELORA_ENULL when stage_events is NULL. With T = 0 no event is
+ * recorded. */
 int moe_lora_forward_timed(const void *x, const float *router_logits, const void *W1,
                            const void *W2, const void *A1, const void *B1, const void *A2,
                            const void *B2, const int32_t *adapter_ids, int32_t topk,

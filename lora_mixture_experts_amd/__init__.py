@@ -124,8 +124,9 @@ def forward(x, router_logits, W1, W2, A1, B1, A2, B2, adapter_ids, topk: int, y=
             workspace=None, stage_events=None) -> torch.Tensor:
     """y[T][h] (bf16) of the fused MoE + multi-LoRA layer; see include/moelora.h.
 
-    stage_events: optional list of N_STAGES + 1 torch.cuda.Event(enable_timing=True) that the
-    library records at the stage boundaries on the current stream (moe_lora_forward_timed)."""
+    stage_events: optional list of N_STAGES + 1 torch.cuda.Event(enable_timing=True) (or None
+    for a boundary not to record) that the library records at the stage boundaries on the
+    current stream (moe_lora_forward_timed)."""
     d = dims_of(x, W1, A1)
     T, h, I, E, nA, r = d.T, d.hidden, d.inter, d.n_experts, d.n_adapters, d.rank
     bf = torch.bfloat16
@@ -152,9 +153,10 @@ def forward(x, router_logits, W1, W2, A1, B1, A2, B2, adapter_ids, topk: int, y=
         if len(stage_events) != N_STAGES + 1:
             raise ValueError(f"need {N_STAGES + 1} events")
         for ev in stage_events:
-            if not ev.cuda_event:  # torch creates the HIP event on its first record
+            if ev is not None and not ev.cuda_event:  # torch creates the HIP event on its first record
                 ev.record()
-        handles = (ctypes.c_void_p * (N_STAGES + 1))(*[ev.cuda_event for ev in stage_events])
+        handles = (ctypes.c_void_p * (N_STAGES + 1))(
+            *[ev.cuda_event if ev is not None else None for ev in stage_events])
         _check(lib().moe_lora_forward_timed(*args, handles), "moe_lora_forward_timed")
     return y
 

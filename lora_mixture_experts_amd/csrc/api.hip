@@ -284,7 +284,7 @@ namespace {
 
 // Records stage boundary i on the stream when the caller asked for timing events.
 bool mark(void* const* ev, int i, hipStream_t s) {
-  return !ev || hipEventRecord((hipEvent_t)ev[i], s) == hipSuccess;
+  return !ev || !ev[i] || hipEventRecord((hipEvent_t)ev[i], s) == hipSuccess;
 }
 
 int forward_impl(const void* x, const float* router_logits, const void* W1, const void* W2,
@@ -516,8 +516,6 @@ int moe_lora_forward_timed(const void* x, const float* router_logits, const void
                            const moe_lora_dims* d, void* y, void* workspace,
                            size_t workspace_bytes, void* stream, void* const* stage_events) {
   if (!stage_events) return MOELORA_ENULL;
-  for (int i = 0; i <= MOELORA_N_STAGES; ++i)
-    if (!stage_events[i]) return MOELORA_ENULL;
   return forward_impl(x, router_logits, W1, W2, A1, B1, A2, B2, adapter_ids, topk, d, y, workspace,
                       workspace_bytes, stream, stage_events);
 }
