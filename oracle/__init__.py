@@ -16,7 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moelora_oracle.c")
 _LIB = os.path.join(_HERE, "libmoelora_oracle.so")
 
-ORC_BF16, ORC_F32, ORC_F64 = 0, 1, 2
+ORC_BF16, ORC_F32, ORC_F64, ORC_FP8E4M3 = 0, 1, 2, 3
 
 
 def build() -> str:
@@ -45,15 +45,19 @@ def lib():
         L.oracle_route.argtypes = [P, i32, i32, i32, P, P]
         L.oracle_align.argtypes = [P, P, i32, i32, i32, i32, i32, i32, P, ctypes.c_int64, P, P, i32, P]
         L.oracle_forward.argtypes = [ctypes.POINTER(_Dims), P, P, P, P, P, i32, P, P]
+        L.oracle_forward_scaled.argtypes = [ctypes.POINTER(_Dims), P, P, P, P, P, P, P, i32, P, P]
+        L.oracle_fp8e4m3_decode.argtypes = [P, ctypes.c_int64, P]
         L.oracle_num_threads.argtypes = []
-        for f in (L.oracle_route, L.oracle_align, L.oracle_forward, L.oracle_num_threads):
+        for f in (L.oracle_route, L.oracle_align, L.oracle_forward, L.oracle_forward_scaled,
+                  L.oracle_fp8e4m3_decode, L.oracle_num_threads):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
 
 
 def _np(a):
-    """numpy view of a CPU array or torch tensor; bf16 comes back as uint16 bit patterns."""
+    """numpy view of a CPU array or torch tensor; bf16 comes back as uint16 bit patterns, E4M3
+    weight codes are uint8."""
     if hasattr(a, "detach"):
         import torch
         a = a.detach()
@@ -65,6 +69,8 @@ def _np(a):
     a = np.ascontiguousarray(a)
     if a.dtype == np.uint16:
         return a, ORC_BF16
+    if a.dtype == np.uint8:
+        return a, ORC_FP8E4M3
     if a.dtype == np.float32:
         return a, ORC_F32
     if a.dtype == np.float64:
@@ -127,7 +133,9 @@ def forward(inputs: dict, topk: int, tokens=None, return_pairs: bool = False):
 
     `inputs` holds x, logits, W1, W2, A1, B1, A2, B2, adapter_ids with the stored layouts
     x[T][h], W1[E][2I][h], W2[E][h][I], A1[nA][E][r][h], B1[nA][E][2I][r], A2[nA][E][r][I],
-    B2[nA][E][h][r]; each may be bf16, float32 or float64."""
+    B2[nA][E][h][r]; each may be bf16, float32 or float64. W1 and W2 may instead be uint8 E4M3
+    codes, with their per-row scales in inputs["W1_scale"] [E][2I] and inputs["W2_scale"]
+    [E][h] (float32)."""
     arrs = []
     dts = []
     for name in ("x", "W1", "W2", "A1", "B1", "A2", "B2"):
@@ -159,11 +167,31 @@ def forward(inputs: dict, topk: int, tokens=None, return_pairs: bool = False):
     dp = np.zeros((n, topk, h), np.float64) if return_pairs else None
     tptr = (ctypes.c_void_p * 7)(*[a.ctypes.data for a in arrs])
     dtarr = (ctypes.c_int32 * 7)(*dts)
-    rc = lib().oracle_forward(ctypes.byref(dims), tptr, dtarr, _ptr(L), _ptr(ad),
-                              None if toks is None else _ptr(toks), n, _ptr(y),
-                              None if dp is None else _ptr(dp))
+    scales = []
+    for name, shape in (("W1_scale", (E, 2 * I)), ("W2_scale", (E, h))):
+        sc = inputs.get(name)
+        if sc is None:
+            scales.append(None)
+            continue
+        sc, sdt = _np(sc)
+        if sdt != ORC_F32 or sc.shape != shape:
+            raise ValueError(f"{name} must be float32 {shape}")
+        scales.append(sc)
+    rc = lib().oracle_forward_scaled(ctypes.byref(dims), tptr, dtarr,
+                                     None if scales[0] is None else _ptr(scales[0]),
+                                     None if scales[1] is None else _ptr(scales[1]), _ptr(L),
+                                     _ptr(ad), None if toks is None else _ptr(toks), n, _ptr(y),
+                                     None if dp is None else _ptr(dp))
     _check(rc, "oracle_forward")
     return (y, dp) if return_pairs else y
+
+
+def fp8e4m3_decode(codes) -> np.ndarray:
+    """float64 values of uint8 E4M3 codes (any shape)."""
+    c = np.ascontiguousarray(np.asarray(codes, dtype=np.uint8))
+    out = np.empty(c.shape, np.float64)
+    _check(lib().oracle_fp8e4m3_decode(_ptr(c), c.size, _ptr(out)), "oracle_fp8e4m3_decode")
+    return out
 
 
 def num_threads() -> int:

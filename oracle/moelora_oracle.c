@@ -32,6 +32,13 @@
  *  x[T][h], logits[T][E] f32, W1[E][2I][h], W2[E][h][I], A1[nA][E][r][h], B1[nA][E][2I][r],
  *  A2[nA][E][r][I], B2[nA][E][h][r], adapter_ids[T].
  *
+ * FP8 expert weights (page "AWS SageMaker MoE kernel optimizations", third paragraph: FP8
+ * expert weights whose scales are applied between the routing and the expert GEMMs): W1 and
+ * W2 may be stored as 8-bit E4M3 codes (the OCP 8-bit floating point format: 1 sign bit,
+ * 4 exponent bits with bias 7, 3 mantissa bits, no infinities, S.1111.111 is NaN) with one
+ * float32 scale per output row (channel): W[e][n][c] = decode(code[e][n][c]) * scale[e][n]
+ * (a reading: the page names FP8 and scales, not their granularity).
+ *
  * Pins (tests/test_oracle_pins.py): brute-force top-k against Python's sort, the full softmax
  * at k = E, the merged-weight form x(W + AB), B = 0 reducing to plain MoE, one adapter for all
  * tokens matching per-token evaluation, E = 1 against numpy matmul, a hand-worked example
@@ -46,6 +53,7 @@
 #define ORC_BF16 0
 #define ORC_F32 1
 #define ORC_F64 2
+#define ORC_FP8E4M3 3 /* uint8 E4M3 codes; weights only, with per-row scales */
 
 #define ORC_OK 0
 #define ORC_EINVAL -1
@@ -64,10 +72,22 @@ static double bf16_to_f64(uint16_t b) {
   return (double)f;
 }
 
+/* OCP E4M3: (-1)^s * 2^(e-7) * (1 + m/8) for e > 0, (-1)^s * 2^-6 * (m/8) for e = 0; NaN for
+ * e = 15, m = 7 (the largest finite magnitude is 448). Exact in float64. */
+static double fp8e4m3_to_f64(uint8_t b) {
+  const int s = b >> 7, e = (b >> 3) & 15, m = b & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0) v = ldexp((double)m / 8.0, -6);
+  else v = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return s ? -v : v;
+}
+
 /* Element i of a stored tensor, widened exactly to float64. */
 static double ld(const void *p, int dt, size_t i) {
   if (dt == ORC_BF16) return bf16_to_f64(((const uint16_t *)p)[i]);
   if (dt == ORC_F32) return (double)((const float *)p)[i];
+  if (dt == ORC_FP8E4M3) return fp8e4m3_to_f64(((const uint8_t *)p)[i]);
   return ((const double *)p)[i];
 }
 
@@ -80,6 +100,9 @@ static double dot_row(const double *v, const void *M, int dt, size_t off, int le
   } else if (dt == ORC_F32) {
     const float *m = (const float *)M + off;
     for (int c = 0; c < len; ++c) s += v[c] * (double)m[c];
+  } else if (dt == ORC_FP8E4M3) {
+    const uint8_t *m = (const uint8_t *)M + off;
+    for (int c = 0; c < len; ++c) s += v[c] * fp8e4m3_to_f64(m[c]);
   } else {
     const double *m = (const double *)M + off;
     for (int c = 0; c < len; ++c) s += v[c] * m[c];
@@ -210,15 +233,19 @@ int oracle_align(const int32_t *topk_ids, const int32_t *adapter_ids, int32_t T,
  *   y[t][m] = sum_j w[t][j] d_j[m], in slot order.
  * With a = -1 the z terms are zero.
  * t[] holds the tensors in the order x, W1, W2, A1, B1, A2, B2 and dt[] their dtypes.
+ * oracle_forward_scaled also takes the per-row scales of W1 [E][2I] and W2 [E][h] (float32),
+ * required when that weight is stored as E4M3 codes (NULL otherwise): the row's sum is the
+ * sum over the decoded codes times the row's scale.
  * tokens/n_tokens select the output rows (NULL: all T tokens, in order). y is
  * [n_tokens][h]; d_pairs, when not NULL, receives the per-slot expert outputs
  * [n_tokens][k][h].
  * ------------------------------------------------------------------------------------------ */
 static double silu(double v) { return v / (1.0 + exp(-v)); }
 
-int oracle_forward(const orc_dims *d, const void *const *t, const int32_t *dt,
-                   const float *logits, const int32_t *adapter_ids, const int32_t *tokens,
-                   int32_t n_tokens, double *y, double *d_pairs) {
+int oracle_forward_scaled(const orc_dims *d, const void *const *t, const int32_t *dt,
+                          const float *w1_scale, const float *w2_scale, const float *logits,
+                          const int32_t *adapter_ids, const int32_t *tokens, int32_t n_tokens,
+                          double *y, double *d_pairs) {
   const int32_t T = d->T, h = d->hidden, I = d->inter, E = d->n_experts, nA = d->n_adapters,
                 r = d->rank, k = d->topk;
   if (T < 0 || h <= 0 || I <= 0 || E <= 0 || nA <= 0 || r <= 0 || k <= 0 || k > E)
@@ -226,6 +253,10 @@ int oracle_forward(const orc_dims *d, const void *const *t, const int32_t *dt,
   const void *x = t[0], *W1 = t[1], *W2 = t[2], *A1 = t[3], *B1 = t[4], *A2 = t[5], *B2 = t[6];
   const int dx = dt[0], dW1 = dt[1], dW2 = dt[2], dA1 = dt[3], dB1 = dt[4], dA2 = dt[5],
             dB2 = dt[6];
+  for (int i = 0; i < 7; ++i)
+    if (dt[i] == ORC_FP8E4M3 && i != 1 && i != 2) return ORC_EINVAL;
+  if ((dW1 == ORC_FP8E4M3) != (w1_scale != NULL) || (dW2 == ORC_FP8E4M3) != (w2_scale != NULL))
+    return ORC_EINVAL;
   int32_t n = tokens ? n_tokens : T;
   for (int32_t i = 0; i < n; ++i) {
     int32_t tok = tokens ? tokens[i] : i;
@@ -267,6 +298,7 @@ int oracle_forward(const orc_dims *d, const void *const *t, const int32_t *dt,
           }
           for (int32_t nn = 0; nn < 2 * I; ++nn) {
             double v = dot_row(xr, W1, dW1, ((size_t)e * 2 * I + nn) * h, h);
+            if (w1_scale) v *= (double)w1_scale[(size_t)e * 2 * I + nn];
             if (a >= 0) v += dot_row(z1, B1, dB1, (((size_t)a * E + e) * 2 * I + nn) * r, r);
             g[nn] = v;
           }
@@ -279,6 +311,7 @@ int oracle_forward(const orc_dims *d, const void *const *t, const int32_t *dt,
           }
           for (int32_t m = 0; m < h; ++m) {
             double v = dot_row(act, W2, dW2, ((size_t)e * h + m) * I, I);
+            if (w2_scale) v *= (double)w2_scale[(size_t)e * h + m];
             if (a >= 0) v += dot_row(z2, B2, dB2, (((size_t)a * E + e) * h + m) * r, r);
             dv[m] = v;
           }
@@ -298,6 +331,19 @@ int oracle_forward(const orc_dims *d, const void *const *t, const int32_t *dt,
     free(w);
   }
   return status;
+}
+
+int oracle_forward(const orc_dims *d, const void *const *t, const int32_t *dt,
+                   const float *logits, const int32_t *adapter_ids, const int32_t *tokens,
+                   int32_t n_tokens, double *y, double *d_pairs) {
+  return oracle_forward_scaled(d, t, dt, NULL, NULL, logits, adapter_ids, tokens, n_tokens, y,
+                               d_pairs);
+}
+
+/* E4M3 codes decoded to float64, for the tests. */
+int oracle_fp8e4m3_decode(const uint8_t *codes, int64_t n, double *out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = fp8e4m3_to_f64(codes[i]);
+  return ORC_OK;
 }
 
 /* Thread count the forward uses (OpenMP's default team size). */

@@ -98,6 +98,30 @@ def make_inputs(w: Workload, seed: int, device="cpu", dtype=torch.bfloat16, b_sc
     return d
 
 
+def quantize_rows_e4m3(W: torch.Tensor):
+    """FP8 expert weights for the layer's FP8 entry point: every output row (last dim = input)
+    gets the scale max|row| / 448 (448 is the largest E4M3 magnitude; an all-zero row gets 1),
+    and its values divided by the scale are rounded to E4M3 by torch (round to nearest even).
+    Returns (codes uint8, same shape; scales float32, shape without the last dim). Input
+    preparation only: both the kernels and the oracle receive the codes and scales as given."""
+    Wf = W.float()
+    amax = Wf.abs().amax(dim=-1)
+    scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax)).float()
+    codes = (Wf / scale.unsqueeze(-1)).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes.contiguous(), scale.contiguous()
+
+
+def make_inputs_fp8(w: Workload, seed: int, device="cpu", b_scale: float = 1.0) -> dict:
+    """make_inputs with W1 and W2 replaced by E4M3 codes and per-row scales (W1_scale [E][2I],
+    W2_scale [E][h]); the other tensors are bf16 as in make_inputs."""
+    d = make_inputs(w, seed, device=device, b_scale=b_scale)
+    for name in ("W1", "W2"):
+        codes, scale = quantize_rows_e4m3(d[name])
+        d[name] = codes
+        d[name + "_scale"] = scale
+    return d
+
+
 def input_bytes(w: Workload) -> int:
     n = w.T * w.hidden * 2 + w.T * w.n_experts * 4 + w.T * 4
     for shp in WEIGHT_SHAPES.values():

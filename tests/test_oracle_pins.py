@@ -292,3 +292,59 @@ def test_forward_rejects_bad_adapter_and_logits():
     bad["logits"][0, 0] = np.inf
     with pytest.raises(oracle.OracleError):
         oracle.forward(bad, w.topk)
+
+
+# ----------------------------------------------------------------------------- FP8 weights
+
+# Values the OCP 8-bit floating point format fixes for E4M3 (bias 7, 3 mantissa bits, no
+# infinities): zeros, the smallest subnormal 2^-9, the largest subnormal 7 * 2^-9, the smallest
+# normal 2^-6, 1, 2, the largest finite 448, and the NaN encodings S.1111.111.
+FP8_SPEC = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0,
+            0x40: 2.0, 0x39: 1.125, 0x3F: 1.875, 0x7E: 448.0, 0x80: -0.0, 0xB8: -1.0,
+            0xFE: -448.0}
+
+
+def test_fp8_decode_spec_values():
+    v = oracle.fp8e4m3_decode(np.arange(256))
+    for code, want in FP8_SPEC.items():
+        assert v[code] == want and np.signbit(v[code]) == np.signbit(want), hex(code)
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF]) and int(np.isnan(v).sum()) == 2
+    pos = v[:0x7F]
+    assert np.all(np.diff(pos) > 0), "codes 0x00..0x7E increase"
+    assert np.array_equal(v[0x80:0xFF], -v[0x00:0x7F])
+
+
+def test_fp8_decode_matches_torch():
+    codes = torch.arange(256, dtype=torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    v = oracle.fp8e4m3_decode(codes.numpy())
+    same = (v == ref) | (np.isnan(v) & np.isnan(ref))
+    assert same.all()
+
+
+def test_fp8_forward_equals_dequantized_weights():
+    """The E4M3 reader (codes times per-row scales) against the float64 path on the decoded
+    weights, which the pins above already fix."""
+    w = configs.Workload("fp8_tiny", 12, 256, 384, 6, 2, 3, 16)
+    d = configs.make_inputs_fp8(w, 5)
+    deq = dict(d)
+    for name in ("W1", "W2"):
+        deq[name] = oracle.fp8e4m3_decode(d[name].numpy()) * d[name + "_scale"].double().numpy()[..., None]
+        del deq[name + "_scale"]
+    y8 = oracle.forward(d, w.topk)
+    y64 = oracle.forward(deq, w.topk)
+    np.testing.assert_allclose(y8, y64, rtol=1e-12, atol=1e-15 * np.abs(y64).max())
+    assert np.abs(y64).max() > 0
+
+
+def test_fp8_quantized_rows_reproduce_weights():
+    """The input preparation: decoded codes times the row scale stay within one E4M3 rounding
+    (relative 2^-4) of the bf16 weights, and every row's largest magnitude maps to 448."""
+    w = configs.Workload("fp8_q", 4, 128, 128, 3, 1, 2, 8)
+    W = configs.make_inputs(w, 1)["W1"]
+    codes, scale = configs.quantize_rows_e4m3(W)
+    back = oracle.fp8e4m3_decode(codes.numpy()) * scale.double().numpy()[..., None]
+    Wf = W.double().numpy()
+    err = np.abs(back - Wf)
+    assert np.all(err <= 2.0 ** -4 * np.abs(Wf) + 2.0 ** -9 * scale.double().numpy()[..., None])
+    assert np.all(np.abs(oracle.fp8e4m3_decode(codes.numpy())).max(axis=-1) == 448.0)
