@@ -5,7 +5,10 @@ One step = one call of moe_lora_forward (route, align, LoRA shrink, gate_up GEMM
 expand and SiLU-and-mul, LoRA shrink, down GEMM with LoRA expand, combine) over one batch of
 seeded synthetic input already resident in HBM. Prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode] [--fp8]
+
+--fp8 runs the FP8 entry point (E4M3 expert weights with per-row scales, moe_lora_forward_fp8)
+on the decode-sized workloads (decode, fg, tiny).
 """
 from __future__ import annotations
 
@@ -24,10 +27,11 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 
 
-def algorithmic_work(w, seg_table, n_seg, topk_ids):
+def algorithmic_work(w, seg_table, n_seg, topk_ids, fp8: bool = False):
     """Bytes and flops the method must move / compute for this routing (no padding, no
     intermediates): touched expert weights, touched (expert, adapter) LoRA weights, x,
-    logits, adapter ids, y. Also the gate_up kernel's own share."""
+    logits, adapter ids, y. Also the gate_up kernel's own share. With fp8 the expert weights
+    are 1 byte each plus a 4-byte scale per weight row."""
     import numpy as np
     ids = topk_ids.cpu().numpy()
     seg = seg_table.cpu().numpy()[:n_seg]
@@ -36,10 +40,12 @@ def algorithmic_work(w, seg_table, n_seg, topk_ids):
     n_ea = int((seg[:, 1] >= 0).sum())  # (expert, adapter) segments that carry an adapter
     P = T * k
     pairs_with_adapter = int(seg[seg[:, 1] >= 0, 3].sum())
-    layer_bytes = (n_exp * 3 * h * I * 2 + n_ea * r * (2 * h + 3 * I) * 2
+    wb = 1 if fp8 else 2  # bytes per expert weight
+    sc = 4 if fp8 else 0   # scale bytes per weight row
+    layer_bytes = (n_exp * (3 * h * I * wb + (2 * I + h) * sc) + n_ea * r * (2 * h + 3 * I) * 2
                    + 2 * T * h + 4 * T * E + 4 * T + 2 * T * h)
     layer_flops = 2 * P * 3 * h * I + 2 * pairs_with_adapter * r * (2 * h + 3 * I)
-    gateup_bytes = (n_exp * 2 * I * h * 2 + n_ea * 2 * I * r * 2 + 2 * T * h + 2 * P * I
+    gateup_bytes = (n_exp * 2 * I * (h * wb + sc) + n_ea * 2 * I * r * 2 + 2 * T * h + 2 * P * I
                     + 4 * pairs_with_adapter * r)
     gateup_flops = 2 * P * 2 * I * h + 2 * pairs_with_adapter * 2 * I * r
     return dict(n_experts_touched=n_exp, n_expert_adapter=n_ea, layer_bytes=layer_bytes,
@@ -91,6 +97,9 @@ def cpu_baseline(w, inp, n_tokens: int, min_seconds: float):
     host = {"x": inp["x"].index_select(0, tok_t).cpu(), "logits": inp["logits"].index_select(0, tok_t).cpu(),
             "adapter_ids": np.array([remap.get(int(a), -1) for a in ad], np.int32),
             "W1": inp["W1"].cpu(), "W2": inp["W2"].cpu()}
+    for n in ("W1_scale", "W2_scale"):
+        if n in inp:
+            host[n] = inp[n].cpu()
     for n in ("A1", "B1", "A2", "B2"):
         host[n] = inp[n].index_select(0, used_t).cpu()
     passes = 0
@@ -119,6 +128,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the oracle over its sample for at least this long")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fp8", action="store_true",
+                    help="E4M3 expert weights with per-row scales (decode-sized workloads)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run a device-to-device copy of this size first (counter calibration)")
     args = ap.parse_args()
@@ -148,18 +159,26 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    inp = configs.make_inputs(w, args.seed, device=dev)
-    d = ml.dims_of(inp["x"], inp["W1"], inp["A1"])
+    if args.fp8 and w.T * w.topk > 24 * w.n_experts:
+        print("--fp8 covers workloads of at most 24 token-expert pairs per expert", file=sys.stderr)
+        sys.exit(2)
+    inp = (configs.make_inputs_fp8 if args.fp8 else configs.make_inputs)(w, args.seed, device=dev)
+    d = ml.Dims(w.T, w.hidden, w.inter, w.n_experts, w.n_adapters, w.rank)
     ws = ml.new_workspace(d, w.topk, dev)
     y = torch.empty((w.T, w.hidden), dtype=torch.bfloat16, device=dev)
 
     ra = ml.route_align(inp["logits"], inp["adapter_ids"], w.topk, d, 1, 1, workspace=ws)
-    work = algorithmic_work(w, ra["seg_table"], int(ra["n_seg"].item()), ra["topk_ids"])
+    work = algorithmic_work(w, ra["seg_table"], int(ra["n_seg"].item()), ra["topk_ids"], args.fp8)
     del ra
 
     def step(events=None):
-        ml.forward(inp["x"], inp["logits"], inp["W1"], inp["W2"], inp["A1"], inp["B1"], inp["A2"],
-                   inp["B2"], inp["adapter_ids"], w.topk, y=y, workspace=ws, stage_events=events)
+        if args.fp8:
+            ml.forward_fp8(inp["x"], inp["logits"], inp["W1"], inp["W1_scale"], inp["W2"],
+                           inp["W2_scale"], inp["A1"], inp["B1"], inp["A2"], inp["B2"],
+                           inp["adapter_ids"], w.topk, y=y, workspace=ws, stage_events=events)
+        else:
+            ml.forward(inp["x"], inp["logits"], inp["W1"], inp["W2"], inp["A1"], inp["B1"], inp["A2"],
+                       inp["B2"], inp["adapter_ids"], w.topk, y=y, workspace=ws, stage_events=events)
 
     for _ in range(args.warmup):
         step()
@@ -211,7 +230,7 @@ def main():
     # the library takes the LDS-tiled GEMM above 24 rows per expert on average
     tiled = w.T * w.topk > 24 * w.n_experts
     roof["kernel"] = ("tiled_gemm_kernel" if tiled else "skinny_gemm_kernel") + " (gate_up)"
-    roof["traffic"] = measured_traffic(args.workload)
+    roof["traffic"] = measured_traffic(args.workload + ("_fp8" if args.fp8 else ""))
 
     layer_s = elapsed / K
     out = {
@@ -225,11 +244,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8-e4m3 expert weights, bf16 activations" if args.fp8 else "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "hidden": w.hidden, "inter": w.inter,
                    "n_experts": w.n_experts, "topk": w.topk, "n_adapters": w.n_adapters,
-                   "rank": w.rank, "adapters": w.adapters, "seed": args.seed},
+                   "rank": w.rank, "adapters": w.adapters, "seed": args.seed,
+                   "expert_weights": "e4m3 + per-row fp32 scale" if args.fp8 else "bf16"},
         "roofline": roof,
         "layer": {"bytes": work["layer_bytes"], "flops": work["layer_flops"],
                   "ms": layer_s * 1e3,

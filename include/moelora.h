@@ -55,6 +55,7 @@ extern "C" {
 #define MOELORA_EWORKSPACE (-4)  /* workspace too small or misaligned (256-byte alignment) */
 #define MOELORA_EHIP (-5)        /* a HIP launch or runtime call failed */
 #define MOELORA_EDEVICE (-6)     /* the current device is not gfx950 */
+#define MOELORA_EUNSUPPORTED (-7) /* FP8 weights with more than 24 token-expert pairs per expert */
 
 /* Device-side flags reported by moe_lora_debug_status. */
 #define MOELORA_FLAG_NONFINITE_LOGIT 1u
@@ -100,6 +101,23 @@ int moe_lora_forward_timed(const void *x, const float *router_logits, const void
                            const void *B2, const int32_t *adapter_ids, int32_t topk,
                            const moe_lora_dims *d, void *y, void *workspace,
                            size_t workspace_bytes, void *stream, void *const *stage_events);
+
+/* moe_lora_forward with FP8 expert weights (page "AWS SageMaker MoE kernel optimizations",
+ * third paragraph: FP8 expert weights, their scales applied on the way into the expert
+ * GEMMs). W1q [E][2I][h] and W2q [E][h][I] hold OCP E4M3 codes (1 byte each: sign, 4 exponent
+ * bits with bias 7, 3 mantissa bits; no infinities) and W1_scale [E][2I], W2_scale [E][h] one
+ * float32 per weight row: weight = decode(code) * scale. Everything else (x, the LoRA weights,
+ * y, the workspace and its size) is as in moe_lora_forward, device pointers, caller-owned.
+ * The codes are 16-byte aligned, the scales 4-byte aligned. The FP8 path covers the
+ * weight-streaming regime (at most 24 token-expert pairs per expert on average, T*topk <=
+ * 24*n_experts): larger batches return MOELORA_EUNSUPPORTED before any device work.
+ * stage_events, when not NULL, is as in moe_lora_forward_timed. */
+int moe_lora_forward_fp8(const void *x, const float *router_logits, const void *W1q,
+                         const float *W1_scale, const void *W2q, const float *W2_scale,
+                         const void *A1, const void *B1, const void *A2, const void *B2,
+                         const int32_t *adapter_ids, int32_t topk, const moe_lora_dims *d,
+                         void *y, void *workspace, size_t workspace_bytes, void *stream,
+                         void *const *stage_events);
 
 /* Upper bound on the padded sorted-pair length for (seg_pad, block_m):
  * T*topk*seg_pad + n_experts*(block_m-1), or -1 for invalid arguments. */

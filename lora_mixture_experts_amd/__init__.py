@@ -16,10 +16,10 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoelora.so")
 
-OK, EINVAL_DIMS, ENULL, EALIGN, EWORKSPACE, EHIP, EDEVICE = 0, -1, -2, -3, -4, -5, -6
+OK, EINVAL_DIMS, ENULL, EALIGN, EWORKSPACE, EHIP, EDEVICE, EUNSUPPORTED = 0, -1, -2, -3, -4, -5, -6, -7
 FLAG_NONFINITE_LOGIT, FLAG_ADAPTER_RANGE = 1, 2
 
-EXPORTS = ("moe_lora_workspace_size", "moe_lora_forward", "moe_lora_forward_timed",
+EXPORTS = ("moe_lora_workspace_size", "moe_lora_forward", "moe_lora_forward_timed", "moe_lora_forward_fp8",
            "moe_lora_sorted_capacity", "moe_lora_route_align", "moe_lora_strerror",
            "moe_lora_debug_status")
 N_STAGES = 7
@@ -55,6 +55,9 @@ def lib() -> ctypes.CDLL:
         L.moe_lora_forward_timed.argtypes = [P, P, P, P, P, P, P, P, P, i32, D, P, P, ctypes.c_size_t, P,
                                              ctypes.POINTER(ctypes.c_void_p)]
         L.moe_lora_forward_timed.restype = ctypes.c_int
+        L.moe_lora_forward_fp8.argtypes = [P, P, P, P, P, P, P, P, P, P, P, i32, D, P, P, ctypes.c_size_t, P,
+                                           ctypes.POINTER(ctypes.c_void_p)]
+        L.moe_lora_forward_fp8.restype = ctypes.c_int
         L.moe_lora_sorted_capacity.argtypes = [D, i32, i32, i32]
         L.moe_lora_sorted_capacity.restype = i64
         L.moe_lora_route_align.argtypes = [P, P, i32, D, i32, i32, P, P, P, i64, P, P, P, P,
@@ -158,6 +161,50 @@ def forward(x, router_logits, W1, W2, A1, B1, A2, B2, adapter_ids, topk: int, y=
         handles = (ctypes.c_void_p * (N_STAGES + 1))(
             *[ev.cuda_event if ev is not None else None for ev in stage_events])
         _check(lib().moe_lora_forward_timed(*args, handles), "moe_lora_forward_timed")
+    return y
+
+
+def forward_fp8(x, router_logits, W1q, W1_scale, W2q, W2_scale, A1, B1, A2, B2, adapter_ids,
+                topk: int, y=None, workspace=None, stage_events=None) -> torch.Tensor:
+    """forward with E4M3 expert weights (moe_lora_forward_fp8): W1q [E][2I][h] and W2q [E][h][I]
+    as uint8 codes, W1_scale [E][2I] and W2_scale [E][h] float32 per-row scales; the rest as
+    in forward. Raises MoeLoraError(EUNSUPPORTED) above 24 token-expert pairs per expert."""
+    T, h = x.shape
+    E, twoI, _ = W1q.shape
+    nA, _, r, _ = A1.shape
+    I = twoI // 2
+    d = Dims(T, h, I, E, nA, r)
+    bf = torch.bfloat16
+    _expect(x, "x", bf, (T, h))
+    _expect(router_logits, "router_logits", torch.float32, (T, E))
+    _expect(W1q, "W1q", torch.uint8, (E, 2 * I, h))
+    _expect(W1_scale, "W1_scale", torch.float32, (E, 2 * I))
+    _expect(W2q, "W2q", torch.uint8, (E, h, I))
+    _expect(W2_scale, "W2_scale", torch.float32, (E, h))
+    _expect(A1, "A1", bf, (nA, E, r, h))
+    _expect(B1, "B1", bf, (nA, E, 2 * I, r))
+    _expect(A2, "A2", bf, (nA, E, r, I))
+    _expect(B2, "B2", bf, (nA, E, h, r))
+    _expect(adapter_ids, "adapter_ids", torch.int32, (T,))
+    if y is None:
+        y = torch.empty((T, h), dtype=bf, device=x.device)
+    _expect(y, "y", bf, (T, h))
+    if workspace is None:
+        workspace = new_workspace(d, topk, x.device)
+    handles = None
+    if stage_events is not None:
+        if len(stage_events) != N_STAGES + 1:
+            raise ValueError(f"need {N_STAGES + 1} events")
+        for ev in stage_events:
+            if ev is not None and not ev.cuda_event:
+                ev.record()
+        handles = (ctypes.c_void_p * (N_STAGES + 1))(
+            *[ev.cuda_event if ev is not None else None for ev in stage_events])
+    _check(lib().moe_lora_forward_fp8(_ptr(x), _ptr(router_logits), _ptr(W1q), _ptr(W1_scale),
+                                      _ptr(W2q), _ptr(W2_scale), _ptr(A1), _ptr(B1), _ptr(A2),
+                                      _ptr(B2), _ptr(adapter_ids), topk, ctypes.byref(d), _ptr(y),
+                                      _ptr(workspace), workspace.numel(), _stream(x.device), handles),
+           "moe_lora_forward_fp8")
     return y
 
 

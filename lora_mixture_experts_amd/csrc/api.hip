@@ -274,6 +274,7 @@ const char* moe_lora_strerror(int code) {
     case MOELORA_EWORKSPACE: return "workspace too small or not 256-byte aligned";
     case MOELORA_EHIP: return "HIP launch or runtime error";
     case MOELORA_EDEVICE: return "current device is not gfx950";
+    case MOELORA_EUNSUPPORTED: return "FP8 weights take at most 24 token-expert pairs per expert";
     default: return "unknown error code";
   }
 }
@@ -287,18 +288,25 @@ bool mark(void* const* ev, int i, hipStream_t s) {
   return !ev || !ev[i] || hipEventRecord((hipEvent_t)ev[i], s) == hipSuccess;
 }
 
+// w1_scale/w2_scale != nullptr: W1/W2 are E4M3 codes with per-row scales (skinny path only)
 int forward_impl(const void* x, const float* router_logits, const void* W1, const void* W2,
                  const void* A1, const void* B1, const void* A2, const void* B2,
                  const int32_t* adapter_ids, int32_t topk, const moe_lora_dims* d, void* y,
-                 void* workspace, size_t workspace_bytes, void* stream_, void* const* ev) {
+                 void* workspace, size_t workspace_bytes, void* stream_, void* const* ev,
+                 const float* w1_scale = nullptr, const float* w2_scale = nullptr) {
   int rc = validate_dims(d, topk);
   if (rc != MOELORA_OK) return rc;
+  const bool fp8 = w1_scale != nullptr || w2_scale != nullptr;
+  if (fp8 && pick_path((int64_t)d->T * topk, d->n_experts, d->hidden, d->inter).tiled)
+    return MOELORA_EUNSUPPORTED;
   if (d->T == 0) return MOELORA_OK;  // empty batch: nothing to do, pointers may be NULL
   const void* ptrs[] = {x, router_logits, W1, W2, A1, B1, A2, B2, adapter_ids, y, workspace};
   for (const void* p : ptrs)
     if (!p) return MOELORA_ENULL;
   for (const void* p : ptrs)
     if (!aligned16(p)) return MOELORA_EALIGN;
+  if (fp8 && (!w1_scale || !w2_scale)) return MOELORA_ENULL;
+  if (fp8 && ((((uintptr_t)w1_scale) | ((uintptr_t)w2_scale)) & 3u) != 0) return MOELORA_EALIGN;
   if (((uintptr_t)workspace & 255u) != 0) return MOELORA_EWORKSPACE;
   MoeLoraLayout L;
   moelora_make_layout(d->T, d->hidden, d->inter, d->n_experts, d->n_adapters, d->rank, topk, &L);
@@ -436,12 +444,21 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   g.X = (const uint16_t*)x;
   g.x_bytes = (uint32_t)((size_t)T * h * 2);
   g.W = (const uint16_t*)W1;
+  g.W8 = (const uint8_t*)W1;
+  g.wscale = w1_scale;
   g.Bw = (const uint16_t*)B1;
   g.zsum = zsum;
   g.zhl = zhl;
   g.K = h;
   g.N = I;
   SkinnyPlan plan = pick_skinny(nt, h, I);
+  if (fp8) {
+    // E4M3 rows carry half the bytes per K element: 128-wide K steps keep the bf16 kernels'
+    // bytes in flight per load (measured: decode gate_up 0.35 -> 0.31 ms); down on 32-row
+    // blocks (short K loops of many experts) keeps 64-wide steps
+    plan.gu.p = 4;
+    plan.dn.p = nt == 1 ? 4 : 2;
+  }
   if (path.tiled) {
     // tiled down: split K in two when the tiles would fill the chip fewer than four times (the
     // last, partial round of 256x256 tiles then costs a large share of the time)
@@ -459,7 +476,7 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   g.d_split_stride = L.cap * (int64_t)h;
   g.n_col_tiles = g.N / (plan.gu.split ? 32 : 64 * plan.gu.rt);
   const hipError_t gu_err = path.tiled ? launch_tiled(path.tc, true, g, stream)
-                                       : launch_skinny(plan.gu, true, g, max_blocks, stream);
+                                       : launch_skinny(plan.gu, true, g, max_blocks, stream, fp8);
   if (gu_err != hipSuccess) return MOELORA_EHIP;
   if (!mark(ev, 4, stream)) return MOELORA_EHIP;
 
@@ -480,13 +497,15 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   g.X = act;
   g.x_bytes = (uint32_t)((size_t)L.cap * I * 2);
   g.W = (const uint16_t*)W2;
+  g.W8 = (const uint8_t*)W2;
+  g.wscale = w2_scale;
   g.Bw = (const uint16_t*)B2;
   g.K = I;
   g.N = h;
   g.ksplit = plan.ksplit;
   g.n_col_tiles = g.N / (64 * plan.dn.rt);
   const hipError_t dn_err = path.tiled ? launch_tiled(path.tc_dn, false, g, stream)
-                                       : launch_skinny(plan.dn, false, g, max_blocks, stream);
+                                       : launch_skinny(plan.dn, false, g, max_blocks, stream, fp8);
   if (dn_err != hipSuccess) return MOELORA_EHIP;
   if (!mark(ev, 6, stream)) return MOELORA_EHIP;
 
@@ -518,6 +537,20 @@ int moe_lora_forward_timed(const void* x, const float* router_logits, const void
   if (!stage_events) return MOELORA_ENULL;
   return forward_impl(x, router_logits, W1, W2, A1, B1, A2, B2, adapter_ids, topk, d, y, workspace,
                       workspace_bytes, stream, stage_events);
+}
+
+int moe_lora_forward_fp8(const void* x, const float* router_logits, const void* W1q,
+                         const float* W1_scale, const void* W2q, const float* W2_scale,
+                         const void* A1, const void* B1, const void* A2, const void* B2,
+                         const int32_t* adapter_ids, int32_t topk, const moe_lora_dims* d,
+                         void* y, void* workspace, size_t workspace_bytes, void* stream,
+                         void* const* stage_events) {
+  if (!W1_scale || !W2_scale) {
+    const int rc = validate_dims(d, topk);
+    return rc != MOELORA_OK ? rc : MOELORA_ENULL;
+  }
+  return forward_impl(x, router_logits, W1q, W2q, A1, B1, A2, B2, adapter_ids, topk, d, y,
+                      workspace, workspace_bytes, stream, stage_events, W1_scale, W2_scale);
 }
 
 int moe_lora_route_align(const float* router_logits, const int32_t* adapter_ids, int32_t topk,

@@ -27,6 +27,22 @@
 
 namespace moelora {
 
+// Eight E4M3 codes (half `hi` of the 16 in v, bytes in K order) as one bf16 MFMA operand. The
+// hardware conversion decodes the OCP E4M3 format into float32; the bf16 is its upper half
+// (exact, as E4M3 has 3 mantissa bits and a narrower exponent range).
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16(u32x4 v, int hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const uint32_t d0 = hi ? v.z : v.x, d1 = hi ? v.w : v.y;
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)d0, false);
+  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)d0, true);
+  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)d1, false);
+  const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)d1, true);
+  auto pack = [](f32x2 f) {
+    return __builtin_amdgcn_perm(__float_as_uint(f.y), __float_as_uint(f.x), 0x07060302u);
+  };
+  return u32x4{pack(a), pack(b), pack(c), pack(d)};
+}
+
 // LoRA expand of the block, as MFMAs added onto the base accumulators: for every adapter run
 // (the distinct adapters of the block's live rows; the sorted layout keeps one expert's rows of
 // one adapter contiguous), acc[t][nt] += B_t z^T, where B_t holds the 16 weight rows of output
@@ -137,9 +153,16 @@ __device__ __forceinline__ void lora_mfma(f32x4 (&acc)[NW][NT], const int (&brow
 // otherwise each step loads then computes and latency is hidden by other wavefronts only.
 // SPLIT (gate_up only, RT = 1): waves 0-1 stream gate rows and waves 2-3 the matching up rows,
 // one weight tile per wave; the up accumulators reach the gate waves through LDS.
-template <int NT, bool GATEUP, int P, int RT, bool PIPE, bool SPLIT>
+// FP8: the weights are E4M3 codes (a.W8) with one float32 scale per output row (a.wscale).
+// Each 16-byte load of a row brings the codes of two of the token rows' 8-element K chunks;
+// they become bf16 in registers just before their MFMAs (exact: every E4M3 value is a bf16),
+// and each accumulator row is multiplied by its row's scale after the main loop, before the
+// LoRA term (bf16 weights, unscaled) is added.
+template <int NT, bool GATEUP, int P, int RT, bool PIPE, bool SPLIT, bool FP8 = false>
 __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs a) {
   static_assert(!SPLIT || (GATEUP && RT == 1), "SPLIT is a gate_up mode with one tile per wave");
+  static_assert(!FP8 || (P % 2 == 0 && !SPLIT), "FP8 rows come in 16-byte pairs of K chunks");
+  constexpr int PW = FP8 ? P / 2 : P;  // weight loads per lane, row and K step
   constexpr int NW = SPLIT ? 1 : (GATEUP ? 2 : 1) * RT;
   constexpr int BM = 16 * NT;
   constexpr int KS = 32 * P;
@@ -199,18 +222,31 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs a) {
   const int nks = K / KS;
   const int ks0 = (nks * zsplit) / a.ksplit, ks1 = (nks * (zsplit + 1)) / a.ksplit;
 
-  const uint16_t* wp[NW];
+  // weight row of tile w for this lane's MFMA row (m), and the first of the 4 accumulator rows
+  // it holds (4 kq)
+  size_t wrow[NW];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     if (SPLIT) {
-      wp[0] = a.W + ((size_t)e * 2 * N + (up_wave ? N : 0) + n0 + m) * K;
+      wrow[0] = (size_t)e * 2 * N + (up_wave ? N : 0) + n0;
     } else if (GATEUP) {
-      wp[rt] = a.W + ((size_t)e * 2 * N + n0 + 16 * rt + m) * K;
-      wp[NW - RT + rt] = a.W + ((size_t)e * 2 * N + N + n0 + 16 * rt + m) * K;
+      wrow[rt] = (size_t)e * 2 * N + n0 + 16 * rt;
+      wrow[NW - RT + rt] = (size_t)e * 2 * N + N + n0 + 16 * rt;
     } else {
-      wp[rt] = a.W + ((size_t)e * N + n0 + 16 * rt + m) * K;
+      wrow[rt] = (size_t)e * N + n0 + 16 * rt;
     }
   }
+  // (bf16 rows: K elements of 2 bytes; E4M3 rows: K bytes)
+  const uint8_t* wp[NW];
+#pragma unroll
+  for (int w = 0; w < NW; ++w)
+    wp[w] = FP8 ? a.W8 + (wrow[w] + m) * K : reinterpret_cast<const uint8_t*>(a.W + (wrow[w] + m) * K);
+  // FP8: the scales of the 4 accumulator rows of each tile, fetched ahead of the main loop
+  float wsc[NW][4];
+#pragma unroll
+  for (int w = 0; w < NW; ++w)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) wsc[w][v] = FP8 ? a.wscale[wrow[w] + 4 * kq + v] : 1.f;
 
   f32x4 acc[NW][NT];
 #pragma unroll
@@ -222,12 +258,12 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs a) {
   // are in flight. Loads are never conditional: past the last step they re-read the last step
   // (L2 hits, results unused), so the compiler's outstanding-load count stays exact and its
   // wait before each compute covers only the older set.
-  u32x4 wa[NW][P], xa[NT][P], wb[NW][P], xb[NT][P];
+  u32x4 wa[NW][PW], xa[NT][P], wb[NW][PW], xb[NT][P];
 #define MOELORA_LOAD(W_, X_, KB_)                                              \
   do {                                                                         \
     _Pragma("unroll") for (int w = 0; w < NW; ++w)                             \
-      _Pragma("unroll") for (int j = 0; j < P; ++j)                            \
-        W_[w][j] = ldg16(wp[w] + (KB_) + 8 * j);                               \
+      _Pragma("unroll") for (int j = 0; j < PW; ++j)                           \
+        W_[w][j] = ldg16(wp[w] + (FP8 ? 1 : 2) * ((KB_) + (FP8 ? 16 : 8) * j)); \
     _Pragma("unroll") for (int nt = 0; nt < NT; ++nt)                          \
       _Pragma("unroll") for (int j = 0; j < P; ++j)                            \
         X_[nt][j] = bufld16(xr, xo[nt] + 2u * (uint32_t)((KB_) + 8 * j));      \
@@ -235,9 +271,11 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs a) {
 #define MOELORA_COMPUTE(W_, X_)                                                \
   do {                                                                         \
     _Pragma("unroll") for (int j = 0; j < P; ++j)                              \
-      _Pragma("unroll") for (int w = 0; w < NW; ++w)                           \
+      _Pragma("unroll") for (int w = 0; w < NW; ++w) {                         \
+        const u32x4 wv = FP8 ? e4m3x8_to_bf16(W_[w][j / 2], j % 2) : W_[w][j % PW]; \
         _Pragma("unroll") for (int nt = 0; nt < NT; ++nt)                      \
-          acc[w][nt] = mfma16(W_[w][j], X_[nt][j], acc[w][nt]);                \
+          acc[w][nt] = mfma16(wv, X_[nt][j], acc[w][nt]);                      \
+      }                                                                        \
   } while (0)
   const int nsteps = ks1 - ks0;
   if (!PIPE || nsteps == 0) z_prologue();
@@ -268,7 +306,15 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs a) {
 #undef MOELORA_COMPUTE
 
   // Epilogue: lane holds weight rows n0 + 16*rt + 4*kq + v (v < 4) for token row (lane % 16).
-  // The LoRA term first (down: K split 0 only), onto the accumulators.
+  if (FP8) {
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[w][nt][v] *= wsc[w][v];
+  }
+  // The LoRA term (down: K split 0 only), onto the accumulators.
   if (zsplit == 0) {
     int brow[NW];
 #pragma unroll
@@ -327,7 +373,7 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs a) {
 }
 
 hipError_t launch_skinny(const SkinnyConfig& c, bool gateup, const GemmArgs& a, int grid_y,
-                         hipStream_t stream) {
+                         hipStream_t stream, bool fp8) {
   const bool split = gateup && c.split;
   const int cols_per_wg = split ? 32 : 4 * 16 * c.rt;
   if (a.N % cols_per_wg != 0) return hipErrorInvalidValue;  // every wavefront has columns
@@ -338,6 +384,27 @@ hipError_t launch_skinny(const SkinnyConfig& c, bool gateup, const GemmArgs& a, 
   // rounded up to the 8 XCDs (the kernel maps its id onto the live items)
   const int total = ((grid_y * ncol) + 7) / 8 * 8;
   dim3 grid(total, 1, gateup ? 1 : a.ksplit), block(256);
+#define MOELORA_SKINNY_FP8(NT_, P_, RT_)                                                          \
+  if (c.nt == NT_ && c.p == P_ && c.rt == RT_ && c.pipe == 1 && !split && fp8) {                  \
+    if (gateup)                                                                                   \
+      hipLaunchKernelGGL((skinny_gemm_kernel<NT_, true, P_, RT_, true, false, true>), grid, block, \
+                         0, stream, a);                                                           \
+    else                                                                                          \
+      hipLaunchKernelGGL((skinny_gemm_kernel<NT_, false, P_, RT_, true, false, true>), grid,      \
+                         block, 0, stream, a);                                                    \
+    return hipGetLastError();                                                                     \
+  }
+  // E4M3 weights (16- and 32-row blocks; 64- and 128-wide K steps)
+  MOELORA_SKINNY_FP8(1, 2, 1)
+  MOELORA_SKINNY_FP8(1, 2, 2)
+  MOELORA_SKINNY_FP8(2, 2, 1)
+  MOELORA_SKINNY_FP8(2, 2, 2)
+  MOELORA_SKINNY_FP8(1, 4, 1)
+  MOELORA_SKINNY_FP8(1, 4, 2)
+  MOELORA_SKINNY_FP8(2, 4, 1)
+  MOELORA_SKINNY_FP8(2, 4, 2)
+  if (fp8) return hipErrorInvalidValue;
+#undef MOELORA_SKINNY_FP8
 #define MOELORA_SKINNY(NT_, P_, RT_, PIPE_)                                                       \
   if (c.nt == NT_ && c.p == P_ && c.rt == RT_ && c.pipe == PIPE_ && !split) {                     \
     if (gateup)                                                                                   \

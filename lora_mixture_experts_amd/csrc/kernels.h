@@ -84,6 +84,8 @@ struct GemmArgs {
   const uint16_t* X;   // gate_up: x [T][K]; down: act [cap][K]
   uint32_t x_bytes;    // size of X (< 2 GiB)
   const uint16_t* W;   // gate_up: W1 [E][2I][h]; down: W2 [E][h][I]
+  const uint8_t* W8;   // skinny FP8 entry: the same weights as E4M3 codes (W unused)
+  const float* wscale; // with W8: one scale per weight row ([E][2I] or [E][h])
   const uint16_t* Bw;  // gate_up: B1 [nA][E][2I][r]; down: B2 [nA][E][h][r]
   const float* zsum;    // skinny: [cap][r] LoRA shrink output (its split parts added)
   const uint16_t* zhl;  // tiled: [2][cap][r] the same as bf16 high and low planes
@@ -134,7 +136,7 @@ hipError_t launch_zfinal(const float* zpart, int S, int64_t cap, int r, const in
                          int bm, int64_t max_rows, float* zsum, uint16_t* zhl,
                          hipStream_t stream);
 hipError_t launch_skinny(const SkinnyConfig& c, bool gateup, const GemmArgs& a, int grid_y,
-                         hipStream_t stream);
+                         hipStream_t stream, bool fp8 = false);
 hipError_t launch_tiled(const TiledConfig& c, bool gateup, const GemmArgs& a, hipStream_t stream);
 hipError_t launch_combine(const float* D, int ksplit, int64_t split_stride, const int* pair_row,
                           const float* topk_w, int T, int k, int h, uint16_t* y,

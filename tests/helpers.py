@@ -39,6 +39,9 @@ def oracle_rows(inp: dict, topk: int, tokens=None) -> np.ndarray:
         "W1": inp["W1"].cpu(),
         "W2": inp["W2"].cpu(),
     }
+    for name in ("W1_scale", "W2_scale"):  # E4M3 weights: per-row scales
+        if name in inp:
+            host[name] = inp[name].cpu()
     for name in ("A1", "B1", "A2", "B2"):
         host[name] = inp[name].index_select(0, used_t).cpu()
     return oracle.forward(host, topk)

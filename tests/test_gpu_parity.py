@@ -268,3 +268,74 @@ def test_forward_full_size_stress_distinct_and_same():
                 what="stress_same")
     del inp, same
     torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------------------- FP8 expert weights
+
+# the skinny-path shapes of SMALL (at most 24 token-expert pairs per expert)
+FP8_SMALL = [n for n, w in SMALL.items() if w.T * w.topk <= 24 * w.n_experts]
+
+
+def _run_fp8(inp: dict, topk: int, workspace=None):
+    g = {k: v.to(DEV) for k, v in inp.items()}
+    y = ml.forward_fp8(g["x"], g["logits"], g["W1"], g["W1_scale"], g["W2"], g["W2_scale"],
+                       g["A1"], g["B1"], g["A2"], g["B2"], g["adapter_ids"], topk,
+                       workspace=workspace)
+    torch.cuda.synchronize()
+    return y
+
+
+def test_fp8_small_cases_exist():
+    assert {"tiny", "ragged", "r8_k1", "r32_k4", "r64_E1", "fg_small", "one_token"} <= set(FP8_SMALL)
+
+
+@pytest.mark.parametrize("name", FP8_SMALL)
+@pytest.mark.parametrize("b_scale", [1.0, 10.0])
+def test_forward_fp8_small_vs_oracle(name, b_scale):
+    w = SMALL[name]
+    _say(f"forward fp8 {name} b_scale={b_scale}")
+    inp = configs.make_inputs_fp8(w, 3, b_scale=b_scale)
+    inp["adapter_ids"][::5] = -1
+    y = _run_fp8(inp, w.topk)
+    check_close(y, oracle_rows(inp, w.topk), what=f"fp8 {name} b_scale={b_scale}")
+
+
+def test_forward_fp8_scales_matter():
+    """Doubling one expert's scales doubles its base term: the output changes where the oracle
+    says it does (a kernel that ignored the scales, or applied them to the wrong rows, fails)."""
+    w = SMALL["ragged"]
+    inp = configs.make_inputs_fp8(w, 4)
+    inp["W1_scale"][1] *= 2.0
+    inp["W2_scale"][3] *= 0.5
+    y = _run_fp8(inp, w.topk)
+    check_close(y, oracle_rows(inp, w.topk), what="fp8 rescaled experts")
+
+
+def test_forward_fp8_tiled_size_unsupported():
+    w = SMALL["mid"]  # 50 pairs per expert
+    inp = configs.make_inputs_fp8(w, 1)
+    with pytest.raises(ml.MoeLoraError) as ei:
+        _run_fp8(inp, w.topk)
+    assert ei.value.code == ml.EUNSUPPORTED
+
+
+@pytest.mark.parametrize("name", ["decode", "fg"])
+def test_forward_fp8_full_size_sampled(name):
+    w = configs.WORKLOADS[name]
+    _say(f"full-size fp8 {name}: generating inputs on the GPU")
+    inp = configs.make_inputs_fp8(w, 0, device=DEV)
+    _say(f"full-size fp8 {name}: forward")
+    args = (inp["x"], inp["logits"], inp["W1"], inp["W1_scale"], inp["W2"], inp["W2_scale"],
+            inp["A1"], inp["B1"], inp["A2"], inp["B2"], inp["adapter_ids"], w.topk)
+    y = ml.forward_fp8(*args)
+    torch.cuda.synchronize()
+    toks = sample_tokens(w.T, 12, 0)
+    _say(f"full-size fp8 {name}: oracle on {len(toks)} tokens")
+    y_ref = oracle_rows(inp, w.topk, toks)
+    rel = check_close(y[torch.from_numpy(toks).long().to(DEV)], y_ref, what=f"fp8 {name}")
+    _say(f"full-size fp8 {name}: max rel err {rel:.2e}")
+    y2 = ml.forward_fp8(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    del inp
+    torch.cuda.empty_cache()
