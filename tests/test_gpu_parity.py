@@ -339,3 +339,39 @@ def test_forward_fp8_full_size_sampled(name):
     assert torch.equal(y, y2)
     del inp
     torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------------------- HIP graph capture
+
+@pytest.mark.parametrize("name", ["ragged", "tiled64", "fg_small"])
+def test_forward_graph_capture_replays(name):
+    """One layer call captured in a HIP graph (the library enqueues kernels only: no memset,
+    no host synchronisation) and replayed several times, with other eager calls on the same
+    workspace in between: every replay equals the eager result."""
+    w = SMALL[name]
+    inp = {k: v.to(DEV) for k, v in _small_inputs(w, 6).items()}
+    other = {k: v.to(DEV) for k, v in _small_inputs(w, 7).items()}
+    d = ml.Dims(w.T, w.hidden, w.inter, w.n_experts, w.n_adapters, w.rank)
+    ws = ml.new_workspace(d, w.topk, DEV)
+    y = torch.empty((w.T, w.hidden), dtype=torch.bfloat16, device=DEV)
+    y_other = torch.empty_like(y)
+    keys = ("x", "logits", "W1", "W2", "A1", "B1", "A2", "B2", "adapter_ids")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        ml.forward(*[inp[k] for k in keys], w.topk, y=y, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    y_eager = y.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ml.forward(*[inp[k] for k in keys], w.topk, y=y, workspace=ws)
+    torch.cuda.synchronize()
+    for i in range(3):
+        y.fill_(0)
+        ml.forward(*[other[k] for k in keys], w.topk, y=y_other, workspace=ws)  # eager, same workspace
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager), f"replay {i}"
+    check_close(y, oracle_rows(inp, w.topk), what=f"graph replay {name}")
