@@ -47,9 +47,10 @@ def lib():
         L.oracle_forward.argtypes = [ctypes.POINTER(_Dims), P, P, P, P, P, i32, P, P]
         L.oracle_forward_scaled.argtypes = [ctypes.POINTER(_Dims), P, P, P, P, P, P, P, i32, P, P]
         L.oracle_fp8e4m3_decode.argtypes = [P, ctypes.c_int64, P]
+        L.oracle_sgmv.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, P]
         L.oracle_num_threads.argtypes = []
         for f in (L.oracle_route, L.oracle_align, L.oracle_forward, L.oracle_forward_scaled,
-                  L.oracle_fp8e4m3_decode, L.oracle_num_threads):
+                  L.oracle_fp8e4m3_decode, L.oracle_sgmv, L.oracle_num_threads):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -184,6 +185,32 @@ def forward(inputs: dict, topk: int, tokens=None, return_pairs: bool = False):
                                      None if dp is None else _ptr(dp))
     _check(rc, "oracle_forward")
     return (y, dp) if return_pairs else y
+
+
+def sgmv(x, A, B, y_in, adapter_ids) -> np.ndarray:
+    """Dense multi-LoRA: y_in + (x A_a^T) B_a^T per token (a = adapter_ids[t], -1: unchanged),
+    float64. x[T][K], A[nA][r][K], B[nA][N][r], y_in[T][N]; bf16, float32 or float64 each."""
+    arrs, dts = [], []
+    for a in (x, A, B, y_in):
+        v, dtc = _np(a)
+        if dtc == ORC_FP8E4M3:
+            raise TypeError("E4M3 is for the expert weights only")
+        arrs.append(v)
+        dts.append(dtc)
+    xa, Aa, Ba, ya = arrs
+    T, K = xa.shape
+    nA, r, K2 = Aa.shape
+    nA2, N, r2 = Ba.shape
+    if K2 != K or nA2 != nA or r2 != r or ya.shape != (T, N):
+        raise ValueError("inconsistent shapes")
+    ad = _i32(adapter_ids)
+    if ad.shape != (T,):
+        raise ValueError("adapter_ids must be [T]")
+    out = np.zeros((T, N), np.float64)
+    dtarr = (ctypes.c_int32 * 4)(*dts)
+    _check(lib().oracle_sgmv(_ptr(xa), _ptr(Aa), _ptr(Ba), _ptr(ya), dtarr, _ptr(ad), T, K, N, nA, r,
+                             _ptr(out)), "oracle_sgmv")
+    return out
 
 
 def fp8e4m3_decode(codes) -> np.ndarray:

@@ -340,6 +340,48 @@ int oracle_forward(const orc_dims *d, const void *const *t, const int32_t *dt,
                                d_pairs);
 }
 
+/* ------------------------------------------------------------------------------------------
+ * Dense multi-LoRA (segmented gather matrix-vector, SGMV). Page "Punica: Multi-Tenant LoRA
+ * Serving", sections on the proposed method: one copy of the base model serves a batch whose
+ * tokens use different adapters; the LoRA add of one projection is applied per segment of
+ * tokens that share an adapter. Page "vLLM MoE LoRA SageMaker Bedrock", section "O Papel da
+ * Multi-LoRA": the shrink computes z = xA, the expand adds zB.
+ *   y_out[t][n] = y_in[t][n] + sum_q z[t][q] B[a][n][q],  z[t][q] = sum_c x[t][c] A[a][q][c]
+ * for a = adapter_ids[t] >= 0; y_out = y_in for a = -1. Layouts: x[T][K], A[nA][r][K],
+ * B[nA][N][r] (stored out x in), y[T][N]; dt[] gives the dtypes of x, A, B, y_in.
+ * ------------------------------------------------------------------------------------------ */
+int oracle_sgmv(const void *x, const void *A, const void *B, const void *y_in, const int32_t *dt,
+                const int32_t *adapter_ids, int32_t T, int32_t K, int32_t N, int32_t nA,
+                int32_t r, double *y_out) {
+  if (T < 0 || K <= 0 || N <= 0 || nA <= 0 || r <= 0) return ORC_EINVAL;
+  for (int32_t t = 0; t < T; ++t)
+    if (adapter_ids[t] < -1 || adapter_ids[t] >= nA) return ORC_EADAPTER;
+  int status = ORC_OK;
+#pragma omp parallel
+  {
+    double *xr = (double *)malloc(sizeof(double) * (size_t)K);
+    double *z = (double *)malloc(sizeof(double) * (size_t)r);
+    if (!xr || !z) {
+#pragma omp atomic write
+      status = ORC_ENOMEM;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int32_t t = 0; t < T; ++t) {
+        const int32_t a = adapter_ids[t];
+        double *yr = y_out + (size_t)t * N;
+        for (int32_t n = 0; n < N; ++n) yr[n] = ld(y_in, dt[3], (size_t)t * N + n);
+        if (a < 0) continue;
+        for (int32_t c = 0; c < K; ++c) xr[c] = ld(x, dt[0], (size_t)t * K + c);
+        for (int32_t q = 0; q < r; ++q) z[q] = dot_row(xr, A, dt[1], ((size_t)a * r + q) * K, K);
+        for (int32_t n = 0; n < N; ++n) yr[n] += dot_row(z, B, dt[2], ((size_t)a * N + n) * r, r);
+      }
+    }
+    free(xr);
+    free(z);
+  }
+  return status;
+}
+
 /* E4M3 codes decoded to float64, for the tests. */
 int oracle_fp8e4m3_decode(const uint8_t *codes, int64_t n, double *out) {
   for (int64_t i = 0; i < n; ++i) out[i] = fp8e4m3_to_f64(codes[i]);

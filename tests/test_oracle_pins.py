@@ -348,3 +348,48 @@ def test_fp8_quantized_rows_reproduce_weights():
     err = np.abs(back - Wf)
     assert np.all(err <= 2.0 ** -4 * np.abs(Wf) + 2.0 ** -9 * scale.double().numpy()[..., None])
     assert np.all(np.abs(oracle.fp8e4m3_decode(codes.numpy())).max(axis=-1) == 448.0)
+
+
+# ----------------------------------------------------------------------------- dense multi-LoRA
+
+def _sgmv_inputs(T, K, N, nA, r, seed, dtype=torch.float64):
+    g = torch.Generator().manual_seed(seed)
+    x = (torch.randn(T, K, generator=g) * 0.5).to(dtype)
+    A = (torch.randn(nA, r, K, generator=g) * 0.1).to(dtype)
+    B = (torch.randn(nA, N, r, generator=g) * 0.1).to(dtype)
+    y = torch.randn(T, N, generator=g).to(dtype)
+    ad = torch.randint(-1, nA, (T,), generator=g, dtype=torch.int32)
+    return x, A, B, y, ad
+
+
+@pytest.mark.parametrize("dtype", [torch.float64, torch.bfloat16])
+def test_sgmv_vs_numpy_merged_weight(dtype):
+    """Per token, y + x (B_a A_a)^T with the merged r-rank update formed by numpy matmul."""
+    x, A, B, y, ad = _sgmv_inputs(37, 96, 80, 5, 8, 0, dtype)
+    out = oracle.sgmv(x, A, B, y, ad)
+    xn, An, Bn, yn = (t.double().numpy() for t in (x, A, B, y))
+    for t in range(x.shape[0]):
+        a = int(ad[t])
+        want = yn[t] if a < 0 else yn[t] + xn[t] @ (Bn[a] @ An[a]).T
+        np.testing.assert_allclose(out[t], want, rtol=1e-12, atol=1e-12)
+
+
+def test_sgmv_no_adapter_and_zero_b():
+    x, A, B, y, ad = _sgmv_inputs(20, 64, 48, 3, 16, 1)
+    ad[:] = -1
+    assert np.array_equal(oracle.sgmv(x, A, B, y, ad), y.numpy())
+    ad2 = torch.zeros_like(ad)
+    assert np.array_equal(oracle.sgmv(x, A, torch.zeros_like(B), y, ad2), y.numpy())
+
+
+def test_sgmv_onto_zero_is_shrink_then_expand():
+    """Onto y = 0 the output is the LoRA term alone, B_a (A_a x): the shrink-then-expand order
+    (the test above multiplies the merged B_a A_a instead)."""
+    T, h, I, nA, r = 9, 32, 16, 3, 8
+    x, A, B, y, ad = _sgmv_inputs(T, h, 2 * I, nA, r, 2)
+    z = oracle.sgmv(x, A, B, torch.zeros(T, 2 * I, dtype=torch.float64), ad)
+    xn, An, Bn = x.numpy(), A.numpy(), B.numpy()
+    for t in range(T):
+        a = int(ad[t])
+        want = np.zeros(2 * I) if a < 0 else Bn[a] @ (An[a] @ xn[t])
+        np.testing.assert_allclose(z[t], want, rtol=1e-12, atol=1e-13)
