@@ -69,6 +69,14 @@ typedef struct {
   int32_t T, hidden, inter, n_experts, n_adapters, rank;
 } moe_lora_dims;
 
+/* Dense multi-LoRA (SGMV) sizes: T tokens, in_features (K) and out_features (N) of the
+ * projection, n_adapters, rank. Supported: T >= 0; in_features a positive multiple of 128;
+ * out_features a positive multiple of 64; n_adapters >= 1; rank in {8, 16, 32, 64}; x (T x K)
+ * under 2 GiB. */
+typedef struct {
+  int32_t T, in_features, out_features, n_adapters, rank;
+} moe_lora_sgmv_dims;
+
 /* Bytes of device workspace moe_lora_forward needs for these sizes (0 when the sizes are
  * unsupported). The workspace must be 256-byte aligned; its contents need no initialisation
  * and are overwritten by every call. */
@@ -123,6 +131,23 @@ int moe_lora_forward_fp8(const void *x, const float *router_logits, const void *
  * T*topk*seg_pad + n_experts*(block_m-1), or -1 for invalid arguments. */
 int64_t moe_lora_sorted_capacity(const moe_lora_dims *d, int32_t topk, int32_t seg_pad,
                                  int32_t block_m);
+
+/* Bytes of device workspace moe_lora_sgmv needs (0 when the sizes are unsupported); 256-byte
+ * aligned, no initialisation needed. */
+size_t moe_lora_sgmv_workspace_size(const moe_lora_sgmv_dims *d);
+
+/* Dense multi-LoRA, the per-adapter segmented shrink and expand of one projection (page
+ * "Punica: Multi-Tenant LoRA Serving", proposed method: one base model, a batch of tokens
+ * with different adapters, the LoRA add applied per segment of tokens sharing an adapter; page
+ * "vLLM MoE LoRA SageMaker Bedrock", section "O Papel da Multi-LoRA": z = xA, then zB):
+ *   y[t] += (x[t] A[a]^T) B[a]^T,  a = adapter_ids[t]; tokens with a = -1 keep y[t].
+ * x [T][K] bf16, A [nA][r][K] bf16, B [nA][N][r] bf16, adapter_ids [T] int32, y [T][N] bf16
+ * updated in place (the sum in fp32, rounded once); device pointers, caller-owned, 16-byte
+ * aligned. Adapter ids outside [-1, nA) act as -1 and set MOELORA_FLAG_ADAPTER_RANGE
+ * (moe_lora_debug_status on this workspace). Asynchronous on `stream`; allocates nothing. */
+int moe_lora_sgmv(const void *x, const void *A, const void *B, const int32_t *adapter_ids,
+                  const moe_lora_sgmv_dims *d, void *y, void *workspace, size_t workspace_bytes,
+                  void *stream);
 
 /* Routing and align on their own, for inspection and tests.
  *   topk_ids   int32 [T][topk]  expert of slot j, slots in descending logit order

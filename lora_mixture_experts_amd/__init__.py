@@ -21,7 +21,7 @@ FLAG_NONFINITE_LOGIT, FLAG_ADAPTER_RANGE = 1, 2
 
 EXPORTS = ("moe_lora_workspace_size", "moe_lora_forward", "moe_lora_forward_timed", "moe_lora_forward_fp8",
            "moe_lora_sorted_capacity", "moe_lora_route_align", "moe_lora_strerror",
-           "moe_lora_debug_status")
+           "moe_lora_debug_status", "moe_lora_sgmv_workspace_size", "moe_lora_sgmv")
 N_STAGES = 7
 STAGES = ("route", "align", "shrink_gate_up", "gate_up", "shrink_down", "down", "combine")
 
@@ -34,6 +34,10 @@ class MoeLoraError(RuntimeError):
 
 class Dims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("T", "hidden", "inter", "n_experts", "n_adapters", "rank")]
+
+
+class SgmvDims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("T", "in_features", "out_features", "n_adapters", "rank")]
 
 
 _lib = None
@@ -58,6 +62,10 @@ def lib() -> ctypes.CDLL:
         L.moe_lora_forward_fp8.argtypes = [P, P, P, P, P, P, P, P, P, P, P, i32, D, P, P, ctypes.c_size_t, P,
                                            ctypes.POINTER(ctypes.c_void_p)]
         L.moe_lora_forward_fp8.restype = ctypes.c_int
+        L.moe_lora_sgmv_workspace_size.argtypes = [ctypes.POINTER(SgmvDims)]
+        L.moe_lora_sgmv_workspace_size.restype = ctypes.c_size_t
+        L.moe_lora_sgmv.argtypes = [P, P, P, P, ctypes.POINTER(SgmvDims), P, P, ctypes.c_size_t, P]
+        L.moe_lora_sgmv.restype = ctypes.c_int
         L.moe_lora_sorted_capacity.argtypes = [D, i32, i32, i32]
         L.moe_lora_sorted_capacity.restype = i64
         L.moe_lora_route_align.argtypes = [P, P, i32, D, i32, i32, P, P, P, i64, P, P, P, P,
@@ -161,6 +169,30 @@ def forward(x, router_logits, W1, W2, A1, B1, A2, B2, adapter_ids, topk: int, y=
         handles = (ctypes.c_void_p * (N_STAGES + 1))(
             *[ev.cuda_event if ev is not None else None for ev in stage_events])
         _check(lib().moe_lora_forward_timed(*args, handles), "moe_lora_forward_timed")
+    return y
+
+
+def sgmv(x, A, B, adapter_ids, y, workspace=None) -> torch.Tensor:
+    """Dense multi-LoRA, in place: y[t] += (x[t] A[a]^T) B[a]^T for a = adapter_ids[t] (-1: y[t]
+    unchanged); moe_lora_sgmv. x [T][K], A [nA][r][K], B [nA][N][r], y [T][N] bf16,
+    adapter_ids [T] int32."""
+    T, K = x.shape
+    nA, r, _ = A.shape
+    N = B.shape[1]
+    d = SgmvDims(T, K, N, nA, r)
+    bf = torch.bfloat16
+    _expect(x, "x", bf, (T, K))
+    _expect(A, "A", bf, (nA, r, K))
+    _expect(B, "B", bf, (nA, N, r))
+    _expect(adapter_ids, "adapter_ids", torch.int32, (T,))
+    _expect(y, "y", bf, (T, N))
+    if workspace is None:
+        n = int(lib().moe_lora_sgmv_workspace_size(ctypes.byref(d)))
+        if n == 0:
+            raise MoeLoraError(EINVAL_DIMS, "moe_lora_sgmv_workspace_size")
+        workspace = torch.empty(n, dtype=torch.uint8, device=x.device)
+    _check(lib().moe_lora_sgmv(_ptr(x), _ptr(A), _ptr(B), _ptr(adapter_ids), ctypes.byref(d), _ptr(y),
+                               _ptr(workspace), workspace.numel(), _stream(x.device)), "moe_lora_sgmv")
     return y
 
 

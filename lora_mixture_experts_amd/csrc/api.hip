@@ -553,6 +553,154 @@ int moe_lora_forward_fp8(const void* x, const float* router_logits, const void* 
                       workspace, workspace_bytes, stream, stage_events, W1_scale, W2_scale);
 }
 
+namespace {
+
+// Workspace of moe_lora_sgmv: flags first (moe_lora_debug_status), then the sorted layout of T
+// single-expert pairs in 16-row blocks, the shrink's split parts and their sum, align scratch.
+struct SgmvLayout {
+  size_t flags, sorted, sorted_ad, expert_off, n_blocks, block_expert, block_seg, seg_table, n_seg,
+      zpart, zsum, align_lists, total;
+  int64_t cap;
+};
+
+int sgmv_validate(const moe_lora_sgmv_dims* d) {
+  if (!d) return MOELORA_ENULL;
+  if (d->T < 0 || d->in_features <= 0 || d->out_features <= 0 || d->n_adapters <= 0)
+    return MOELORA_EINVAL_DIMS;
+  if (d->in_features % 128 != 0 || d->out_features % 64 != 0) return MOELORA_EINVAL_DIMS;
+  if (!(d->rank == 8 || d->rank == 16 || d->rank == 32 || d->rank == 64)) return MOELORA_EINVAL_DIMS;
+  if ((int64_t)d->T * d->in_features * 2 >= ((int64_t)1 << 31)) return MOELORA_EINVAL_DIMS;
+  if ((int64_t)d->T + 256 >= ((int64_t)1 << 30) || (int64_t)d->n_adapters + 1 >= ((int64_t)1 << 28))
+    return MOELORA_EINVAL_DIMS;
+  return MOELORA_OK;
+}
+
+void sgmv_layout(const moe_lora_sgmv_dims* d, SgmvLayout* L) {
+  const int64_t T = d->T, r = d->rank;
+  L->cap = round_up64(T + 15, 256);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + (bytes ? bytes : 1));
+    return o;
+  };
+  L->flags = take(16);
+  L->sorted = take(4 * (size_t)L->cap);
+  L->sorted_ad = take(4 * (size_t)L->cap);
+  L->expert_off = take(8);
+  L->n_blocks = take(4);
+  L->block_expert = take(4 * (size_t)(L->cap / 16 + 1));
+  L->block_seg = take(4 * (size_t)(L->cap / 16 + 1));
+  L->seg_table = take(16 * (size_t)T);
+  L->n_seg = take(4);
+  L->zpart = take(4 * (size_t)kMaxSplit * L->cap * r);
+  L->zsum = take(4 * (size_t)L->cap * r);
+  L->align_lists = take(4 * align_list_ints((int)T, 1, 1, d->n_adapters));
+  L->total = off;
+}
+
+}  // namespace
+
+size_t moe_lora_sgmv_workspace_size(const moe_lora_sgmv_dims* d) {
+  if (sgmv_validate(d) != MOELORA_OK) return 0;
+  SgmvLayout L;
+  sgmv_layout(d, &L);
+  return L.total;
+}
+
+int moe_lora_sgmv(const void* x, const void* A, const void* B, const int32_t* adapter_ids,
+                  const moe_lora_sgmv_dims* d, void* y, void* workspace, size_t workspace_bytes,
+                  void* stream_) {
+  int rc = sgmv_validate(d);
+  if (rc != MOELORA_OK) return rc;
+  if (d->T == 0) return MOELORA_OK;
+  const void* ptrs[] = {x, A, B, adapter_ids, y, workspace};
+  for (const void* p : ptrs)
+    if (!p) return MOELORA_ENULL;
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOELORA_EALIGN;
+  if (((uintptr_t)workspace & 255u) != 0) return MOELORA_EWORKSPACE;
+  SgmvLayout L;
+  sgmv_layout(d, &L);
+  if (workspace_bytes < L.total) return MOELORA_EWORKSPACE;
+  rc = check_device();
+  if (rc != MOELORA_OK) return rc;
+
+  hipStream_t stream = (hipStream_t)stream_;
+  char* ws = (char*)workspace;
+  const int T = d->T, K = d->in_features, N = d->out_features, nA = d->n_adapters, r = d->rank;
+  const int bm = 16;
+  const int max_blocks = (T + bm - 1 + 15) / bm;  // T rows plus at most 15 padding rows
+
+  // align: one expert, one pair per token; segments by adapter
+  AlignArgs al;
+  al.topk_ids = nullptr;
+  al.adapter_ids = adapter_ids;
+  al.tok_flags = nullptr;
+  al.T = T;
+  al.k = 1;
+  al.E = 1;
+  al.nA = nA;
+  al.seg_pad = 1;
+  al.block_m = bm;
+  al.sorted_pairs = (int*)(ws + L.sorted);
+  al.expert_offsets = (int*)(ws + L.expert_off);
+  al.seg_table = (int*)(ws + L.seg_table);
+  al.n_seg = (int*)(ws + L.n_seg);
+  al.flags = (int*)(ws + L.flags);
+  al.block_expert = (int*)(ws + L.block_expert);
+  al.block_seg = (int*)(ws + L.block_seg);
+  al.pair_row = nullptr;
+  al.sorted_ad = (int*)(ws + L.sorted_ad);
+  al.n_blocks = (int*)(ws + L.n_blocks);
+  al.g_lists = (int*)(ws + L.align_lists);
+  const size_t lds = align_lds_plan(T, 1, 1, nA, &al);
+  if (launch_align(al, lds, stream) != hipSuccess) return MOELORA_EHIP;
+
+  // shrink z = x A_a^T over 16-row tiles, split over K
+  ShrinkArgs sh;
+  sh.X = (const uint16_t*)x;
+  sh.x_bytes = (uint32_t)((size_t)T * K * 2);
+  sh.sorted_pairs = al.sorted_pairs;
+  sh.sorted_ad = al.sorted_ad;
+  sh.block_expert = al.block_expert;
+  sh.block_seg = al.block_seg;
+  sh.seg_table = al.seg_table;
+  sh.n_seg = al.n_seg;
+  sh.n_blocks = al.n_blocks;
+  sh.bm = bm;
+  sh.adapter_ids = adapter_ids;
+  sh.k = 1;
+  sh.nA = nA;
+  sh.E = 1;
+  sh.r = r;
+  sh.K = K;
+  sh.Aw = (const uint16_t*)A;
+  sh.S = pick_splits(std::min<int64_t>(max_blocks, (T + 15) / 16 + 1), K);
+  sh.zpart = (float*)(ws + L.zpart);
+  sh.cap = L.cap;
+  sh.xcd_ranges = 0;
+  sh.after64 = 0;
+  if (launch_shrink(true, sh, max_blocks, stream) != hipSuccess) return MOELORA_EHIP;
+  float* zsum = (float*)(ws + L.zsum);
+  if (launch_zfinal(sh.zpart, sh.S, L.cap, r, al.n_blocks, bm, (int64_t)max_blocks * bm, zsum,
+                    nullptr, stream) != hipSuccess)
+    return MOELORA_EHIP;
+
+  // expand y += z B_a^T
+  SgmvArgs sa;
+  sa.sorted_pairs = al.sorted_pairs;
+  sa.sorted_ad = al.sorted_ad;
+  sa.n_blocks = al.n_blocks;
+  sa.zsum = zsum;
+  sa.B = (const uint16_t*)B;
+  sa.y = (uint16_t*)y;
+  sa.N = N;
+  sa.r = r;
+  if (launch_sgmv_expand(sa, max_blocks, stream) != hipSuccess) return MOELORA_EHIP;
+  return MOELORA_OK;
+}
+
 int moe_lora_route_align(const float* router_logits, const int32_t* adapter_ids, int32_t topk,
                          const moe_lora_dims* d, int32_t seg_pad, int32_t block_m,
                          int32_t* topk_ids, float* topk_w, int32_t* sorted_pairs,

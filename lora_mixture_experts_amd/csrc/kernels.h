@@ -10,9 +10,9 @@ constexpr int kAlignStaticLds = 17 * 1024;  // >= the align kernel's static LDS 
 constexpr int kLdsBytes = 160 * 1024;
 
 struct AlignArgs {
-  const int* topk_ids;     // [T*k]
+  const int* topk_ids;     // [T*k], or nullptr: expert 0 for every pair (no routing)
   const int* adapter_ids;  // [T]
-  const int* tok_flags;    // [T]
+  const int* tok_flags;    // [T] or nullptr
   int T, k, E, nA, seg_pad, block_m;
   int* sorted_pairs;    // [>= padded total]
   int* expert_offsets;  // [E+1]
@@ -109,6 +109,17 @@ struct GemmArgs {
   int n_col_tiles;    // skinny: column tiles of one row block (N / columns per workgroup)
 };
 
+// Dense multi-LoRA expand: y[t] += z[t] B_a^T over the sorted layout of T tokens (k = 1, E = 1).
+struct SgmvArgs {
+  const int* sorted_pairs;  // [cap]: token of each sorted row, -1 for padding
+  const int* sorted_ad;     // [cap]: its adapter, -1 for none or padding
+  const int* n_blocks;      // live 16-row blocks
+  const float* zsum;        // [cap][r] shrink output (split parts added)
+  const uint16_t* B;        // [nA][N][r]
+  uint16_t* y;              // [T][N], updated in place
+  int N, r;
+};
+
 // Tile shape of the LDS-staged GEMM: nw wavefronts of WM x WN each; NST LDS stages of BK k.
 struct TiledConfig {
   int bm, bn, wm, wn;
@@ -138,6 +149,7 @@ hipError_t launch_zfinal(const float* zpart, int S, int64_t cap, int r, const in
 hipError_t launch_skinny(const SkinnyConfig& c, bool gateup, const GemmArgs& a, int grid_y,
                          hipStream_t stream, bool fp8 = false);
 hipError_t launch_tiled(const TiledConfig& c, bool gateup, const GemmArgs& a, hipStream_t stream);
+hipError_t launch_sgmv_expand(const SgmvArgs& a, int max_blocks, hipStream_t stream);
 hipError_t launch_combine(const float* D, int ksplit, int64_t split_stride, const int* pair_row,
                           const float* topk_w, int T, int k, int h, uint16_t* y,
                           hipStream_t stream);

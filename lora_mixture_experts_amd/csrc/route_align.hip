@@ -281,7 +281,7 @@ __global__ __launch_bounds__(1024) void align_kernel(AlignArgs a) {
   // phase 0
   // (loads in batches of 8 per thread, issued before any is used)
   int fl_nonfinite = 0, fl_range = 0;
-  for (int t0 = 0; t0 < T; t0 += 8 * bd) {
+  for (int t0 = 0; a.tok_flags && t0 < T; t0 += 8 * bd) {
     int f[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -296,7 +296,7 @@ __global__ __launch_bounds__(1024) void align_kernel(AlignArgs a) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int p = q0 + u * bd + tid;
-      ex[u] = p < P ? a.topk_ids[p] : 0;
+      ex[u] = (p < P && a.topk_ids) ? a.topk_ids[p] : 0;
       av[u] = p < P ? a.adapter_ids[token_of(p)] : -1;
     }
 #pragma unroll

@@ -2,6 +2,7 @@
 
 Routing ids, slot order, sorted pairs, expert offsets and the segment table must match
 bit for bit; y must satisfy max|y - y_ref| <= 2e-2 * max|y_ref| globally and per token."""
+import ctypes
 import sys
 
 import numpy as np
@@ -375,3 +376,75 @@ def test_forward_graph_capture_replays(name):
         torch.cuda.synchronize()
         assert torch.equal(y, y_eager), f"replay {i}"
     check_close(y, oracle_rows(inp, w.topk), what=f"graph replay {name}")
+
+
+# ----------------------------------------------------------------------------- dense multi-LoRA
+
+SGMV_CASES = [
+    # T, K, N, nA, r, adapters
+    (37, 256, 192, 5, 16, "uniform"),
+    (1, 128, 64, 3, 8, "uniform"),
+    (200, 512, 320, 64, 32, "uniform"),
+    (300, 384, 256, 4, 64, "runs"),
+    (64, 256, 128, 1, 16, "same"),
+    (700, 256, 256, 700, 16, "distinct"),
+    (2000, 128, 64, 8, 8, "runs"),
+]
+
+
+def _sgmv_case(T, K, N, nA, r, adapters, seed):
+    g = torch.Generator().manual_seed(seed)
+    x = (torch.randn(T, K, generator=g) * 0.5).to(torch.bfloat16)
+    A = (torch.randn(nA, r, K, generator=g) * 0.05).to(torch.bfloat16)
+    B = (torch.randn(nA, N, r, generator=g) * 0.05).to(torch.bfloat16)
+    if adapters == "uniform":
+        ad = torch.randint(-1, nA, (T,), generator=g, dtype=torch.int32)
+    elif adapters == "runs":
+        ad = (torch.arange(T, dtype=torch.int32) // 41) % nA
+        ad[::7] = -1
+    elif adapters == "same":
+        ad = torch.zeros(T, dtype=torch.int32)
+    else:
+        ad = torch.randperm(nA, generator=g)[:T].to(torch.int32)
+    return x, A, B, ad
+
+
+@pytest.mark.parametrize("T,K,N,nA,r,adapters", SGMV_CASES)
+def test_sgmv_vs_oracle(T, K, N, nA, r, adapters):
+    _say(f"sgmv T={T} K={K} N={N} nA={nA} r={r} {adapters}")
+    x, A, B, ad = _sgmv_case(T, K, N, nA, r, adapters, T + nA)
+    # onto y = 0: the LoRA term alone, against the oracle's; untouched tokens stay exactly 0
+    y = torch.zeros(T, N, dtype=torch.bfloat16, device=DEV)
+    ml.sgmv(x.to(DEV), A.to(DEV), B.to(DEV), ad.to(DEV), y)
+    torch.cuda.synchronize()
+    ref = oracle.sgmv(x, A, B, torch.zeros(T, N, dtype=torch.bfloat16), ad)
+    check_close(y, ref, what="sgmv term")
+    none = (ad < 0).numpy()
+    assert np.all(y.float().cpu().numpy()[none] == 0)
+    # onto a given y: within one bf16 rounding of the sum, tokens without adapter bit-exact
+    y0 = torch.randn(T, N, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
+    y = y0.to(DEV)
+    ml.sgmv(x.to(DEV), A.to(DEV), B.to(DEV), ad.to(DEV), y)
+    torch.cuda.synchronize()
+    ref = oracle.sgmv(x, A, B, y0, ad)
+    got = y.double().cpu().numpy()
+    term = np.abs(ref - y0.double().numpy()).max()
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 2e-2 * term)
+    assert torch.equal(y.cpu()[torch.from_numpy(none)], y0[torch.from_numpy(none)])
+
+
+def test_sgmv_empty_and_bad_adapters():
+    x, A, B, ad = _sgmv_case(50, 128, 64, 3, 8, "uniform", 9)
+    ad[::4] = 17  # out of range: no adapter, flag set
+    d = ml.SgmvDims(50, 128, 64, 3, 8)
+    ws = torch.empty(int(ml.lib().moe_lora_sgmv_workspace_size(ctypes.byref(d))), dtype=torch.uint8,
+                     device=DEV)
+    y = torch.zeros(50, 64, dtype=torch.bfloat16, device=DEV)
+    ml.sgmv(x.to(DEV), A.to(DEV), B.to(DEV), ad.to(DEV), y, workspace=ws)
+    torch.cuda.synchronize()
+    ad_ref = torch.where(ad >= 3, torch.full_like(ad, -1), ad)
+    check_close(y, oracle.sgmv(x, A, B, torch.zeros(50, 64, dtype=torch.bfloat16), ad_ref),
+                what="sgmv bad adapters")
+    assert ml.debug_status(ws) == ml.FLAG_ADAPTER_RANGE
+    e = torch.zeros(0, 64, dtype=torch.bfloat16, device=DEV)
+    ml.sgmv(x[:0].to(DEV), A.to(DEV), B.to(DEV), ad[:0].to(DEV), e)
