@@ -8,7 +8,8 @@ seeded synthetic input already resident in HBM. Prints one JSON line.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode] [--fp8]
 
 --fp8 runs the FP8 entry point (E4M3 expert weights with per-row scales, moe_lora_forward_fp8)
-on the decode-sized workloads (decode, fg, tiny).
+on the decode-sized workloads (decode, fg, tiny). --workload sgmv measures the dense
+multi-LoRA entry point (moe_lora_sgmv) instead of the layer.
 """
 from __future__ import annotations
 
@@ -116,13 +117,73 @@ def cpu_baseline(w, inp, n_tokens: int, min_seconds: float):
                       f"oracle with OpenMP over tokens, inputs already in host memory; {dt:.1f} s wall"}
 
 
+# dense multi-LoRA: a serving batch of 256 tokens on a 4096 x 4096 projection, 64 adapters of
+# rank 16, one adapter per request of 4 tokens (uniform over the adapters)
+SGMV = dict(T=256, K=4096, N=4096, nA=64, r=16, run=4)
+
+
+def run_sgmv(args, torch, ml, dev):
+    """moe_lora_sgmv over seeded inputs in HBM: value = tokens/s; roofline = the call's
+    algorithmic bytes (touched A and B slabs, x, y read and written) over its time."""
+    import numpy as np
+    c = SGMV
+    g = torch.Generator().manual_seed(args.seed)
+    T, K, N, nA, r = c["T"], c["K"], c["N"], c["nA"], c["r"]
+    x = (torch.randn(T, K, generator=g) * 0.02).to(torch.bfloat16)
+    A = (torch.randn(nA, r, K, generator=g) * 0.02).to(torch.bfloat16)
+    B = (torch.randn(nA, N, r, generator=g) * 0.02).to(torch.bfloat16)
+    ad = torch.randint(0, nA, (T // c["run"] + 1,), generator=g, dtype=torch.int32).repeat_interleave(c["run"])[:T]
+    y = torch.zeros(T, N, dtype=torch.bfloat16)
+    xd, Ad, Bd, add, yd = (t.to(dev) for t in (x, A, B, ad, y))
+    d = ml.SgmvDims(T, K, N, nA, r)
+    import ctypes
+    ws = torch.empty(int(ml.lib().moe_lora_sgmv_workspace_size(ctypes.byref(d))), dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        ml.sgmv(xd, Ad, Bd, add, yd, workspace=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        ml.sgmv(xd, Ad, Bd, add, yd, workspace=ws)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    n_ad = len(np.unique(ad.numpy()))
+    nbytes = n_ad * r * (K + N) * 2 + T * K * 2 + 2 * T * N * 2 + 4 * T
+    per_call = elapsed / args.steps
+    ach = nbytes / per_call / 1e9
+    out = {
+        "metric": "tokens/s of the dense multi-LoRA (SGMV) add",
+        "value": T * args.steps / elapsed, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": per_call * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "sgmv", "T": T, "in_features": K, "out_features": N,
+                   "n_adapters": nA, "rank": r, "tokens_per_adapter_run": c["run"], "seed": args.seed},
+        "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": ach / HBM_PEAK_GBS, "traffic": None, "kernel": "whole call (4 launches)"},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        toks = np.arange(0, T, max(1, T // 32))
+        xs, ys, ads = x[toks], y[toks].float().to(torch.bfloat16), ad[toks]
+        passes, t1 = 0, time.perf_counter()
+        while True:
+            oracle.sgmv(xs, A, B, ys, ads)
+            passes += 1
+            dt = time.perf_counter() - t1
+            if dt >= args.cpu_seconds:
+                break
+        out["cpu_baseline"] = {"value": passes * len(toks) / dt, "unit": "tokens/s",
+                               "cores": min(oracle.num_threads(), len(toks)), "kind": "oracle",
+                               "sample": f"{passes} passes over {len(toks)} of {T} tokens, fp64 C oracle; {dt:.1f} s wall"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "prefill", "fg", "stress_distinct", "stress_same", "tiny"])
+                    choices=["decode", "prefill", "fg", "stress_distinct", "stress_same", "tiny", "sgmv"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-tokens", type=int, default=64, help="oracle sample size (tokens)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -148,6 +209,9 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.workload == "sgmv":
+        run_sgmv(args, torch, ml, dev)
+        return
     w = configs.WORKLOADS[args.workload]
 
     if args.copy_probe_mib:
