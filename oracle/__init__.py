@@ -48,9 +48,11 @@ def lib():
         L.oracle_forward_scaled.argtypes = [ctypes.POINTER(_Dims), P, P, P, P, P, P, P, i32, P, P]
         L.oracle_fp8e4m3_decode.argtypes = [P, ctypes.c_int64, P]
         L.oracle_sgmv.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, P]
+        L.oracle_router_logits.argtypes = [P, P, P, i32, i32, i32, P]
         L.oracle_num_threads.argtypes = []
         for f in (L.oracle_route, L.oracle_align, L.oracle_forward, L.oracle_forward_scaled,
-                  L.oracle_fp8e4m3_decode, L.oracle_sgmv, L.oracle_num_threads):
+                  L.oracle_fp8e4m3_decode, L.oracle_sgmv, L.oracle_router_logits,
+                  L.oracle_num_threads):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -185,6 +187,20 @@ def forward(inputs: dict, topk: int, tokens=None, return_pairs: bool = False):
                                      None if dp is None else _ptr(dp))
     _check(rc, "oracle_forward")
     return (y, dp) if return_pairs else y
+
+
+def router_logits(x, W_router) -> np.ndarray:
+    """logits[T][E] = x W_router^T in float64 (x [T][h], W_router [E][h]; bf16, f32 or f64)."""
+    xa, dx = _np(x)
+    wa, dw = _np(W_router)
+    T, h = xa.shape
+    E, h2 = wa.shape
+    if h2 != h or ORC_FP8E4M3 in (dx, dw):
+        raise ValueError("x [T][h] and W_router [E][h] (bf16, f32 or f64)")
+    out = np.zeros((T, E), np.float64)
+    dtarr = (ctypes.c_int32 * 2)(dx, dw)
+    _check(lib().oracle_router_logits(_ptr(xa), _ptr(wa), dtarr, T, h, E, _ptr(out)), "oracle_router_logits")
+    return out
 
 
 def sgmv(x, A, B, y_in, adapter_ids) -> np.ndarray:

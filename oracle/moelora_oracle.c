@@ -382,6 +382,32 @@ int oracle_sgmv(const void *x, const void *A, const void *B, const void *y_in, c
   return status;
 }
 
+/* Router logits: logits[t][e] = sum_c x[t][c] W_router[e][c] (page "vLLM MoE LoRA SageMaker
+ * Bedrock", section "Entendendo os Modelos MoE": a router scores every expert for each token
+ * before the top-k selection). x [T][h], W_router [E][h]; dtypes in dt[0], dt[1]. */
+int oracle_router_logits(const void *x, const void *W_router, const int32_t *dt, int32_t T,
+                         int32_t h, int32_t E, double *logits) {
+  if (T < 0 || h <= 0 || E <= 0) return ORC_EINVAL;
+  int status = ORC_OK;
+#pragma omp parallel
+  {
+    double *xr = (double *)malloc(sizeof(double) * (size_t)h);
+    if (!xr) {
+#pragma omp atomic write
+      status = ORC_ENOMEM;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int32_t t = 0; t < T; ++t) {
+        for (int32_t c = 0; c < h; ++c) xr[c] = ld(x, dt[0], (size_t)t * h + c);
+        for (int32_t e = 0; e < E; ++e)
+          logits[(size_t)t * E + e] = dot_row(xr, W_router, dt[1], (size_t)e * h, h);
+      }
+    }
+    free(xr);
+  }
+  return status;
+}
+
 /* E4M3 codes decoded to float64, for the tests. */
 int oracle_fp8e4m3_decode(const uint8_t *codes, int64_t n, double *out) {
   for (int64_t i = 0; i < n; ++i) out[i] = fp8e4m3_to_f64(codes[i]);

@@ -393,3 +393,15 @@ def test_sgmv_onto_zero_is_shrink_then_expand():
         a = int(ad[t])
         want = np.zeros(2 * I) if a < 0 else Bn[a] @ (An[a] @ xn[t])
         np.testing.assert_allclose(z[t], want, rtol=1e-12, atol=1e-13)
+
+
+# ----------------------------------------------------------------------------- router logits
+
+@pytest.mark.parametrize("dtype", [torch.float64, torch.bfloat16])
+def test_router_logits_vs_numpy(dtype):
+    g = torch.Generator().manual_seed(11)
+    x = torch.randn(23, 160, generator=g).to(dtype)
+    W = torch.randn(12, 160, generator=g).to(dtype)
+    got = oracle.router_logits(x, W)
+    want = x.double().numpy() @ W.double().numpy().T
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
