@@ -110,6 +110,22 @@ int moe_lora_forward_timed(const void *x, const float *router_logits, const void
                            const moe_lora_dims *d, void *y, void *workspace,
                            size_t workspace_bytes, void *stream, void *const *stage_events);
 
+/* Router logits (page "vLLM MoE LoRA SageMaker Bedrock", section "Entendendo os Modelos MoE":
+ * the router scores every expert for each token): logits[t][e] = sum_c x[t][c] W_router[e][c],
+ * bf16 inputs x [T][hidden] and W_router [n_experts][hidden] (16-byte aligned), fp32 sums,
+ * logits [T][n_experts] float32. hidden a positive multiple of 128, n_experts in [1, 1024].
+ * Asynchronous on `stream`. */
+int moe_lora_router_logits(const void *x, const void *W_router, int32_t T, int32_t hidden,
+                           int32_t n_experts, float *logits, void *stream);
+
+/* moe_lora_forward starting from the router weights: the logits of moe_lora_router_logits go
+ * into the workspace (moe_lora_workspace_size covers them) and the layer runs from them, so the
+ * result equals moe_lora_forward on those logits. */
+int moe_lora_forward_routed(const void *x, const void *W_router, const void *W1, const void *W2,
+                            const void *A1, const void *B1, const void *A2, const void *B2,
+                            const int32_t *adapter_ids, int32_t topk, const moe_lora_dims *d,
+                            void *y, void *workspace, size_t workspace_bytes, void *stream);
+
 /* moe_lora_forward with FP8 expert weights (page "AWS SageMaker MoE kernel optimizations",
  * third paragraph: FP8 expert weights, their scales applied on the way into the expert
  * GEMMs). W1q [E][2I][h] and W2q [E][h][I] hold OCP E4M3 codes (1 byte each: sign, 4 exponent

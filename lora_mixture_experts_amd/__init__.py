@@ -21,7 +21,8 @@ FLAG_NONFINITE_LOGIT, FLAG_ADAPTER_RANGE = 1, 2
 
 EXPORTS = ("moe_lora_workspace_size", "moe_lora_forward", "moe_lora_forward_timed", "moe_lora_forward_fp8",
            "moe_lora_sorted_capacity", "moe_lora_route_align", "moe_lora_strerror",
-           "moe_lora_debug_status", "moe_lora_sgmv_workspace_size", "moe_lora_sgmv")
+           "moe_lora_debug_status", "moe_lora_sgmv_workspace_size", "moe_lora_sgmv",
+           "moe_lora_router_logits", "moe_lora_forward_routed")
 N_STAGES = 7
 STAGES = ("route", "align", "shrink_gate_up", "gate_up", "shrink_down", "down", "combine")
 
@@ -62,6 +63,10 @@ def lib() -> ctypes.CDLL:
         L.moe_lora_forward_fp8.argtypes = [P, P, P, P, P, P, P, P, P, P, P, i32, D, P, P, ctypes.c_size_t, P,
                                            ctypes.POINTER(ctypes.c_void_p)]
         L.moe_lora_forward_fp8.restype = ctypes.c_int
+        L.moe_lora_router_logits.argtypes = [P, P, i32, i32, i32, P, P]
+        L.moe_lora_router_logits.restype = ctypes.c_int
+        L.moe_lora_forward_routed.argtypes = [P, P, P, P, P, P, P, P, P, i32, D, P, P, ctypes.c_size_t, P]
+        L.moe_lora_forward_routed.restype = ctypes.c_int
         L.moe_lora_sgmv_workspace_size.argtypes = [ctypes.POINTER(SgmvDims)]
         L.moe_lora_sgmv_workspace_size.restype = ctypes.c_size_t
         L.moe_lora_sgmv.argtypes = [P, P, P, P, ctypes.POINTER(SgmvDims), P, P, ctypes.c_size_t, P]
@@ -169,6 +174,45 @@ def forward(x, router_logits, W1, W2, A1, B1, A2, B2, adapter_ids, topk: int, y=
         handles = (ctypes.c_void_p * (N_STAGES + 1))(
             *[ev.cuda_event if ev is not None else None for ev in stage_events])
         _check(lib().moe_lora_forward_timed(*args, handles), "moe_lora_forward_timed")
+    return y
+
+
+def router_logits(x, W_router) -> torch.Tensor:
+    """logits [T][E] float32 = x W_router^T (moe_lora_router_logits)."""
+    T, h = x.shape
+    E = W_router.shape[0]
+    _expect(x, "x", torch.bfloat16, (T, h))
+    _expect(W_router, "W_router", torch.bfloat16, (E, h))
+    out = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    _check(lib().moe_lora_router_logits(_ptr(x), _ptr(W_router), T, h, E, _ptr(out), _stream(x.device)),
+           "moe_lora_router_logits")
+    return out
+
+
+def forward_routed(x, W_router, W1, W2, A1, B1, A2, B2, adapter_ids, topk: int, y=None,
+                   workspace=None) -> torch.Tensor:
+    """forward starting from the router weights W_router [E][h] (moe_lora_forward_routed)."""
+    d = dims_of(x, W1, A1)
+    T, h, I, E, nA, r = d.T, d.hidden, d.inter, d.n_experts, d.n_adapters, d.rank
+    bf = torch.bfloat16
+    _expect(x, "x", bf, (T, h))
+    _expect(W_router, "W_router", bf, (E, h))
+    _expect(W1, "W1", bf, (E, 2 * I, h))
+    _expect(W2, "W2", bf, (E, h, I))
+    _expect(A1, "A1", bf, (nA, E, r, h))
+    _expect(B1, "B1", bf, (nA, E, 2 * I, r))
+    _expect(A2, "A2", bf, (nA, E, r, I))
+    _expect(B2, "B2", bf, (nA, E, h, r))
+    _expect(adapter_ids, "adapter_ids", torch.int32, (T,))
+    if y is None:
+        y = torch.empty((T, h), dtype=bf, device=x.device)
+    _expect(y, "y", bf, (T, h))
+    if workspace is None:
+        workspace = new_workspace(d, topk, x.device)
+    _check(lib().moe_lora_forward_routed(_ptr(x), _ptr(W_router), _ptr(W1), _ptr(W2), _ptr(A1), _ptr(B1),
+                                         _ptr(A2), _ptr(B2), _ptr(adapter_ids), topk, ctypes.byref(d),
+                                         _ptr(y), _ptr(workspace), workspace.numel(), _stream(x.device)),
+           "moe_lora_forward_routed")
     return y
 
 

@@ -245,6 +245,7 @@ bool moelora_make_layout(int T, int h, int I, int E, int nA, int r, int topk, Mo
   L->act = take(2 * (size_t)L->cap * I);
   L->dpair = take(4 * (size_t)kMaxDownSplit * L->cap * h);
   L->align_lists = take(4 * align_list_ints(T, topk, E, nA));
+  L->logits = take(4 * (size_t)T * E);
   L->total = off;
   return true;
 }
@@ -537,6 +538,43 @@ int moe_lora_forward_timed(const void* x, const float* router_logits, const void
   if (!stage_events) return MOELORA_ENULL;
   return forward_impl(x, router_logits, W1, W2, A1, B1, A2, B2, adapter_ids, topk, d, y, workspace,
                       workspace_bytes, stream, stage_events);
+}
+
+int moe_lora_router_logits(const void* x, const void* W_router, int32_t T, int32_t hidden,
+                           int32_t n_experts, float* logits, void* stream) {
+  if (T < 0 || hidden <= 0 || hidden % 128 != 0 || n_experts < 1 || n_experts > kMaxExperts)
+    return MOELORA_EINVAL_DIMS;
+  if ((int64_t)T * hidden * 2 >= ((int64_t)1 << 31) ||
+      (int64_t)n_experts * hidden * 2 >= ((int64_t)1 << 31))
+    return MOELORA_EINVAL_DIMS;
+  if (T == 0) return MOELORA_OK;
+  if (!x || !W_router || !logits) return MOELORA_ENULL;
+  if (!aligned16(x) || !aligned16(W_router) || ((uintptr_t)logits & 3u) != 0) return MOELORA_EALIGN;
+  const int rc = check_device();
+  if (rc != MOELORA_OK) return rc;
+  return launch_router_logits((const uint16_t*)x, (const uint16_t*)W_router, T, hidden, n_experts,
+                              logits, (hipStream_t)stream) == hipSuccess
+             ? MOELORA_OK
+             : MOELORA_EHIP;
+}
+
+int moe_lora_forward_routed(const void* x, const void* W_router, const void* W1, const void* W2,
+                            const void* A1, const void* B1, const void* A2, const void* B2,
+                            const int32_t* adapter_ids, int32_t topk, const moe_lora_dims* d,
+                            void* y, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = validate_dims(d, topk);
+  if (rc != MOELORA_OK) return rc;
+  if (d->T == 0) return MOELORA_OK;
+  if (!workspace || !W_router) return MOELORA_ENULL;
+  if (((uintptr_t)workspace & 255u) != 0) return MOELORA_EWORKSPACE;
+  MoeLoraLayout L;
+  moelora_make_layout(d->T, d->hidden, d->inter, d->n_experts, d->n_adapters, d->rank, topk, &L);
+  if (workspace_bytes < L.total) return MOELORA_EWORKSPACE;
+  float* logits = (float*)((char*)workspace + L.logits);
+  rc = moe_lora_router_logits(x, W_router, d->T, d->hidden, d->n_experts, logits, stream);
+  if (rc != MOELORA_OK) return rc;
+  return forward_impl(x, logits, W1, W2, A1, B1, A2, B2, adapter_ids, topk, d, y, workspace,
+                      workspace_bytes, stream, nullptr);
 }
 
 int moe_lora_forward_fp8(const void* x, const float* router_logits, const void* W1q,

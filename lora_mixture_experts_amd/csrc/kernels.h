@@ -140,6 +140,8 @@ struct SkinnyConfig {
 hipError_t launch_route(const float* logits, int T, int E, int k, int* topk_ids, float* topk_w,
                         int* tok_flags, hipStream_t stream);
 hipError_t launch_align(const AlignArgs& a, size_t dyn_lds, hipStream_t stream);
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* W, int T, int K, int E,
+                                float* logits, hipStream_t stream);
 hipError_t launch_shrink(bool gather, const ShrinkArgs& a, int tiles, hipStream_t stream);
 hipError_t launch_shrink_tiled(bool gather, const ShrinkArgs& a, int n_sub_max,
                                hipStream_t stream);

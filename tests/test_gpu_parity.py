@@ -448,3 +448,44 @@ def test_sgmv_empty_and_bad_adapters():
     assert ml.debug_status(ws) == ml.FLAG_ADAPTER_RANGE
     e = torch.zeros(0, 64, dtype=torch.bfloat16, device=DEV)
     ml.sgmv(x[:0].to(DEV), A.to(DEV), B.to(DEV), ad[:0].to(DEV), e)
+
+
+# ----------------------------------------------------------------------------- router GEMM
+
+@pytest.mark.parametrize("T,h,E", [(37, 256, 8), (64, 4096, 16), (256, 2048, 128), (1, 128, 1),
+                                   (300, 384, 200)])
+def test_router_logits_vs_oracle(T, h, E):
+    """fp32 logits within a rounding bound of the float64 dot products: 3e-5 of the sum of the
+    products' magnitudes (a dropped or wrong K chunk moves a logit by far more)."""
+    g = torch.Generator().manual_seed(T + E)
+    x = torch.randn(T, h, generator=g).to(torch.bfloat16)
+    W = (torch.randn(E, h, generator=g) * 0.02).to(torch.bfloat16)
+    got = ml.router_logits(x.to(DEV), W.to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle.router_logits(x, W)
+    bound = 3e-5 * (np.abs(x.double().numpy()) @ np.abs(W.double().numpy()).T) + 1e-30
+    err = np.abs(got.cpu().double().numpy() - ref)
+    assert np.all(err <= bound), float((err / bound).max())
+
+
+@pytest.mark.parametrize("name", ["ragged", "fg_small", "tiled64"])
+def test_forward_routed_equals_forward_on_its_logits(name):
+    """The layer from router weights equals the layer on the router kernel's logits, bit for
+    bit, and routing on those fp32 logits matches the oracle's selection on the same values."""
+    w = SMALL[name]
+    inp = {k: v.to(DEV) for k, v in _small_inputs(w, 8).items()}
+    Wr = (torch.randn(w.n_experts, w.hidden, generator=torch.Generator().manual_seed(5)) * 0.5).to(
+        torch.bfloat16).to(DEV)
+    keys = ("W1", "W2", "A1", "B1", "A2", "B2", "adapter_ids")
+    y_r = ml.forward_routed(inp["x"], Wr, *[inp[k] for k in keys], w.topk)
+    logits = ml.router_logits(inp["x"], Wr)
+    y_f = ml.forward(inp["x"], logits, *[inp[k] for k in keys], w.topk)
+    torch.cuda.synchronize()
+    assert torch.equal(y_r, y_f)
+    ra = ml.route_align(logits, inp["adapter_ids"], w.topk, _dims(w), 1, 1)
+    torch.cuda.synchronize()
+    ids_ref, _ = oracle.route(logits.cpu(), w.topk)
+    np.testing.assert_array_equal(ra["topk_ids"].cpu().numpy(), ids_ref)
+    host = {k: v.cpu() for k, v in inp.items()}
+    host["logits"] = logits.cpu()
+    check_close(y_r, oracle_rows(host, w.topk), what=f"routed {name}")
