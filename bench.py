@@ -8,14 +8,17 @@ seeded synthetic input already resident in HBM. Prints one JSON line.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode] [--fp8]
 
 --fp8 runs the FP8 entry point (E4M3 expert weights with per-row scales, moe_lora_forward_fp8)
-on the decode-sized workloads (decode, fg, tiny). --workload sgmv measures the dense
-multi-LoRA entry point (moe_lora_sgmv) instead of the layer.
+on the decode-sized workloads (decode, fg, tiny). --routed starts each step from router weights
+(moe_lora_forward_routed: the router GEMM joins the step; the logits come from a seeded router
+weight scaled to unit spread, so the workload's own logits, and fg's hot experts, are not used).
+--workload sgmv measures the dense multi-LoRA entry point (moe_lora_sgmv) instead of the layer.
 """
 from __future__ import annotations
 
 import argparse
 import hashlib
 import json
+import math
 import os
 import statistics
 import sys
@@ -191,6 +194,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fp8", action="store_true",
                     help="E4M3 expert weights with per-row scales (decode-sized workloads)")
+    ap.add_argument("--routed", action="store_true",
+                    help="start from router weights: moe_lora_forward_routed (router GEMM in the step)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run a device-to-device copy of this size first (counter calibration)")
     args = ap.parse_args()
@@ -226,17 +231,42 @@ def main():
     if args.fp8 and w.T * w.topk > 24 * w.n_experts:
         print("--fp8 covers workloads of at most 24 token-expert pairs per expert", file=sys.stderr)
         sys.exit(2)
+    if args.fp8 and args.routed:
+        print("--routed covers the bf16 entry point", file=sys.stderr)
+        sys.exit(2)
     inp = (configs.make_inputs_fp8 if args.fp8 else configs.make_inputs)(w, args.seed, device=dev)
+    Wr = None
+    if args.routed:
+        # router weight whose logits x W_router^T have about unit spread (like the workload's)
+        g = torch.Generator().manual_seed(args.seed + 7)
+        sx = float(inp["x"].float().std())
+        Wr = (torch.randn(w.n_experts, w.hidden, generator=g) / (sx * math.sqrt(w.hidden))).to(
+            torch.bfloat16).to(dev)
+        inp["logits"] = ml.router_logits(inp["x"], Wr)  # what the routed entry computes
     d = ml.Dims(w.T, w.hidden, w.inter, w.n_experts, w.n_adapters, w.rank)
     ws = ml.new_workspace(d, w.topk, dev)
     y = torch.empty((w.T, w.hidden), dtype=torch.bfloat16, device=dev)
 
     ra = ml.route_align(inp["logits"], inp["adapter_ids"], w.topk, d, 1, 1, workspace=ws)
     work = algorithmic_work(w, ra["seg_table"], int(ra["n_seg"].item()), ra["topk_ids"], args.fp8)
+    if args.routed:  # the router weight read and the router GEMM
+        work["layer_bytes"] += 2 * w.n_experts * w.hidden
+        work["layer_flops"] += 2 * w.T * w.hidden * w.n_experts
     del ra
 
+    keys = ("W1", "W2", "A1", "B1", "A2", "B2", "adapter_ids")
+
     def step(events=None):
-        if args.fp8:
+        if args.routed and events is None:
+            ml.forward_routed(inp["x"], Wr, *[inp[k] for k in keys], w.topk, y=y, workspace=ws)
+        elif args.routed:
+            # the routed entry's kernels, with the router GEMM and every stage boundary timed
+            events[-1][0].record()
+            ml.router_logits(inp["x"], Wr, out=inp["logits"])
+            events[-1][1].record()
+            ml.forward(inp["x"], inp["logits"], *[inp[k] for k in keys], w.topk, y=y, workspace=ws,
+                       stage_events=events[:-1])
+        elif args.fp8:
             ml.forward_fp8(inp["x"], inp["logits"], inp["W1"], inp["W1_scale"], inp["W2"],
                            inp["W2_scale"], inp["A1"], inp["B1"], inp["A2"], inp["B2"],
                            inp["adapter_ids"], w.topk, y=y, workspace=ws, stage_events=events)
@@ -253,31 +283,48 @@ def main():
     # a separate pass after the timed region.
     K = args.steps
     GU = ml.STAGES.index("gate_up")
-    gu_events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
-    for evs in gu_events:  # create the HIP events outside the timed region
-        for ev in evs:
-            ev.record()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        evs = [None] * (ml.N_STAGES + 1)
-        evs[GU], evs[GU + 1] = gu_events[i]
-        step(evs)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    gu_ms = statistics.fmean(a.elapsed_time(b) for a, b in gu_events)
+    if args.routed:
+        # the routed entry records no stage events: gate_up and the router GEMM are timed in the
+        # breakdown pass below, over the same kernels
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            step()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+    else:
+        gu_events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+        for evs in gu_events:  # create the HIP events outside the timed region
+            for ev in evs:
+                ev.record()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            evs = [None] * (ml.N_STAGES + 1)
+            evs[GU], evs[GU + 1] = gu_events[i]
+            step(evs)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        gu_ms = statistics.fmean(a.elapsed_time(b) for a, b in gu_events)
 
     # stage breakdown (diagnostics): a few more calls with every boundary recorded
-    NB = min(K, 5)
+    NB = min(K, 5) if not args.routed else K
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(ml.N_STAGES + 1)] for _ in range(NB)]
+    if args.routed:
+        for evs in events:
+            evs.append([torch.cuda.Event(enable_timing=True) for _ in range(2)])
     for i in range(NB):
         step(events[i])
     torch.cuda.synchronize()
     stage_ms = {name: [] for name in ml.STAGES}
+    if args.routed:
+        stage_ms = {"router": [evs[-1][0].elapsed_time(evs[-1][1]) for evs in events], **stage_ms}
     for evs in events:
         for s, name in enumerate(ml.STAGES):
             stage_ms[name].append(evs[s].elapsed_time(evs[s + 1]))
     stage_avg = {k: statistics.fmean(v) for k, v in stage_ms.items()}
+    if args.routed:
+        gu_ms = stage_avg["gate_up"]
 
     ms_per_step = elapsed * 1e3 / K
     value = w.T * K / elapsed
@@ -294,7 +341,8 @@ def main():
     # the library takes the LDS-tiled GEMM above 24 rows per expert on average
     tiled = w.T * w.topk > 24 * w.n_experts
     roof["kernel"] = ("tiled_gemm_kernel" if tiled else "skinny_gemm_kernel") + " (gate_up)"
-    roof["traffic"] = measured_traffic(args.workload + ("_fp8" if args.fp8 else ""))
+    roof["traffic"] = measured_traffic(args.workload + ("_fp8" if args.fp8 else "")
+                                       + ("_routed" if args.routed else ""))
 
     layer_s = elapsed / K
     out = {
@@ -313,7 +361,8 @@ def main():
         "config": {"workload": w.name, "T": w.T, "hidden": w.hidden, "inter": w.inter,
                    "n_experts": w.n_experts, "topk": w.topk, "n_adapters": w.n_adapters,
                    "rank": w.rank, "adapters": w.adapters, "seed": args.seed,
-                   "expert_weights": "e4m3 + per-row fp32 scale" if args.fp8 else "bf16"},
+                   "expert_weights": "e4m3 + per-row fp32 scale" if args.fp8 else "bf16",
+                   "logits": "x W_router^T (routed entry)" if args.routed else "given"},
         "roofline": roof,
         "layer": {"bytes": work["layer_bytes"], "flops": work["layer_flops"],
                   "ms": layer_s * 1e3,

@@ -177,13 +177,15 @@ def forward(x, router_logits, W1, W2, A1, B1, A2, B2, adapter_ids, topk: int, y=
     return y
 
 
-def router_logits(x, W_router) -> torch.Tensor:
-    """logits [T][E] float32 = x W_router^T (moe_lora_router_logits)."""
+def router_logits(x, W_router, out=None) -> torch.Tensor:
+    """logits [T][E] float32 = x W_router^T (moe_lora_router_logits), into `out` if given."""
     T, h = x.shape
     E = W_router.shape[0]
     _expect(x, "x", torch.bfloat16, (T, h))
     _expect(W_router, "W_router", torch.bfloat16, (E, h))
-    out = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    if out is None:
+        out = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    _expect(out, "out", torch.float32, (T, E))
     _check(lib().moe_lora_router_logits(_ptr(x), _ptr(W_router), T, h, E, _ptr(out), _stream(x.device)),
            "moe_lora_router_logits")
     return out

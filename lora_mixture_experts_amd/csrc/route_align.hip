@@ -492,49 +492,52 @@ __global__ __launch_bounds__(1024) void align_kernel(AlignArgs a) {
 // ------------------------------------------------------------------------------------------
 // Router logits, logits[t][e] = sum_c x[t][c] W_router[e][c] in fp32 (page "vLLM MoE LoRA
 // SageMaker Bedrock", section "Entendendo os Modelos MoE": the router scores every expert for
-// each token). One workgroup per (16 tokens, 16 experts); its four wavefronts take a quarter of
-// K each, 16x16x32 bf16 MFMAs with the router rows on the A side and the token rows on the B
-// side, the loads of four K chunks issued together; the four partial tiles are added in wave
-// order through LDS. Token rows past T and expert rows past E load zeros and are not stored.
+// each token). One workgroup per (16 tokens, 16 experts): 16x16x32 bf16 MFMAs with the router
+// rows on the A side and the token rows on the B side. The product is latency-bound (a decode
+// batch is a handful of tiles), so the workgroup's sixteen wavefronts take the 32-wide K chunks
+// in turn (chunk c to wavefront c % 16) and each issues the loads of up to eight of its chunks
+// before their MFMAs: K = 4096 costs one memory round trip. The sixteen partial tiles are added
+// in wavefront order through LDS. Token rows past T and expert rows past E load zeros and are
+// not stored.
 // ------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
-                                                            uint32_t x_bytes,
-                                                            const uint16_t* __restrict__ W,
-                                                            uint32_t w_bytes, int T, int K, int E,
-                                                            float* __restrict__ logits) {
+constexpr int kRouterWaves = 16;
+
+__global__ __launch_bounds__(64 * kRouterWaves) void router_logits_kernel(
+    const uint16_t* __restrict__ x, uint32_t x_bytes, const uint16_t* __restrict__ W,
+    uint32_t w_bytes, int T, int K, int E, float* __restrict__ logits) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m = lane & 15, kq = lane >> 4;
   const int tok = blockIdx.x * 16 + m, erow = blockIdx.y * 16 + m;
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, x_bytes), wr = make_rsrc(W, w_bytes);
   const uint32_t xo = tok < T ? (uint32_t)((size_t)tok * K * 2) : kOutOfRange;
   const uint32_t wo = erow < E ? (uint32_t)((size_t)erow * K * 2) : kOutOfRange;
-  const int kw = K / 4;  // a multiple of 32
-  const int k0 = wave * kw, k1 = k0 + kw;
+  const int nch = K / 32;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  int kb = k0;
-  for (; kb + 128 <= k1; kb += 128) {
-    u32x4 xa[4], wa[4];
+  int c = wave;
+  for (; c + kRouterWaves * 7 < nch; c += kRouterWaves * 8) {
+    u32x4 xa[8], wa[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t kk = (uint32_t)(kb + 32 * j + 8 * kq) * 2;
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t kk = (uint32_t)((c + kRouterWaves * j) * 32 + 8 * kq) * 2;
       xa[j] = bufld16(xr, xo + kk);
       wa[j] = bufld16(wr, wo + kk);
     }
+    __builtin_amdgcn_sched_barrier(0);  // all sixteen loads in flight before the first MFMA
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc = mfma16(wa[j], xa[j], acc);
+    for (int j = 0; j < 8; ++j) acc = mfma16(wa[j], xa[j], acc);
   }
-  for (; kb < k1; kb += 32) {
-    const uint32_t kk = (uint32_t)(kb + 8 * kq) * 2;
+  for (; c < nch; c += kRouterWaves) {
+    const uint32_t kk = (uint32_t)(c * 32 + 8 * kq) * 2;
     acc = mfma16(bufld16(wr, wo + kk), bufld16(xr, xo + kk), acc);
   }
   // acc[v]: expert blockIdx.y*16 + 4 kq + v, token blockIdx.x*16 + m
-  __shared__ f32x4 s_part[4][64];
+  __shared__ f32x4 s_part[kRouterWaves][64];
   s_part[wave][lane] = acc;
   __syncthreads();
   if (wave == 0) {
     f32x4 t = s_part[0][lane];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) t += s_part[w][lane];
+    for (int w = 1; w < kRouterWaves; ++w) t += s_part[w][lane];
     if (tok < T) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
@@ -554,7 +557,7 @@ hipError_t launch_router_logits(const uint16_t* x, const uint16_t* W, int T, int
   if (T <= 0) return hipSuccess;
   if (K % 128 != 0) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((T + 15) / 16), (unsigned)((E + 15) / 16));
-  hipLaunchKernelGGL(router_logits_kernel, grid, dim3(256), 0, stream, x,
+  hipLaunchKernelGGL(router_logits_kernel, grid, dim3(64 * kRouterWaves), 0, stream, x,
                      (uint32_t)((size_t)T * K * 2), W, (uint32_t)((size_t)E * K * 2), T, K, E,
                      logits);
   return hipGetLastError();
