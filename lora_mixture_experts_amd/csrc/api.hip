@@ -438,8 +438,11 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   if (launch_shrink(true, sh, tiles16, stream) != hipSuccess) return MOELORA_EHIP;
   float* zsum = (float*)(ws + L.zsum);
   uint16_t* zhl = path.tiled ? (uint16_t*)(ws + L.zhl) : nullptr;
-  if (launch_zfinal(z1, s1, L.cap, r, n_blocks, bm, (int64_t)max_blocks * bm, zsum, zhl, stream) !=
-      hipSuccess)
+  // the skinny GEMMs add the split parts themselves (one launch fewer per projection); the
+  // tiled GEMMs take z as bf16 high and low planes, made by zfinal
+  if (path.tiled &&
+      launch_zfinal(z1, s1, L.cap, r, n_blocks, bm, (int64_t)max_blocks * bm, zsum, zhl, stream) !=
+          hipSuccess)
     return MOELORA_EHIP;
   if (!mark(ev, 3, stream)) return MOELORA_EHIP;
   g.X = (const uint16_t*)x;
@@ -450,6 +453,8 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   g.Bw = (const uint16_t*)B1;
   g.zsum = zsum;
   g.zhl = zhl;
+  g.zpart = z1;
+  g.zsplits = path.tiled ? 0 : s1;
   g.K = h;
   g.N = I;
   SkinnyPlan plan = pick_skinny(nt, h, I);
@@ -491,9 +496,12 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   if (shrink64 && launch_shrink_tiled(false, sh, n_sub_max, stream) != hipSuccess)
     return MOELORA_EHIP;
   if (launch_shrink(false, sh, tiles16, stream) != hipSuccess) return MOELORA_EHIP;
-  if (launch_zfinal(z2, s2, L.cap, r, n_blocks, bm, (int64_t)max_blocks * bm, zsum, zhl, stream) !=
-      hipSuccess)
+  if (path.tiled &&
+      launch_zfinal(z2, s2, L.cap, r, n_blocks, bm, (int64_t)max_blocks * bm, zsum, zhl, stream) !=
+          hipSuccess)
     return MOELORA_EHIP;
+  g.zpart = z2;
+  g.zsplits = path.tiled ? 0 : s2;
   if (!mark(ev, 5, stream)) return MOELORA_EHIP;
   g.X = act;
   g.x_bytes = (uint32_t)((size_t)L.cap * I * 2);

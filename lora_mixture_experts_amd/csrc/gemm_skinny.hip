@@ -104,17 +104,35 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs a) {
   const int zsplit = blockIdx.z;
   constexpr int BMZ = 16 * NT;
 
-  // The block's z rows (the shrink's split parts already added) go into LDS for the epilogue
-  // (rows without an adapter hold values nobody reads). Only K split 0 of down adds the LoRA
-  // term. Run after the first weight loads are issued, so the two latencies overlap. (The grid
-  // covers N exactly: every wavefront has columns.)
+  // The block's z rows go into LDS for the epilogue (rows without an adapter hold values nobody
+  // reads): the sum of the shrink's K-split parts, added here in split order (a.zsplits > 0),
+  // or already added (a.zsum). Only K split 0 of down adds the LoRA term. Run after the first
+  // weight loads are issued, so the two latencies overlap. (The grid covers N exactly: every
+  // wavefront has columns.)
   __shared__ __attribute__((aligned(16))) float s_z[BMZ * 64];
   auto z_prologue = [&]() {
     if (zsplit != 0) return;
     const int nz = BMZ * a.r;
-    const float* zp = a.zsum + (size_t)blk * BMZ * a.r;
-    for (int i = threadIdx.x * 4; i < nz; i += 256 * 4)
-      *reinterpret_cast<f32x4*>(s_z + i) = *reinterpret_cast<const f32x4*>(zp + i);
+    const size_t off = (size_t)blk * BMZ * a.r;
+    if (a.zsplits > 0) {
+      // every part's load is issued before the first add (parts past zsplits re-read the last
+      // one and are not added), so the sum costs one memory round trip
+      const size_t part = (size_t)a.cap * a.r;
+      for (int i = threadIdx.x * 4; i < nz; i += 256 * 4) {
+        f32x4 zz[kMaxSplit];
+#pragma unroll
+        for (int sp = 0; sp < kMaxSplit; ++sp)
+          zz[sp] = *reinterpret_cast<const f32x4*>(a.zpart + min(sp, a.zsplits - 1) * part + off + i);
+        f32x4 z = zz[0];
+#pragma unroll
+        for (int sp = 1; sp < kMaxSplit; ++sp)
+          if (sp < a.zsplits) z += zz[sp];
+        *reinterpret_cast<f32x4*>(s_z + i) = z;
+      }
+    } else {
+      for (int i = threadIdx.x * 4; i < nz; i += 256 * 4)
+        *reinterpret_cast<f32x4*>(s_z + i) = *reinterpret_cast<const f32x4*>(a.zsum + off + i);
+    }
     __syncthreads();
   };
   const size_t N = (size_t)a.N;

@@ -87,7 +87,9 @@ struct GemmArgs {
   const uint8_t* W8;   // skinny FP8 entry: the same weights as E4M3 codes (W unused)
   const float* wscale; // with W8: one scale per weight row ([E][2I] or [E][h])
   const uint16_t* Bw;  // gate_up: B1 [nA][E][2I][r]; down: B2 [nA][E][h][r]
-  const float* zsum;    // skinny: [cap][r] LoRA shrink output (its split parts added)
+  const float* zsum;    // [cap][r] LoRA shrink output (its split parts added), when zsplits = 0
+  const float* zpart;   // skinny: [zsplits][cap][r] the shrink's split parts, added in the
+  int zsplits;          //   prologue in split order (zsum unused) when zsplits > 0
   const uint16_t* zhl;  // tiled: [2][cap][r] the same as bf16 high and low planes
   int64_t cap;
   const int* sorted_pairs;
