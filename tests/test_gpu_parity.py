@@ -453,7 +453,7 @@ def test_sgmv_empty_and_bad_adapters():
 # ----------------------------------------------------------------------------- router GEMM
 
 @pytest.mark.parametrize("T,h,E", [(37, 256, 8), (64, 4096, 16), (256, 2048, 128), (1, 128, 1),
-                                   (300, 384, 200)])
+                                   (300, 384, 200), (4096, 4096, 8), (16, 8192, 32), (5, 640, 3)])
 def test_router_logits_vs_oracle(T, h, E):
     """fp32 logits within a rounding bound of the float64 dot products: 3e-5 of the sum of the
     products' magnitudes (a dropped or wrong K chunk moves a logit by far more)."""
