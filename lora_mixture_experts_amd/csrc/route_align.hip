@@ -98,18 +98,25 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
 
 // Route for up to 256 experts: the rank of each logit, the number of logits that beat it
 // (larger, or equal with a lower expert id), is its slot when it is below k, which is the same
-// selection as k rounds of arg-max. The wavefront stages the token's logits in LDS and every lane
-// counts, for its (up to VPL) logits, how many of the E staged ones beat it: broadcast reads, no
-// cross-lane reductions. Non-finite logits are flagged and take part as -infinity.
+// selection as k rounds of arg-max. The token's logits are staged in LDS and every lane counts,
+// for its (up to VPL) logits, how many of the E staged ones beat it: broadcast reads, no
+// cross-lane reductions. Up to 64 experts a wavefront takes one token (four per workgroup);
+// above, the four wavefronts of a workgroup share one token and each counts against a quarter
+// of the logits (the counts are added through LDS), which keeps the serial compare chain per
+// wavefront at E/4. Non-finite logits are flagged and take part as -infinity.
 template <int VPL>
 __global__ __launch_bounds__(256) void route_rank_kernel(const float* __restrict__ logits, int T,
                                                          int E, int k, int* __restrict__ topk_ids,
                                                          float* __restrict__ topk_w,
                                                          int* __restrict__ tok_flags) {
-  __shared__ __attribute__((aligned(16))) float s_l[4][64 * VPL];
-  __shared__ float s_sel[4][kMaxTopk];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int t = blockIdx.x * 4 + w;
+  constexpr int TPB = VPL == 1 ? 4 : 1;  // tokens per workgroup
+  constexpr int WPT = 4 / TPB;           // wavefronts per token
+  __shared__ __attribute__((aligned(16))) float s_l[TPB][64 * VPL];
+  __shared__ int s_rank[WPT][64 * VPL];
+  __shared__ float s_sel[TPB][kMaxTopk];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int w = wv / WPT, part = wv % WPT;  // token slot, quarter of the comparisons
+  const int t = blockIdx.x * TPB + w;
   const bool active = t < T;  // (no early exit: every wavefront reaches the barriers)
   const float* row = logits + (size_t)(active ? t : 0) * E;
   float v[VPL];
@@ -126,19 +133,21 @@ __global__ __launch_bounds__(256) void route_rank_kernel(const float* __restrict
       }
     }
     v[i] = f;
-    s_l[w][e] = f;  // (slots past E hold -infinity and are never counted)
+    if (part == 0) s_l[w][e] = f;  // (slots past E hold -infinity and are never counted)
   }
   __syncthreads();
   int rank[VPL];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) rank[i] = 0;
-  const int e4 = (E + 3) & ~3;
-  for (int c = 0; c < e4; c += 4) {
+  // this wavefront's compare range [c0, c1): quarters rounded to whole 16-byte LDS reads
+  const int eq = WPT == 1 ? E : ((E + 4 * WPT - 1) / (4 * WPT)) * 4;
+  const int c0 = part * eq, c1 = min(E, c0 + eq);
+  for (int c = c0; c < c1; c += 4) {
     const f32x4 o = *reinterpret_cast<const f32x4*>(&s_l[w][c]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int eo = c + j;
-      if (eo >= E) break;
+      if (eo >= c1) break;
 #pragma unroll
       for (int i = 0; i < VPL; ++i) {
         const int e = lane + 64 * i;
@@ -146,17 +155,30 @@ __global__ __launch_bounds__(256) void route_rank_kernel(const float* __restrict
       }
     }
   }
-  const uint64_t anybad = __ballot(bad);
+  if (WPT > 1) {
 #pragma unroll
-  for (int i = 0; i < VPL; ++i) {
-    const int e = lane + 64 * i;
-    if (active && e < E && rank[i] < k) {
-      topk_ids[(size_t)t * k + rank[i]] = e;
-      s_sel[w][rank[i]] = v[i];
+    for (int i = 0; i < VPL; ++i) s_rank[part][lane + 64 * i] = rank[i];
+    __syncthreads();
+    if (part == 0) {
+#pragma unroll
+      for (int i = 0; i < VPL; ++i)
+#pragma unroll
+        for (int q = 1; q < WPT; ++q) rank[i] += s_rank[q][lane + 64 * i];
+    }
+  }
+  const uint64_t anybad = __ballot(bad);
+  if (part == 0) {
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int e = lane + 64 * i;
+      if (active && e < E && rank[i] < k) {
+        topk_ids[(size_t)t * k + rank[i]] = e;
+        s_sel[w][rank[i]] = v[i];
+      }
     }
   }
   __syncthreads();
-  if (active && lane == 0) {
+  if (active && part == 0 && lane == 0) {
     const float top = s_sel[w][0];
     float ex[kMaxTopk];
     float den = 0.f;
@@ -567,14 +589,15 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int* topk_ids,
                         int* tok_flags, hipStream_t stream) {
   if (T <= 0) return hipSuccess;
   const dim3 grid((T + 3) / 4), block(256);
+  const dim3 grid1((unsigned)T);  // above 64 experts: one token per workgroup
   if (E <= 64)
     hipLaunchKernelGGL(route_rank_kernel<1>, grid, block, 0, stream, logits, T, E, k, topk_ids,
                        topk_w, tok_flags);
   else if (E <= 128)
-    hipLaunchKernelGGL(route_rank_kernel<2>, grid, block, 0, stream, logits, T, E, k, topk_ids,
+    hipLaunchKernelGGL(route_rank_kernel<2>, grid1, block, 0, stream, logits, T, E, k, topk_ids,
                        topk_w, tok_flags);
   else if (E <= 256)
-    hipLaunchKernelGGL(route_rank_kernel<4>, grid, block, 0, stream, logits, T, E, k, topk_ids,
+    hipLaunchKernelGGL(route_rank_kernel<4>, grid1, block, 0, stream, logits, T, E, k, topk_ids,
                        topk_w, tok_flags);
   else
     hipLaunchKernelGGL(route_topk_kernel, grid, block, 0, stream, logits, T, E, k, topk_ids,
