@@ -161,7 +161,7 @@ def run_sgmv(args, torch, ml, dev):
         "config": {"workload": "sgmv", "T": T, "in_features": K, "out_features": N,
                    "n_adapters": nA, "rank": r, "tokens_per_adapter_run": c["run"], "seed": args.seed},
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": ach / HBM_PEAK_GBS, "traffic": None, "kernel": "whole call (4 launches)"},
+                     "frac": ach / HBM_PEAK_GBS, "traffic": None, "kernel": "whole call (3 launches)"},
     }
     if not args.no_cpu_baseline:
         import oracle

@@ -240,7 +240,6 @@ bool moelora_make_layout(int T, int h, int I, int E, int nA, int r, int topk, Mo
   L->n_seg = take(4);
   L->z1 = take(4 * (size_t)kMaxSplit * L->cap * r);
   L->z2 = take(4 * (size_t)kMaxSplit * L->cap * r);
-  L->zsum = take(4 * (size_t)L->cap * r);
   L->zhl = take(2 * 2 * (size_t)L->cap * r);
   L->act = take(2 * (size_t)L->cap * I);
   L->dpair = take(4 * (size_t)kMaxDownSplit * L->cap * h);
@@ -436,12 +435,11 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   if (shrink64 && launch_shrink_tiled(true, sh, n_sub_max, stream) != hipSuccess)
     return MOELORA_EHIP;
   if (launch_shrink(true, sh, tiles16, stream) != hipSuccess) return MOELORA_EHIP;
-  float* zsum = (float*)(ws + L.zsum);
   uint16_t* zhl = path.tiled ? (uint16_t*)(ws + L.zhl) : nullptr;
   // the skinny GEMMs add the split parts themselves (one launch fewer per projection); the
   // tiled GEMMs take z as bf16 high and low planes, made by zfinal
   if (path.tiled &&
-      launch_zfinal(z1, s1, L.cap, r, n_blocks, bm, (int64_t)max_blocks * bm, zsum, zhl, stream) !=
+      launch_zfinal(z1, s1, L.cap, r, n_blocks, bm, (int64_t)max_blocks * bm, zhl, stream) !=
           hipSuccess)
     return MOELORA_EHIP;
   if (!mark(ev, 3, stream)) return MOELORA_EHIP;
@@ -451,7 +449,6 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   g.W8 = (const uint8_t*)W1;
   g.wscale = w1_scale;
   g.Bw = (const uint16_t*)B1;
-  g.zsum = zsum;
   g.zhl = zhl;
   g.zpart = z1;
   g.zsplits = path.tiled ? 0 : s1;
@@ -497,7 +494,7 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
     return MOELORA_EHIP;
   if (launch_shrink(false, sh, tiles16, stream) != hipSuccess) return MOELORA_EHIP;
   if (path.tiled &&
-      launch_zfinal(z2, s2, L.cap, r, n_blocks, bm, (int64_t)max_blocks * bm, zsum, zhl, stream) !=
+      launch_zfinal(z2, s2, L.cap, r, n_blocks, bm, (int64_t)max_blocks * bm, zhl, stream) !=
           hipSuccess)
     return MOELORA_EHIP;
   g.zpart = z2;
@@ -602,10 +599,10 @@ int moe_lora_forward_fp8(const void* x, const float* router_logits, const void* 
 namespace {
 
 // Workspace of moe_lora_sgmv: flags first (moe_lora_debug_status), then the sorted layout of T
-// single-expert pairs in 16-row blocks, the shrink's split parts and their sum, align scratch.
+// single-expert pairs in 16-row blocks, the shrink's split parts, align scratch.
 struct SgmvLayout {
   size_t flags, sorted, sorted_ad, expert_off, n_blocks, block_expert, block_seg, seg_table, n_seg,
-      zpart, zsum, align_lists, total;
+      zpart, align_lists, total;
   int64_t cap;
 };
 
@@ -640,7 +637,6 @@ void sgmv_layout(const moe_lora_sgmv_dims* d, SgmvLayout* L) {
   L->seg_table = take(16 * (size_t)T);
   L->n_seg = take(4);
   L->zpart = take(4 * (size_t)kMaxSplit * L->cap * r);
-  L->zsum = take(4 * (size_t)L->cap * r);
   L->align_lists = take(4 * align_list_ints((int)T, 1, 1, d->n_adapters));
   L->total = off;
 }
@@ -728,17 +724,15 @@ int moe_lora_sgmv(const void* x, const void* A, const void* B, const int32_t* ad
   sh.xcd_ranges = 0;
   sh.after64 = 0;
   if (launch_shrink(true, sh, max_blocks, stream) != hipSuccess) return MOELORA_EHIP;
-  float* zsum = (float*)(ws + L.zsum);
-  if (launch_zfinal(sh.zpart, sh.S, L.cap, r, al.n_blocks, bm, (int64_t)max_blocks * bm, zsum,
-                    nullptr, stream) != hipSuccess)
-    return MOELORA_EHIP;
 
   // expand y += z B_a^T
   SgmvArgs sa;
   sa.sorted_pairs = al.sorted_pairs;
   sa.sorted_ad = al.sorted_ad;
   sa.n_blocks = al.n_blocks;
-  sa.zsum = zsum;
+  sa.zpart = sh.zpart;  // the expand adds the split parts itself
+  sa.zsplits = sh.S;
+  sa.cap = L.cap;
   sa.B = (const uint16_t*)B;
   sa.y = (uint16_t*)y;
   sa.N = N;

@@ -83,7 +83,7 @@ __device__ __forceinline__ int sanitize_adapter(int a, int nA) {
 // ------------------------------------------------------------------------------------------
 struct MoeLoraLayout {
   size_t topk_ids, topk_w, tok_flags, flags, sorted, expert_off, n_blocks, block_expert, block_seg,
-      pair_row, sorted_ad, seg_table, n_seg, z1, z2, zsum, zhl, act, dpair, align_lists, logits;
+      pair_row, sorted_ad, seg_table, n_seg, z1, z2, zhl, act, dpair, align_lists, logits;
   size_t total;
   int64_t cap;     // rows of the sorted layout at the largest row-block size
   int max_bm;      // largest row-block size any path uses

@@ -105,8 +105,8 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs a) {
   constexpr int BMZ = 16 * NT;
 
   // The block's z rows go into LDS for the epilogue (rows without an adapter hold values nobody
-  // reads): the sum of the shrink's K-split parts, added here in split order (a.zsplits > 0),
-  // or already added (a.zsum). Only K split 0 of down adds the LoRA term. Run after the first
+  // reads): the sum of the shrink's K-split parts, added here in split order. Only K split 0 of
+  // down adds the LoRA term. Run after the first
   // weight loads are issued, so the two latencies overlap. (The grid covers N exactly: every
   // wavefront has columns.)
   __shared__ __attribute__((aligned(16))) float s_z[BMZ * 64];
@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs a) {
     if (zsplit != 0) return;
     const int nz = BMZ * a.r;
     const size_t off = (size_t)blk * BMZ * a.r;
-    if (a.zsplits > 0) {
+    {
       // every part's load is issued before the first add (parts past zsplits re-read the last
       // one and are not added), so the sum costs one memory round trip
       const size_t part = (size_t)a.cap * a.r;
@@ -129,9 +129,6 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs a) {
           if (sp < a.zsplits) z += zz[sp];
         *reinterpret_cast<f32x4*>(s_z + i) = z;
       }
-    } else {
-      for (int i = threadIdx.x * 4; i < nz; i += 256 * 4)
-        *reinterpret_cast<f32x4*>(s_z + i) = *reinterpret_cast<const f32x4*>(a.zsum + off + i);
     }
     __syncthreads();
   };
@@ -296,6 +293,7 @@ hipError_t launch_skinny(const SkinnyConfig& c, bool gateup, const GemmArgs& a, 
   if (a.N % cols_per_wg != 0) return hipErrorInvalidValue;  // every wavefront has columns
   const int ncol = a.N / cols_per_wg;
   if (ncol <= 0 || grid_y <= 0) return hipSuccess;
+  if (a.zsplits < 1 || a.zsplits > kMaxSplit) return hipErrorInvalidValue;  // z parts to add
   if (ncol != a.n_col_tiles) return hipErrorInvalidValue;
   // one workgroup per (row block, column tile) for the largest block count, in a 1-D grid
   // rounded up to the 8 XCDs (the kernel maps its id onto the live items)

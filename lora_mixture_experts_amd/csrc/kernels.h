@@ -87,9 +87,8 @@ struct GemmArgs {
   const uint8_t* W8;   // skinny FP8 entry: the same weights as E4M3 codes (W unused)
   const float* wscale; // with W8: one scale per weight row ([E][2I] or [E][h])
   const uint16_t* Bw;  // gate_up: B1 [nA][E][2I][r]; down: B2 [nA][E][h][r]
-  const float* zsum;    // [cap][r] LoRA shrink output (its split parts added), when zsplits = 0
-  const float* zpart;   // skinny: [zsplits][cap][r] the shrink's split parts, added in the
-  int zsplits;          //   prologue in split order (zsum unused) when zsplits > 0
+  const float* zpart;   // skinny: [zsplits][cap][r] the LoRA shrink's split parts, added in
+  int zsplits;          //   the prologue in split order
   const uint16_t* zhl;  // tiled: [2][cap][r] the same as bf16 high and low planes
   int64_t cap;
   const int* sorted_pairs;
@@ -116,7 +115,9 @@ struct SgmvArgs {
   const int* sorted_pairs;  // [cap]: token of each sorted row, -1 for padding
   const int* sorted_ad;     // [cap]: its adapter, -1 for none or padding
   const int* n_blocks;      // live 16-row blocks
-  const float* zsum;        // [cap][r] shrink output (split parts added)
+  const float* zpart;       // [zsplits][cap][r] the shrink's split parts, added in split order
+  int zsplits;
+  int64_t cap;
   const uint16_t* B;        // [nA][N][r]
   uint16_t* y;              // [T][N], updated in place
   int N, r;
@@ -148,8 +149,7 @@ hipError_t launch_shrink(bool gather, const ShrinkArgs& a, int tiles, hipStream_
 hipError_t launch_shrink_tiled(bool gather, const ShrinkArgs& a, int n_sub_max,
                                hipStream_t stream);
 hipError_t launch_zfinal(const float* zpart, int S, int64_t cap, int r, const int* n_blocks,
-                         int bm, int64_t max_rows, float* zsum, uint16_t* zhl,
-                         hipStream_t stream);
+                         int bm, int64_t max_rows, uint16_t* zhl, hipStream_t stream);
 hipError_t launch_skinny(const SkinnyConfig& c, bool gateup, const GemmArgs& a, int grid_y,
                          hipStream_t stream, bool fp8 = false);
 hipError_t launch_tiled(const TiledConfig& c, bool gateup, const GemmArgs& a, hipStream_t stream);

@@ -31,12 +31,22 @@ __global__ __launch_bounds__(256) void sgmv_expand_kernel(SgmvArgs a) {
   const int tok = a.sorted_pairs[row];  // one pair per token: the pair id is the token
   const int adap[1] = {a.sorted_ad[row]};
 
-  // the block's z rows (split parts already added) into LDS
+  // the block's z rows into LDS: the shrink's split parts added in split order, every part's
+  // load issued before the first add (parts past zsplits re-read the last one, unused)
   __shared__ __attribute__((aligned(16))) float s_z[16 * 64];
   const int nz = 16 * a.r;
-  const float* zp = a.zsum + (size_t)blk * 16 * a.r;
-  for (int i = threadIdx.x * 4; i < nz; i += 256 * 4)
-    *reinterpret_cast<f32x4*>(s_z + i) = *reinterpret_cast<const f32x4*>(zp + i);
+  const size_t off = (size_t)blk * 16 * a.r, part = (size_t)a.cap * a.r;
+  for (int i = threadIdx.x * 4; i < nz; i += 256 * 4) {
+    f32x4 zz[kMaxSplit];
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplit; ++sp)
+      zz[sp] = *reinterpret_cast<const f32x4*>(a.zpart + min(sp, a.zsplits - 1) * part + off + i);
+    f32x4 z = zz[0];
+#pragma unroll
+    for (int sp = 1; sp < kMaxSplit; ++sp)
+      if (sp < a.zsplits) z += zz[sp];
+    *reinterpret_cast<f32x4*>(s_z + i) = z;
+  }
   __syncthreads();
 
   f32x4 acc[1][1] = {{f32x4{0.f, 0.f, 0.f, 0.f}}};
@@ -55,7 +65,7 @@ __global__ __launch_bounds__(256) void sgmv_expand_kernel(SgmvArgs a) {
 }
 
 hipError_t launch_sgmv_expand(const SgmvArgs& a, int max_blocks, hipStream_t stream) {
-  if (a.N % 64 != 0) return hipErrorInvalidValue;
+  if (a.N % 64 != 0 || a.zsplits < 1 || a.zsplits > kMaxSplit) return hipErrorInvalidValue;
   const int64_t items = (int64_t)max_blocks * (a.N / 64);
   if (items <= 0) return hipSuccess;
   hipLaunchKernelGGL(sgmv_expand_kernel, dim3((unsigned)((items + 7) / 8 * 8)), dim3(256), 0,

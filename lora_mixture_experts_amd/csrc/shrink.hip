@@ -204,16 +204,15 @@ __global__ __launch_bounds__(256) void lora_shrink_kernel(ShrinkArgs a) {
   }
 }
 
-// z for the GEMM epilogues: the S split parts of each row added in split order, once, into
-// zsum [cap][r] (fp32, read by the skinny GEMMs), so that every workgroup reading a row's z
-// loads it once instead of S times. For the LDS-tiled GEMMs (zhl != nullptr) the sum is also
-// split into bf16 high and low parts (hi = bf16(z), lo = bf16(z - hi)), written as two planes
-// [cap][r], which their epilogue loads straight into MFMA operands. One thread per 8
-// consecutive values of a row; rows past the live row blocks are skipped.
+// z for the LDS-tiled GEMM epilogues: the S split parts of each row added in split order, once
+// (every workgroup reading a row's z then loads it once instead of S times), and split into bf16
+// high and low parts (hi = bf16(z), lo = bf16(z - hi)), written as two planes [cap][r] that
+// their epilogue loads straight into MFMA operands. One thread per 8 consecutive values of a
+// row; rows past the live row blocks are skipped. (The skinny GEMMs and the dense multi-LoRA
+// expand add the parts themselves.)
 __global__ __launch_bounds__(256) void zfinal_kernel(const float* __restrict__ zpart, int S,
                                                      int64_t cap, int r,
                                                      const int* __restrict__ n_blocks, int bm,
-                                                     float* __restrict__ zsum,
                                                      uint16_t* __restrict__ zhl) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int per_row = r / 8;
@@ -226,11 +225,6 @@ __global__ __launch_bounds__(256) void zfinal_kernel(const float* __restrict__ z
     const float* src = zpart + (sp * cap + row) * r + q;
     z0 += *reinterpret_cast<const f32x4*>(src);
     z1 += *reinterpret_cast<const f32x4*>(src + 4);
-  }
-  if (zhl == nullptr) {
-    *reinterpret_cast<f32x4*>(zsum + row * r + q) = z0;
-    *reinterpret_cast<f32x4*>(zsum + row * r + q + 4) = z1;
-    return;
   }
   uint32_t hb[8], lb[8];
 #pragma unroll
@@ -246,13 +240,12 @@ __global__ __launch_bounds__(256) void zfinal_kernel(const float* __restrict__ z
 }
 
 hipError_t launch_zfinal(const float* zpart, int S, int64_t cap, int r, const int* n_blocks,
-                         int bm, int64_t max_rows, float* zsum, uint16_t* zhl,
-                         hipStream_t stream) {
-  if (r % 8 != 0) return hipErrorInvalidValue;
+                         int bm, int64_t max_rows, uint16_t* zhl, hipStream_t stream) {
+  if (r % 8 != 0 || zhl == nullptr || S < 1 || S > kMaxSplit) return hipErrorInvalidValue;
   const int64_t n = max_rows * (r / 8);
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(zfinal_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, zpart,
-                     S, cap, r, n_blocks, bm, zsum, zhl);
+                     S, cap, r, n_blocks, bm, zhl);
   return hipGetLastError();
 }
 
