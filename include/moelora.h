@@ -61,10 +61,14 @@ extern "C" {
 #define MOELORA_FLAG_NONFINITE_LOGIT 1u
 #define MOELORA_FLAG_ADAPTER_RANGE 2u
 
-/* Layer sizes. Supported: T >= 0; hidden and inter positive multiples of 128; n_experts in
- * [1, 1024]; n_adapters >= 1; rank in {8, 16, 32, 64}; 1 <= topk <= min(n_experts, 16).
- * Buffers the kernels address with 32-bit offsets must stay under 2 GiB: x (T x hidden), the
- * activations ((T*topk + 256*n_experts) x inter) and one expert's W1 (2*inter x hidden). */
+/* Layer sizes (page "vLLM MoE LoRA SageMaker Bedrock", sections "Entendendo os Modelos MoE" and
+ * "O Papel da Multi-LoRA": T tokens of width hidden, n_experts experts of intermediate width
+ * inter, n_adapters LoRA adapters of rank r). Supported: T >= 0; hidden and inter positive
+ * multiples of 128; n_experts in [1, 1024]; n_adapters >= 1; rank in {8, 16, 32, 64};
+ * 1 <= topk <= min(n_experts, 16). Buffers the kernels address with 32-bit offsets must stay
+ * under 2 GiB: x (T x hidden), the activations (capacity x inter, capacity as reported by
+ * moe_lora_workspace_layout, at most T*topk + 255*n_experts rounded up to 256) and one expert's
+ * W1 (2*inter x hidden); larger sizes are rejected with MOELORA_EINVAL_DIMS. */
 typedef struct {
   int32_t T, hidden, inter, n_experts, n_adapters, rank;
 } moe_lora_dims;
@@ -78,15 +82,26 @@ typedef struct {
 } moe_lora_sgmv_dims;
 
 /* Bytes of device workspace moe_lora_forward needs for these sizes (0 when the sizes are
- * unsupported). The workspace must be 256-byte aligned; its contents need no initialisation
- * and are overwritten by every call. */
+ * unsupported): the routing, the pairs sorted by (expert, adapter, token) with their segment
+ * table (page "vLLM MoE LoRA SageMaker Bedrock", section "Implementação Técnica no vLLM"; page
+ * "Punica: Multi-Tenant LoRA Serving", proposed method), the LoRA shrink outputs z = xA (section
+ * "O Papel da Multi-LoRA") and the expert intermediates, sized for the GEMM path these sizes
+ * take. The workspace must be 256-byte aligned; its contents need no initialisation and are
+ * overwritten by every call. Host-only. */
 size_t moe_lora_workspace_size(const moe_lora_dims *d, int32_t topk);
 
-/* The fused layer: routing (top-k softmax), sorting token-expert pairs by (expert, adapter,
- * token), LoRA shrink for gate_up, gate_up GEMM with the LoRA expand and SiLU-and-mul fused in
- * its epilogue, LoRA shrink for down, down GEMM with the LoRA expand fused, and the weighted
- * top-k combine. See the header comment for layouts. Returns MOELORA_OK once the work is
- * enqueued on `stream`. With T = 0 nothing is enqueued and no pointer is inspected. */
+/* The fused layer (page "vLLM MoE LoRA SageMaker Bedrock", section "Entendendo os Modelos MoE":
+ * each token goes to its top-k experts, whose gate_up and down outputs are aggregated with the
+ * router weights; section "O Papel da Multi-LoRA": every projection with frozen W also adds the
+ * token's adapter term xAB, as shrink z = xA then expand zB; section "Implementação Técnica no
+ * vLLM": the expert and adapter sparsities handled together). Steps: routing (top-k softmax),
+ * sorting token-expert pairs by (expert, adapter, token), LoRA shrink for gate_up, gate_up GEMM
+ * with the LoRA expand and SiLU-and-mul fused in its epilogue, LoRA shrink for down, down GEMM
+ * with the LoRA expand fused, and the weighted top-k combine. See the header comment for
+ * layouts; every pointer is device memory owned by the caller, 16-byte aligned (workspace:
+ * 256-byte aligned, at least moe_lora_workspace_size bytes). Returns MOELORA_OK once the work is
+ * enqueued on `stream`, or a negative code before any device work (sizes, NULL or misaligned
+ * pointers, workspace, device). With T = 0 nothing is enqueued and no pointer is inspected. */
 int moe_lora_forward(const void *x, const float *router_logits, const void *W1, const void *W2,
                      const void *A1, const void *B1, const void *A2, const void *B2,
                      const int32_t *adapter_ids, int32_t topk, const moe_lora_dims *d, void *y,
@@ -97,7 +112,7 @@ int moe_lora_forward(const void *x, const float *router_logits, const void *W1, 
  * expand), 6 combine. */
 #define MOELORA_N_STAGES 7
 
-/* moe_lora_forward for measurement: additionally records stage_events[i] (caller-created
+/* moe_lora_forward for measurement (the layer of moe_lora_forward, same passages): additionally records stage_events[i] (caller-created
  * hipEvent_t handles, an array of MOELORA_N_STAGES + 1) on `stream` right before stage i and
  * stage_events[MOELORA_N_STAGES] after the last stage, so the elapsed time between events i
  * and i+1 is stage i. A NULL entry is not recorded (each record adds a gap between launches,
@@ -118,9 +133,12 @@ int moe_lora_forward_timed(const void *x, const float *router_logits, const void
 int moe_lora_router_logits(const void *x, const void *W_router, int32_t T, int32_t hidden,
                            int32_t n_experts, float *logits, void *stream);
 
-/* moe_lora_forward starting from the router weights: the logits of moe_lora_router_logits go
- * into the workspace (moe_lora_workspace_size covers them) and the layer runs from them, so the
- * result equals moe_lora_forward on those logits. */
+/* moe_lora_forward starting from the router weights (page "vLLM MoE LoRA SageMaker Bedrock",
+ * section "Entendendo os Modelos MoE": the router scores the experts of each token, then the
+ * layer of moe_lora_forward runs): the logits of moe_lora_router_logits go into the workspace
+ * (moe_lora_workspace_size covers them) and the layer runs from them, so the result equals
+ * moe_lora_forward on those logits. W_router bf16 [n_experts][hidden], 16-byte aligned. Every
+ * argument is checked, as in moe_lora_forward, before the router GEMM is enqueued. */
 int moe_lora_forward_routed(const void *x, const void *W_router, const void *W1, const void *W2,
                             const void *A1, const void *B1, const void *A2, const void *B2,
                             const int32_t *adapter_ids, int32_t topk, const moe_lora_dims *d,
@@ -143,13 +161,16 @@ int moe_lora_forward_fp8(const void *x, const float *router_logits, const void *
                          void *y, void *workspace, size_t workspace_bytes, void *stream,
                          void *const *stage_events);
 
-/* Upper bound on the padded sorted-pair length for (seg_pad, block_m):
- * T*topk*seg_pad + n_experts*(block_m-1), or -1 for invalid arguments. */
+/* Upper bound on the padded sorted-pair length for (seg_pad, block_m) of moe_lora_route_align
+ * (pairs grouped by expert and adapter, page "Punica: Multi-Tenant LoRA Serving", proposed
+ * method: segments of tokens sharing an adapter): T*topk*seg_pad + n_experts*(block_m-1), or -1
+ * for invalid arguments. Host-only. */
 int64_t moe_lora_sorted_capacity(const moe_lora_dims *d, int32_t topk, int32_t seg_pad,
                                  int32_t block_m);
 
-/* Bytes of device workspace moe_lora_sgmv needs (0 when the sizes are unsupported); 256-byte
- * aligned, no initialisation needed. */
+/* Bytes of device workspace moe_lora_sgmv needs (0 when the sizes are unsupported): the tokens
+ * sorted into adapter segments and the shrink outputs (page "Punica: Multi-Tenant LoRA Serving",
+ * proposed method). 256-byte aligned, no initialisation needed. Host-only. */
 size_t moe_lora_sgmv_workspace_size(const moe_lora_sgmv_dims *d);
 
 /* Dense multi-LoRA, the per-adapter segmented shrink and expand of one projection (page
@@ -165,7 +186,10 @@ int moe_lora_sgmv(const void *x, const void *A, const void *B, const int32_t *ad
                   const moe_lora_sgmv_dims *d, void *y, void *workspace, size_t workspace_bytes,
                   void *stream);
 
-/* Routing and align on their own, for inspection and tests.
+/* Routing and align on their own, for inspection and tests (page "vLLM MoE LoRA SageMaker
+ * Bedrock", section "Entendendo os Modelos MoE": each token's top-k experts and their weights;
+ * section "Implementação Técnica no vLLM": the pairs grouped by expert, then by adapter; page
+ * "Punica: Multi-Tenant LoRA Serving", proposed method: tokens of one adapter form a segment).
  *   topk_ids   int32 [T][topk]  expert of slot j, slots in descending logit order
  *   topk_w     f32   [T][topk]  softmax of the selected logits
  *   sorted_pairs int32 [sorted_cap]  pair ids p = t*topk + j ordered by the key
@@ -185,11 +209,43 @@ int moe_lora_route_align(const float *router_logits, const int32_t *adapter_ids,
                          int64_t sorted_cap, int32_t *expert_offsets, int32_t *seg_table,
                          int32_t *n_seg, void *workspace, size_t workspace_bytes, void *stream);
 
-/* Text for a return code. Never NULL. */
+/* Where moe_lora_forward (and its _timed, _routed and _fp8 variants) keeps the sorted layout of a
+ * call inside the workspace, so that a caller can read the layer's own routing tables back after
+ * a call and check them (page "vLLM MoE LoRA SageMaker Bedrock", section "Implementação Técnica
+ * no vLLM": token-expert pairs grouped by expert and, inside an expert, by adapter). Offsets are
+ * bytes from the start of the workspace; each region holds int32 (topk_w: float32):
+ *   topk_ids [T][topk], topk_w [T][topk]     the routing of every token
+ *   sorted_pairs [capacity]   pair ids t*topk + j in (expert, adapter, token) order, each expert
+ *                             block padded with -1 to a multiple of block_m (seg_pad 1)
+ *   expert_offsets [E+1], seg_table [n_seg][4], n_seg [1]   as in moe_lora_route_align
+ *   n_blocks [1]              padded total / block_m
+ *   block_expert [n_blocks]   expert of each row block
+ *   block_seg [n_blocks]      segment holding the block's first row, -1 when that row is padding
+ *   pair_row [T*topk]         sorted row of each pair
+ *   sorted_ad [capacity]      adapter of each sorted row, -1 for none and for padding rows
+ * Only the rows below the padded total are defined. Host-only: touches no device memory.
+ * Returns MOELORA_OK, or the error moe_lora_workspace_size would meet (MOELORA_ENULL for a NULL
+ * out). */
+typedef struct {
+  int32_t tiled;    /* 1: LDS-tiled MFMA GEMMs; 0: weight-streaming GEMMs */
+  int32_t block_m;  /* row-block size of the sorted layout */
+  int64_t capacity; /* rows reserved for sorted_pairs and sorted_ad */
+  int64_t workspace_bytes;
+  int64_t topk_ids, topk_w, sorted_pairs, expert_offsets, seg_table, n_seg, n_blocks,
+      block_expert, block_seg, pair_row, sorted_ad;
+} moe_lora_layout_info;
+
+int moe_lora_workspace_layout(const moe_lora_dims *d, int32_t topk, moe_lora_layout_info *out);
+
+/* Text for a return code (the MOELORA_E* codes above; no page defines them). Never NULL; the
+ * string is static and owned by the library. */
 const char *moe_lora_strerror(int code);
 
 /* Synchronises `stream`, then reads the device flags of the last call that used this
- * workspace into *flags (MOELORA_FLAG_* bits). Returns MOELORA_OK or an error code. */
+ * workspace into *flags (MOELORA_FLAG_* bits: the data checks that the pages leave open, a
+ * non-finite router logit and an adapter id outside [-1, nA), raised by the routing and align
+ * kernels of the layer). Returns MOELORA_OK, MOELORA_ENULL, MOELORA_EWORKSPACE (misaligned or
+ * under 16 bytes) or MOELORA_EHIP. */
 int moe_lora_debug_status(const void *workspace, size_t workspace_bytes, void *stream,
                           uint32_t *flags);
 

@@ -22,7 +22,7 @@ FLAG_NONFINITE_LOGIT, FLAG_ADAPTER_RANGE = 1, 2
 EXPORTS = ("moe_lora_workspace_size", "moe_lora_forward", "moe_lora_forward_timed", "moe_lora_forward_fp8",
            "moe_lora_sorted_capacity", "moe_lora_route_align", "moe_lora_strerror",
            "moe_lora_debug_status", "moe_lora_sgmv_workspace_size", "moe_lora_sgmv",
-           "moe_lora_router_logits", "moe_lora_forward_routed")
+           "moe_lora_router_logits", "moe_lora_forward_routed", "moe_lora_workspace_layout")
 N_STAGES = 7
 STAGES = ("route", "align", "shrink_gate_up", "gate_up", "shrink_down", "down", "combine")
 
@@ -35,6 +35,13 @@ class MoeLoraError(RuntimeError):
 
 class Dims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("T", "hidden", "inter", "n_experts", "n_adapters", "rank")]
+
+
+class LayoutInfo(ctypes.Structure):
+    _fields_ = [("tiled", ctypes.c_int32), ("block_m", ctypes.c_int32)] + [
+        (n, ctypes.c_int64) for n in ("capacity", "workspace_bytes", "topk_ids", "topk_w", "sorted_pairs",
+                                      "expert_offsets", "seg_table", "n_seg", "n_blocks", "block_expert",
+                                      "block_seg", "pair_row", "sorted_ad")]
 
 
 class SgmvDims(ctypes.Structure):
@@ -76,6 +83,8 @@ def lib() -> ctypes.CDLL:
         L.moe_lora_route_align.argtypes = [P, P, i32, D, i32, i32, P, P, P, i64, P, P, P, P,
                                            ctypes.c_size_t, P]
         L.moe_lora_route_align.restype = ctypes.c_int
+        L.moe_lora_workspace_layout.argtypes = [D, i32, ctypes.POINTER(LayoutInfo)]
+        L.moe_lora_workspace_layout.restype = ctypes.c_int
         L.moe_lora_strerror.argtypes = [ctypes.c_int]
         L.moe_lora_strerror.restype = ctypes.c_char_p
         L.moe_lora_debug_status.argtypes = [P, ctypes.c_size_t, P, ctypes.POINTER(ctypes.c_uint32)]
@@ -113,6 +122,42 @@ def new_workspace(d: Dims, topk: int, device) -> torch.Tensor:
     if n == 0:
         raise MoeLoraError(EINVAL_DIMS, "workspace_size")
     return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def workspace_layout(d: Dims, topk: int) -> dict:
+    """Where the forward keeps its sorted layout in the workspace (moe_lora_workspace_layout)."""
+    info = LayoutInfo()
+    _check(lib().moe_lora_workspace_layout(ctypes.byref(d), topk, ctypes.byref(info)),
+           "moe_lora_workspace_layout")
+    return {name: getattr(info, name) for name, _ in LayoutInfo._fields_}
+
+
+def read_layout_tables(workspace: torch.Tensor, d: Dims, topk: int) -> dict:
+    """The forward's routing and sorted-layout tables, copied to the host from the workspace of
+    the last call that used it (int32 numpy arrays; topk_w float32). Synchronises."""
+    info = workspace_layout(d, topk)
+    host = workspace.cpu()
+    P = d.T * topk
+
+    def region(name, n, dtype=torch.int32):
+        off = info[name]
+        return host[off:off + 4 * n].view(dtype).numpy()
+
+    n_blocks = int(region("n_blocks", 1)[0])
+    n_seg = int(region("n_seg", 1)[0])
+    total = n_blocks * info["block_m"]
+    return {
+        "info": info, "n_blocks": n_blocks, "n_seg": n_seg,
+        "topk_ids": region("topk_ids", P).reshape(d.T, topk),
+        "topk_w": region("topk_w", P, torch.float32).reshape(d.T, topk),
+        "sorted_pairs": region("sorted_pairs", total),
+        "expert_offsets": region("expert_offsets", d.n_experts + 1),
+        "seg_table": region("seg_table", 4 * n_seg).reshape(n_seg, 4),
+        "block_expert": region("block_expert", n_blocks),
+        "block_seg": region("block_seg", n_blocks),
+        "pair_row": region("pair_row", P),
+        "sorted_ad": region("sorted_ad", total),
+    }
 
 
 def _ptr(t) -> int | None:

@@ -32,9 +32,8 @@ int validate_dims(const moe_lora_dims* d, int32_t topk) {
   if (P + (int64_t)d->n_experts * kMaxBM >= ((int64_t)1 << 30)) return MOELORA_EINVAL_DIMS;
   if ((int64_t)d->n_experts * (d->n_adapters + 1) >= ((int64_t)1 << 28)) return MOELORA_EINVAL_DIMS;
   // x and the intermediate activations are read with 32-bit buffer offsets (< 2 GiB each)
+  // (the activations are checked against the capacity of the path a call takes, once planned)
   if ((int64_t)d->T * d->hidden * 2 >= ((int64_t)1 << 31)) return MOELORA_EINVAL_DIMS;
-  if ((P + (int64_t)d->n_experts * kMaxBM) * d->inter * 2 >= ((int64_t)1 << 31))
-    return MOELORA_EINVAL_DIMS;
   // so is one expert's slice of W1 (2I x h, the larger of the two projections)
   if ((int64_t)2 * d->inter * d->hidden * 2 >= ((int64_t)1 << 31)) return MOELORA_EINVAL_DIMS;
   return MOELORA_OK;
@@ -213,12 +212,84 @@ int pick_splits(int64_t tiles, int K) {
   return (nks + per - 1) / per;
 }
 
+// Everything about a layer call that follows from the sizes alone: the GEMM path and its row-block
+// size, the skinny tiles, the K splits of down and of the two LoRA shrinks, the launch grids.
+struct ForwardPlan {
+  PathPlan path;
+  SkinnyPlan sk;  // skinny tiles; sk.ksplit is the down GEMM's K splits on either path
+  int bm;
+  int64_t P;
+  int max_blocks;  // row blocks of the largest padded layout
+  int tiles16;     // 16-row tiles of it
+  int n_sub_max;   // 64-row sub-blocks of it
+  int s1, s2;      // K splits of the gate_up and down shrinks
+  bool shrink64;   // 64-row shrink on the tiled path
+};
+
+ForwardPlan make_plan(const moe_lora_dims* d, int topk, bool fp8) {
+  ForwardPlan pl;
+  const int h = d->hidden, I = d->inter, E = d->n_experts, r = d->rank;
+  pl.P = (int64_t)d->T * topk;
+  pl.path = pick_path(pl.P, E, h, I);
+  pl.bm = pl.path.bm;
+  pl.sk = pick_skinny(pl.path.nt, h, I);
+  if (fp8) {
+    // E4M3 rows carry half the bytes per K element: 128-wide K steps keep the bf16 kernels'
+    // bytes in flight per load (measured: decode gate_up 0.35 -> 0.31 ms); down on 32-row
+    // blocks (short K loops of many experts) keeps 64-wide steps
+    pl.sk.gu.p = 4;
+    pl.sk.dn.p = pl.path.nt == 1 ? 4 : 2;
+  }
+  if (pl.path.tiled) {
+    // tiled down: split K in two when the tiles would fill the chip fewer than four times (the
+    // last, partial round of 256x256 tiles then costs a large share of the time)
+    const int64_t est_tiles =
+        (int64_t)((pl.P + pl.bm - 1) / pl.bm + E) * (h / pl.path.tc_dn.bn);
+    pl.sk.ksplit = est_tiles < 4 * 256 ? kMaxDownSplit : 1;
+    // MOELORA_DOWN_SPLIT=1|2 overrides it (experiments)
+    static int down_split = -1;
+    if (down_split < 0) {
+      const char* env = getenv("MOELORA_DOWN_SPLIT");
+      down_split = env ? atoi(env) : 0;
+    }
+    if (down_split == 1 || down_split == 2) pl.sk.ksplit = down_split;
+  }
+  const int64_t max_rows = pl.P + (int64_t)E * (pl.bm - 1);
+  pl.max_blocks = (int)((max_rows + pl.bm - 1) / pl.bm);
+  pl.tiles16 = pl.max_blocks * (pl.bm / 16);
+  // Split the shrink's K by the tiles that can hold pairs (at most P/16 plus one partial tile per
+  // expert), not by the padded grid: padding tiles exit at once.
+  const int64_t live_tiles = std::min<int64_t>(pl.tiles16, (pl.P + 15) / 16 + E);
+  pl.s1 = pick_splits(live_tiles, h);
+  pl.s2 = pick_splits(live_tiles, I);
+  // On the tiled path (row blocks of >= 64 rows) the shrink takes 64 rows per workgroup where a
+  // sub-block holds few adapter runs, so that a run's A slab is fetched once per 64 rows; the
+  // 16-row shrink then takes the rest. Both use the same K splits, as many as either needs to
+  // fill the chip (MOELORA_SHRINK64=0 turns the 64-row shrink off, for experiments).
+  static int shrink64_env = -1;
+  if (shrink64_env < 0) {
+    const char* env = getenv("MOELORA_SHRINK64");
+    shrink64_env = env ? atoi(env) : 1;
+  }
+  pl.shrink64 = shrink64_env != 0 && pl.path.tiled && r <= 64 && pl.bm % 64 == 0;
+  pl.n_sub_max = pl.max_blocks * pl.bm / 64;
+  if (pl.shrink64) {
+    const int64_t live_sub = std::min<int64_t>(pl.n_sub_max, (pl.P + 63) / 64 + E);
+    pl.s1 = std::max(pl.s1, pick_splits(live_sub, h));
+    pl.s2 = std::max(pl.s2, pick_splits(live_sub, I));
+  }
+  return pl;
+}
+
 }  // namespace
 
-bool moelora_make_layout(int T, int h, int I, int E, int nA, int r, int topk, MoeLoraLayout* L) {
+// Workspace regions for a call with row blocks of bm rows and dsplit K splits of down: only what
+// that path uses (decode: ~30 MB; 256-row prefill blocks: ~0.6 GB).
+bool moelora_make_layout(int T, int h, int I, int E, int nA, int r, int topk, int bm, int dsplit,
+                         MoeLoraLayout* L) {
   const int64_t P = (int64_t)T * topk;
-  L->max_bm = kMaxBM;
-  L->cap = round_up64(P + (int64_t)E * (kMaxBM - 1), 256);
+  L->max_bm = bm;
+  L->cap = round_up64(P + (int64_t)E * (bm - 1), 256);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -242,20 +313,62 @@ bool moelora_make_layout(int T, int h, int I, int E, int nA, int r, int topk, Mo
   L->z2 = take(4 * (size_t)kMaxSplit * L->cap * r);
   L->zhl = take(2 * 2 * (size_t)L->cap * r);
   L->act = take(2 * (size_t)L->cap * I);
-  L->dpair = take(4 * (size_t)kMaxDownSplit * L->cap * h);
+  L->dpair = take(4 * (size_t)dsplit * L->cap * h);
   L->align_lists = take(4 * align_list_ints(T, topk, E, nA));
   L->logits = take(4 * (size_t)T * E);
   L->total = off;
   return true;
 }
 
+namespace {
+
+// The plan and workspace layout of a forward call; MOELORA_EINVAL_DIMS when a buffer the kernels
+// address with 32-bit offsets would reach 2 GiB (the activations at this path's capacity).
+int plan_and_layout(const moe_lora_dims* d, int32_t topk, bool fp8, ForwardPlan* pl,
+                    MoeLoraLayout* L) {
+  const int rc = validate_dims(d, topk);
+  if (rc != MOELORA_OK) return rc;
+  *pl = make_plan(d, topk, fp8);
+  moelora_make_layout(d->T, d->hidden, d->inter, d->n_experts, d->n_adapters, d->rank, topk, pl->bm,
+                      pl->sk.ksplit, L);
+  // act [cap][I] bf16 is read with 32-bit buffer offsets, and padding lanes use offset 2^31
+  if (L->cap * (int64_t)d->inter * 2 >= ((int64_t)1 << 31)) return MOELORA_EINVAL_DIMS;
+  return MOELORA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t moe_lora_workspace_size(const moe_lora_dims* d, int32_t topk) {
-  if (validate_dims(d, topk) != MOELORA_OK) return 0;
+  ForwardPlan pl;
   MoeLoraLayout L;
-  moelora_make_layout(d->T, d->hidden, d->inter, d->n_experts, d->n_adapters, d->rank, topk, &L);
+  if (plan_and_layout(d, topk, false, &pl, &L) != MOELORA_OK) return 0;
   return L.total;
+}
+
+int moe_lora_workspace_layout(const moe_lora_dims* d, int32_t topk, moe_lora_layout_info* out) {
+  if (!out) return MOELORA_ENULL;
+  ForwardPlan pl;
+  MoeLoraLayout L;
+  const int rc = plan_and_layout(d, topk, false, &pl, &L);
+  if (rc != MOELORA_OK) return rc;
+  out->tiled = pl.path.tiled ? 1 : 0;
+  out->block_m = pl.bm;
+  out->capacity = L.cap;
+  out->workspace_bytes = (int64_t)L.total;
+  out->topk_ids = (int64_t)L.topk_ids;
+  out->topk_w = (int64_t)L.topk_w;
+  out->sorted_pairs = (int64_t)L.sorted;
+  out->expert_offsets = (int64_t)L.expert_off;
+  out->seg_table = (int64_t)L.seg_table;
+  out->n_seg = (int64_t)L.n_seg;
+  out->n_blocks = (int64_t)L.n_blocks;
+  out->block_expert = (int64_t)L.block_expert;
+  out->block_seg = (int64_t)L.block_seg;
+  out->pair_row = (int64_t)L.pair_row;
+  out->sorted_ad = (int64_t)L.sorted_ad;
+  return MOELORA_OK;
 }
 
 int64_t moe_lora_sorted_capacity(const moe_lora_dims* d, int32_t topk, int32_t seg_pad,
@@ -288,36 +401,15 @@ bool mark(void* const* ev, int i, hipStream_t s) {
   return !ev || !ev[i] || hipEventRecord((hipEvent_t)ev[i], s) == hipSuccess;
 }
 
-// w1_scale/w2_scale != nullptr: W1/W2 are E4M3 codes with per-row scales (skinny path only)
-int forward_impl(const void* x, const float* router_logits, const void* W1, const void* W2,
-                 const void* A1, const void* B1, const void* A2, const void* B2,
-                 const int32_t* adapter_ids, int32_t topk, const moe_lora_dims* d, void* y,
-                 void* workspace, size_t workspace_bytes, void* stream_, void* const* ev,
-                 const float* w1_scale = nullptr, const float* w2_scale = nullptr) {
-  int rc = validate_dims(d, topk);
-  if (rc != MOELORA_OK) return rc;
-  const bool fp8 = w1_scale != nullptr || w2_scale != nullptr;
-  if (fp8 && pick_path((int64_t)d->T * topk, d->n_experts, d->hidden, d->inter).tiled)
-    return MOELORA_EUNSUPPORTED;
-  if (d->T == 0) return MOELORA_OK;  // empty batch: nothing to do, pointers may be NULL
-  const void* ptrs[] = {x, router_logits, W1, W2, A1, B1, A2, B2, adapter_ids, y, workspace};
-  for (const void* p : ptrs)
-    if (!p) return MOELORA_ENULL;
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return MOELORA_EALIGN;
-  if (fp8 && (!w1_scale || !w2_scale)) return MOELORA_ENULL;
-  if (fp8 && ((((uintptr_t)w1_scale) | ((uintptr_t)w2_scale)) & 3u) != 0) return MOELORA_EALIGN;
-  if (((uintptr_t)workspace & 255u) != 0) return MOELORA_EWORKSPACE;
-  MoeLoraLayout L;
-  moelora_make_layout(d->T, d->hidden, d->inter, d->n_experts, d->n_adapters, d->rank, topk, &L);
-  if (workspace_bytes < L.total) return MOELORA_EWORKSPACE;
-  rc = check_device();
-  if (rc != MOELORA_OK) return rc;
-
-  hipStream_t stream = (hipStream_t)stream_;
-  char* ws = (char*)workspace;
+// The launch sequence of one layer call (arguments already checked, T > 0).
+int enqueue_forward(const ForwardPlan& pl, const MoeLoraLayout& L, const void* x,
+                    const float* router_logits, const void* W_router, const void* W1,
+                    const void* W2, const void* A1, const void* B1, const void* A2, const void* B2,
+                    const int32_t* adapter_ids, int32_t topk, const moe_lora_dims* d, void* y,
+                    char* ws, hipStream_t stream, void* const* ev, const float* w1_scale,
+                    const float* w2_scale) {
+  const bool fp8 = w1_scale != nullptr;
   const int T = d->T, h = d->hidden, I = d->inter, E = d->n_experts, nA = d->n_adapters, r = d->rank;
-  const int64_t P = (int64_t)T * topk;
   int* topk_ids = (int*)(ws + L.topk_ids);
   float* topk_w = (float*)(ws + L.topk_w);
   int* tok_flags = (int*)(ws + L.tok_flags);
@@ -332,14 +424,21 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   uint16_t* act = (uint16_t*)(ws + L.act);
   float* dpair = (float*)(ws + L.dpair);
 
+  if (W_router) {  // router GEMM: logits into the workspace
+    float* logits = (float*)(ws + L.logits);
+    if (launch_router_logits((const uint16_t*)x, (const uint16_t*)W_router, T, h, E, logits,
+                             stream) != hipSuccess)
+      return MOELORA_EHIP;
+    router_logits = logits;
+  }
+
   if (!mark(ev, 0, stream)) return MOELORA_EHIP;
   if (launch_route(router_logits, T, E, topk, topk_ids, topk_w, tok_flags, stream) != hipSuccess)
     return MOELORA_EHIP;
   if (!mark(ev, 1, stream)) return MOELORA_EHIP;
 
-  const PathPlan path = pick_path(P, E, h, I);
-  const int nt = path.nt;
-  const int bm = path.bm;
+  const PathPlan& path = pl.path;
+  const int bm = pl.bm;
   AlignArgs al;
   al.topk_ids = topk_ids;
   al.adapter_ids = adapter_ids;
@@ -361,33 +460,9 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   al.sorted_ad = sorted_ad;
   al.n_blocks = n_blocks;
   al.g_lists = (int*)(ws + L.align_lists);
-  const int64_t max_rows = P + (int64_t)E * (bm - 1);
-  const int max_blocks = (int)((max_rows + bm - 1) / bm);
-  const int tiles16 = max_blocks * (bm / 16);
-  // Split the shrink's K by the tiles that can hold pairs (at most P/16 plus one partial tile per
-  // expert), not by the padded grid: padding tiles exit at once.
-  const int64_t live_tiles = std::min<int64_t>(tiles16, (P + 15) / 16 + E);
-  int s1 = pick_splits(live_tiles, h), s2 = pick_splits(live_tiles, I);
-  // On the tiled path (row blocks of >= 64 rows) the shrink takes 64 rows per workgroup where a
-  // sub-block holds few adapter runs, so that a run's A slab is fetched once per 64 rows; the
-  // 16-row shrink then takes the rest. Both use the same K splits, as many as either needs to
-  // fill the chip (MOELORA_SHRINK64=0 turns the 64-row shrink off, for experiments).
-  static int shrink64_env = -1;
-  if (shrink64_env < 0) {
-    const char* env = getenv("MOELORA_SHRINK64");
-    shrink64_env = env ? atoi(env) : 1;
-  }
-  const bool shrink64 = shrink64_env != 0 && path.tiled && r <= 64 && bm % 64 == 0;
-  const int n_sub_max = max_blocks * bm / 64;
-  if (shrink64) {
-    const int64_t live_sub = std::min<int64_t>(n_sub_max, (P + 63) / 64 + E);
-    s1 = std::max(s1, pick_splits(live_sub, h));
-    s2 = std::max(s2, pick_splits(live_sub, I));
-  }
   const size_t lds = align_lds_plan(T, topk, E, nA, &al);
   if (launch_align(al, lds, stream) != hipSuccess) return MOELORA_EHIP;
   if (!mark(ev, 2, stream)) return MOELORA_EHIP;
-
 
   ShrinkArgs sh;
   sh.sorted_pairs = sorted;
@@ -421,26 +496,26 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   g.r = r;
   g.act_out = act;
   g.d_out = dpair;
-  g.n_blocks_max = max_blocks;
+  g.n_blocks_max = pl.max_blocks;
 
   // gate_up: shrink z1 = x A1, then W1 GEMM + z1 B1 + SiLU-and-mul -> act
   sh.X = (const uint16_t*)x;
   sh.x_bytes = (uint32_t)((size_t)T * h * 2);
   sh.Aw = (const uint16_t*)A1;
   sh.K = h;
-  sh.S = s1;
+  sh.S = pl.s1;
   sh.zpart = z1;
   sh.cap = L.cap;
-  sh.after64 = shrink64 ? 1 : 0;
-  if (shrink64 && launch_shrink_tiled(true, sh, n_sub_max, stream) != hipSuccess)
+  sh.after64 = pl.shrink64 ? 1 : 0;
+  if (pl.shrink64 && launch_shrink_tiled(true, sh, pl.n_sub_max, stream) != hipSuccess)
     return MOELORA_EHIP;
-  if (launch_shrink(true, sh, tiles16, stream) != hipSuccess) return MOELORA_EHIP;
+  if (launch_shrink(true, sh, pl.tiles16, stream) != hipSuccess) return MOELORA_EHIP;
   uint16_t* zhl = path.tiled ? (uint16_t*)(ws + L.zhl) : nullptr;
   // the skinny GEMMs add the split parts themselves (one launch fewer per projection); the
   // tiled GEMMs take z as bf16 high and low planes, made by zfinal
+  const int64_t max_rows = (int64_t)pl.max_blocks * bm;
   if (path.tiled &&
-      launch_zfinal(z1, s1, L.cap, r, n_blocks, bm, (int64_t)max_blocks * bm, zhl, stream) !=
-          hipSuccess)
+      launch_zfinal(z1, pl.s1, L.cap, r, n_blocks, bm, max_rows, zhl, stream) != hipSuccess)
     return MOELORA_EHIP;
   if (!mark(ev, 3, stream)) return MOELORA_EHIP;
   g.X = (const uint16_t*)x;
@@ -451,35 +526,15 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   g.Bw = (const uint16_t*)B1;
   g.zhl = zhl;
   g.zpart = z1;
-  g.zsplits = path.tiled ? 0 : s1;
+  g.zsplits = path.tiled ? 0 : pl.s1;
   g.K = h;
   g.N = I;
-  SkinnyPlan plan = pick_skinny(nt, h, I);
-  if (fp8) {
-    // E4M3 rows carry half the bytes per K element: 128-wide K steps keep the bf16 kernels'
-    // bytes in flight per load (measured: decode gate_up 0.35 -> 0.31 ms); down on 32-row
-    // blocks (short K loops of many experts) keeps 64-wide steps
-    plan.gu.p = 4;
-    plan.dn.p = nt == 1 ? 4 : 2;
-  }
-  if (path.tiled) {
-    // tiled down: split K in two when the tiles would fill the chip fewer than four times (the
-    // last, partial round of 256x256 tiles then costs a large share of the time)
-    const int64_t est_tiles = (int64_t)((P + path.bm - 1) / path.bm + E) * (h / path.tc_dn.bn);
-    plan.ksplit = est_tiles < 4 * 256 ? kMaxDownSplit : 1;
-    // MOELORA_DOWN_SPLIT=1|2 overrides it (experiments)
-    static int down_split = -1;
-    if (down_split < 0) {
-      const char* env = getenv("MOELORA_DOWN_SPLIT");
-      down_split = env ? atoi(env) : 0;
-    }
-    if (down_split == 1 || down_split == 2) plan.ksplit = down_split;
-  }
   g.ksplit = 1;
   g.d_split_stride = L.cap * (int64_t)h;
-  g.n_col_tiles = g.N / (plan.gu.split ? 32 : 64 * plan.gu.rt);
-  const hipError_t gu_err = path.tiled ? launch_tiled(path.tc, true, g, stream)
-                                       : launch_skinny(plan.gu, true, g, max_blocks, stream, fp8);
+  g.n_col_tiles = g.N / (pl.sk.gu.split ? 32 : 64 * pl.sk.gu.rt);
+  const hipError_t gu_err = path.tiled
+                                ? launch_tiled(path.tc, true, g, stream)
+                                : launch_skinny(pl.sk.gu, true, g, pl.max_blocks, stream, fp8);
   if (gu_err != hipSuccess) return MOELORA_EHIP;
   if (!mark(ev, 4, stream)) return MOELORA_EHIP;
 
@@ -488,17 +543,16 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   sh.x_bytes = (uint32_t)((size_t)L.cap * I * 2);
   sh.Aw = (const uint16_t*)A2;
   sh.K = I;
-  sh.S = s2;
+  sh.S = pl.s2;
   sh.zpart = z2;
-  if (shrink64 && launch_shrink_tiled(false, sh, n_sub_max, stream) != hipSuccess)
+  if (pl.shrink64 && launch_shrink_tiled(false, sh, pl.n_sub_max, stream) != hipSuccess)
     return MOELORA_EHIP;
-  if (launch_shrink(false, sh, tiles16, stream) != hipSuccess) return MOELORA_EHIP;
+  if (launch_shrink(false, sh, pl.tiles16, stream) != hipSuccess) return MOELORA_EHIP;
   if (path.tiled &&
-      launch_zfinal(z2, s2, L.cap, r, n_blocks, bm, (int64_t)max_blocks * bm, zhl, stream) !=
-          hipSuccess)
+      launch_zfinal(z2, pl.s2, L.cap, r, n_blocks, bm, max_rows, zhl, stream) != hipSuccess)
     return MOELORA_EHIP;
   g.zpart = z2;
-  g.zsplits = path.tiled ? 0 : s2;
+  g.zsplits = path.tiled ? 0 : pl.s2;
   if (!mark(ev, 5, stream)) return MOELORA_EHIP;
   g.X = act;
   g.x_bytes = (uint32_t)((size_t)L.cap * I * 2);
@@ -508,19 +562,64 @@ int forward_impl(const void* x, const float* router_logits, const void* W1, cons
   g.Bw = (const uint16_t*)B2;
   g.K = I;
   g.N = h;
-  g.ksplit = plan.ksplit;
-  g.n_col_tiles = g.N / (64 * plan.dn.rt);
-  const hipError_t dn_err = path.tiled ? launch_tiled(path.tc_dn, false, g, stream)
-                                       : launch_skinny(plan.dn, false, g, max_blocks, stream, fp8);
+  g.ksplit = pl.sk.ksplit;
+  g.n_col_tiles = g.N / (64 * pl.sk.dn.rt);
+  const hipError_t dn_err = path.tiled
+                                ? launch_tiled(path.tc_dn, false, g, stream)
+                                : launch_skinny(pl.sk.dn, false, g, pl.max_blocks, stream, fp8);
   if (dn_err != hipSuccess) return MOELORA_EHIP;
   if (!mark(ev, 6, stream)) return MOELORA_EHIP;
 
   // weighted top-k combine -> y (bf16)
-  if (launch_combine(dpair, plan.ksplit, L.cap * (int64_t)h, pair_row, topk_w, T, topk, h,
+  if (launch_combine(dpair, pl.sk.ksplit, L.cap * (int64_t)h, pair_row, topk_w, T, topk, h,
                      (uint16_t*)y, stream) != hipSuccess)
     return MOELORA_EHIP;
   if (!mark(ev, 7, stream)) return MOELORA_EHIP;
   return MOELORA_OK;
+}
+
+// Host checks of a layer call, before anything is enqueued: sizes, the FP8 path's range,
+// pointers (NULL, 16-byte alignment; W_router and the scales when given), the workspace and the
+// device. logits may be NULL when W_router is given (the router GEMM writes them into the
+// workspace). Fills the plan and layout.
+int check_forward(const void* x, const float* router_logits, const void* W_router, const void* W1,
+                  const void* W2, const void* A1, const void* B1, const void* A2, const void* B2,
+                  const int32_t* adapter_ids, int32_t topk, const moe_lora_dims* d, const void* y,
+                  const void* workspace, size_t workspace_bytes, const float* w1_scale,
+                  const float* w2_scale, bool fp8, ForwardPlan* pl, MoeLoraLayout* L) {
+  int rc = plan_and_layout(d, topk, fp8, pl, L);
+  if (rc != MOELORA_OK) return rc;
+  if (fp8 && pl->path.tiled) return MOELORA_EUNSUPPORTED;
+  if (d->T == 0) return MOELORA_OK;  // empty batch: nothing to do, pointers may be NULL
+  const void* logits_or_router = W_router ? W_router : (const void*)router_logits;
+  const void* ptrs[] = {x, logits_or_router, W1, W2, A1, B1, A2, B2, adapter_ids, y, workspace};
+  for (const void* p : ptrs)
+    if (!p) return MOELORA_ENULL;
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOELORA_EALIGN;
+  if (fp8 && (!w1_scale || !w2_scale)) return MOELORA_ENULL;
+  if (fp8 && ((((uintptr_t)w1_scale) | ((uintptr_t)w2_scale)) & 3u) != 0) return MOELORA_EALIGN;
+  if (((uintptr_t)workspace & 255u) != 0) return MOELORA_EWORKSPACE;
+  if (workspace_bytes < L->total) return MOELORA_EWORKSPACE;
+  return check_device();
+}
+
+// The layer. W_router != nullptr: the router GEMM first writes the logits into the workspace
+// (router_logits unused). w1_scale/w2_scale != nullptr: W1/W2 are E4M3 codes with per-row
+// scales (skinny path only).
+int forward_impl(const void* x, const float* router_logits, const void* W_router, const void* W1,
+                 const void* W2, const void* A1, const void* B1, const void* A2, const void* B2,
+                 const int32_t* adapter_ids, int32_t topk, const moe_lora_dims* d, void* y,
+                 void* workspace, size_t workspace_bytes, void* stream_, void* const* ev,
+                 const float* w1_scale = nullptr, const float* w2_scale = nullptr) {
+  const bool fp8 = w1_scale != nullptr || w2_scale != nullptr;
+  ForwardPlan pl;
+  MoeLoraLayout L;
+  const int rc = check_forward(x, router_logits, W_router, W1, W2, A1, B1, A2, B2, adapter_ids, topk,
+                               d, y, workspace, workspace_bytes, w1_scale, w2_scale, fp8, &pl, &L);
+  if (rc != MOELORA_OK || d->T == 0) return rc;
+  return enqueue_forward(pl, L, x, router_logits, W_router, W1, W2, A1, B1, A2, B2, adapter_ids,
+                         topk, d, y, (char*)workspace, (hipStream_t)stream_, ev, w1_scale, w2_scale);
 }
 
 }  // namespace
@@ -531,8 +630,8 @@ int moe_lora_forward(const void* x, const float* router_logits, const void* W1, 
                      const void* A1, const void* B1, const void* A2, const void* B2,
                      const int32_t* adapter_ids, int32_t topk, const moe_lora_dims* d, void* y,
                      void* workspace, size_t workspace_bytes, void* stream) {
-  return forward_impl(x, router_logits, W1, W2, A1, B1, A2, B2, adapter_ids, topk, d, y, workspace,
-                      workspace_bytes, stream, nullptr);
+  return forward_impl(x, router_logits, nullptr, W1, W2, A1, B1, A2, B2, adapter_ids, topk, d, y,
+                      workspace, workspace_bytes, stream, nullptr);
 }
 
 int moe_lora_forward_timed(const void* x, const float* router_logits, const void* W1,
@@ -541,8 +640,8 @@ int moe_lora_forward_timed(const void* x, const float* router_logits, const void
                            const moe_lora_dims* d, void* y, void* workspace,
                            size_t workspace_bytes, void* stream, void* const* stage_events) {
   if (!stage_events) return MOELORA_ENULL;
-  return forward_impl(x, router_logits, W1, W2, A1, B1, A2, B2, adapter_ids, topk, d, y, workspace,
-                      workspace_bytes, stream, stage_events);
+  return forward_impl(x, router_logits, nullptr, W1, W2, A1, B1, A2, B2, adapter_ids, topk, d, y,
+                      workspace, workspace_bytes, stream, stage_events);
 }
 
 int moe_lora_router_logits(const void* x, const void* W_router, int32_t T, int32_t hidden,
@@ -567,19 +666,12 @@ int moe_lora_forward_routed(const void* x, const void* W_router, const void* W1,
                             const void* A1, const void* B1, const void* A2, const void* B2,
                             const int32_t* adapter_ids, int32_t topk, const moe_lora_dims* d,
                             void* y, void* workspace, size_t workspace_bytes, void* stream) {
-  int rc = validate_dims(d, topk);
-  if (rc != MOELORA_OK) return rc;
-  if (d->T == 0) return MOELORA_OK;
-  if (!workspace || !W_router) return MOELORA_ENULL;
-  if (((uintptr_t)workspace & 255u) != 0) return MOELORA_EWORKSPACE;
-  MoeLoraLayout L;
-  moelora_make_layout(d->T, d->hidden, d->inter, d->n_experts, d->n_adapters, d->rank, topk, &L);
-  if (workspace_bytes < L.total) return MOELORA_EWORKSPACE;
-  float* logits = (float*)((char*)workspace + L.logits);
-  rc = moe_lora_router_logits(x, W_router, d->T, d->hidden, d->n_experts, logits, stream);
-  if (rc != MOELORA_OK) return rc;
-  return forward_impl(x, logits, W1, W2, A1, B1, A2, B2, adapter_ids, topk, d, y, workspace,
-                      workspace_bytes, stream, nullptr);
+  if (d && d->T > 0 && !W_router) {  // (forward_impl takes a NULL W_router as "logits given")
+    const int rc = validate_dims(d, topk);
+    return rc != MOELORA_OK ? rc : MOELORA_ENULL;
+  }
+  return forward_impl(x, nullptr, W_router, W1, W2, A1, B1, A2, B2, adapter_ids, topk, d, y,
+                      workspace, workspace_bytes, stream, nullptr);
 }
 
 int moe_lora_forward_fp8(const void* x, const float* router_logits, const void* W1q,
@@ -592,7 +684,7 @@ int moe_lora_forward_fp8(const void* x, const float* router_logits, const void* 
     const int rc = validate_dims(d, topk);
     return rc != MOELORA_OK ? rc : MOELORA_ENULL;
   }
-  return forward_impl(x, router_logits, W1q, W2q, A1, B1, A2, B2, adapter_ids, topk, d, y,
+  return forward_impl(x, router_logits, nullptr, W1q, W2q, A1, B1, A2, B2, adapter_ids, topk, d, y,
                       workspace, workspace_bytes, stream, stage_events, W1_scale, W2_scale);
 }
 
@@ -757,8 +849,10 @@ int moe_lora_route_align(const float* router_logits, const int32_t* adapter_ids,
   for (const void* p : ptrs)
     if (((uintptr_t)p & 3u) != 0) return MOELORA_EALIGN;
   if (((uintptr_t)workspace & 255u) != 0) return MOELORA_EWORKSPACE;
+  ForwardPlan pl;
   MoeLoraLayout L;
-  moelora_make_layout(d->T, d->hidden, d->inter, d->n_experts, d->n_adapters, d->rank, topk, &L);
+  rc = plan_and_layout(d, topk, false, &pl, &L);
+  if (rc != MOELORA_OK) return rc;
   if (workspace_bytes < L.total) return MOELORA_EWORKSPACE;
   rc = check_device();
   if (rc != MOELORA_OK) return rc;

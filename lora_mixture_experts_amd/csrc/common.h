@@ -89,4 +89,5 @@ struct MoeLoraLayout {
   int max_bm;      // largest row-block size any path uses
 };
 
-bool moelora_make_layout(int T, int h, int I, int E, int nA, int r, int topk, MoeLoraLayout* L);
+bool moelora_make_layout(int T, int h, int I, int E, int nA, int r, int topk, int bm, int dsplit,
+                         MoeLoraLayout* L);

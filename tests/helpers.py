@@ -47,6 +47,41 @@ def oracle_rows(inp: dict, topk: int, tokens=None) -> np.ndarray:
     return oracle.forward(host, topk)
 
 
+def expected_layout(logits, adapter_ids, topk: int, n_experts: int, n_adapters: int, block_m: int) -> dict:
+    """The routing and sorted-layout tables a layer call must produce at row blocks of block_m
+    (seg_pad 1), from the oracle's route and align; the per-block and per-row tables follow from
+    those by their definitions (expert of the padded region holding the block's first row,
+    segment holding it or -1 for padding, inverse of the sorted order, adapter of the row's
+    token or -1)."""
+    L = logits.cpu() if isinstance(logits, torch.Tensor) else torch.from_numpy(np.asarray(logits))
+    ad = (adapter_ids.cpu().numpy() if isinstance(adapter_ids, torch.Tensor)
+          else np.asarray(adapter_ids)).astype(np.int32)
+    ids, w = oracle.route(L, topk)
+    al = oracle.align(ids, ad, n_experts, n_adapters, 1, block_m)
+    sp, off, seg = al["sorted_pairs"], al["expert_offsets"], al["seg_table"]
+    total = len(sp)
+    assert total % block_m == 0
+    n_blocks = total // block_m
+    rows0 = np.arange(n_blocks, dtype=np.int64) * block_m
+    block_expert = (np.searchsorted(off, rows0, side="right") - 1).astype(np.int32)
+    block_seg = np.full(n_blocks, -1, np.int32)
+    for s, (_, _, st, cnt) in enumerate(seg):
+        b_lo = -(-int(st) // block_m)
+        for b in range(b_lo, n_blocks):
+            if b * block_m >= st + cnt:
+                break
+            block_seg[b] = s
+    real = sp >= 0
+    pair_row = np.full(ids.size, -1, np.int32)
+    pair_row[sp[real]] = np.nonzero(real)[0].astype(np.int32)
+    sorted_ad = np.full(total, -1, np.int32)
+    sorted_ad[real] = ad[sp[real] // topk]
+    return {"topk_ids": ids, "topk_w": w.astype(np.float32), "sorted_pairs": sp,
+            "expert_offsets": off, "seg_table": seg, "n_blocks": n_blocks,
+            "block_expert": block_expert, "block_seg": block_seg, "pair_row": pair_row,
+            "sorted_ad": sorted_ad}
+
+
 def check_close(y_gpu: torch.Tensor, y_ref: np.ndarray, tol: float = TOL, what: str = ""):
     y = y_gpu.double().cpu().numpy()
     assert y.shape == y_ref.shape, (y.shape, y_ref.shape)

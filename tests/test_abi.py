@@ -121,3 +121,88 @@ def test_binding_refuses_host_tensors():
     x = torch.zeros(4, 128, dtype=torch.bfloat16)
     with pytest.raises((ValueError, TypeError)):
         ml._expect(x, "x", torch.bfloat16, (4, 128))
+
+
+def _routed(ptrs, d, topk=2, ws_bytes=None):
+    """moe_lora_forward_routed with ptrs = x, W_router, W1, W2, A1, B1, A2, B2, adapter_ids, y,
+    workspace (aligned fake addresses that the host checks reject before any device call)."""
+    if ws_bytes is None:
+        ws_bytes = ml.workspace_size(d, topk) if ml.workspace_size(d, topk) else 1 << 40
+    return ml.lib().moe_lora_forward_routed(*ptrs[:9], topk, ctypes.byref(d), ptrs[9], ptrs[10],
+                                            ws_bytes, None)
+
+
+def test_forward_routed_host_validation_without_device():
+    """Every pointer of the routed entry (W1 included) is checked before the router GEMM is
+    enqueued: with no GPU here, any enqueue would fail with EHIP or EDEVICE instead."""
+    d = Dims(16, 256, 512, 8, 4, 8)
+    for i in range(11):
+        p = list(FAKE)
+        p[i] = None
+        assert _routed(p, d) == ml.ENULL, i
+    for i in range(10):
+        p = list(FAKE)
+        p[i] += 8
+        assert _routed(p, d) == ml.EALIGN, i
+    p = list(FAKE)
+    p[10] += 16
+    assert _routed(p, d) == ml.EWORKSPACE
+    assert _routed(FAKE, d, ws_bytes=ml.workspace_size(d, 2) - 1) == ml.EWORKSPACE
+    assert _routed(FAKE, Dims(16, 250, 512, 8, 4, 8)) == ml.EINVAL_DIMS
+    assert _routed([None] * 11, Dims(0, 256, 512, 8, 4, 8)) == ml.OK
+
+
+def test_forward_fp8_host_validation_without_device():
+    lib = ml.lib()
+    d = Dims(16, 256, 512, 8, 4, 8)
+    ws = ml.workspace_size(d, 2)
+    # x, logits, W1q, W1_scale, W2q, W2_scale, A1, B1, A2, B2, adapter_ids, y, workspace
+    base = [0x10000 * (i + 1) for i in range(13)]
+
+    def call(pp, dd=d, topk=2):
+        return lib.moe_lora_forward_fp8(*pp[:11], topk, ctypes.byref(dd), pp[11], pp[12], ws, None, None)
+
+    for i in range(13):
+        q = list(base)
+        q[i] = None
+        assert call(q) == ml.ENULL, i
+    q = list(base)
+    q[3] += 2  # scales need 4-byte alignment
+    assert call(q) == ml.EALIGN
+    # above 24 token-expert pairs per expert the FP8 entry is not supported
+    big = Dims(200, 256, 512, 8, 4, 8)
+    assert call(base, dd=big) == ml.EUNSUPPORTED
+
+
+def test_workspace_layout_follows_the_path():
+    """The workspace is sized for the path a call takes: weight-streaming calls (few rows per
+    expert) reserve 16- or 32-row blocks, tiled calls 64 to 256; every region lies inside it."""
+    decode = Dims(64, 4096, 11008, 16, 8, 16)
+    info = ml.workspace_layout(decode, 2)
+    assert info["tiled"] == 0 and info["block_m"] == 16
+    assert info["capacity"] == 512  # 128 pairs + 16 experts x 15 padding rows, rounded to 256
+    assert info["workspace_bytes"] == ml.workspace_size(decode, 2)
+    assert info["workspace_bytes"] < 64 << 20
+    prefill = Dims(4096, 4096, 14336, 8, 32, 64)
+    info = ml.workspace_layout(prefill, 2)
+    assert info["tiled"] == 1 and info["block_m"] == 256
+    assert info["capacity"] == 8192 + 8 * 256
+    regions = ("topk_ids", "topk_w", "sorted_pairs", "expert_offsets", "seg_table", "n_seg", "n_blocks",
+               "block_expert", "block_seg", "pair_row", "sorted_ad")
+    for dd in (decode, prefill, Dims(256, 2048, 768, 128, 64, 32), Dims(1024, 4096, 11008, 16, 1024, 16)):
+        info = ml.workspace_layout(dd, 2 if dd.n_experts < 128 else 8)
+        offs = sorted(info[r] for r in regions)
+        assert len(set(offs)) == len(offs)
+        assert all(o % 256 == 0 and 0 < o < info["workspace_bytes"] for o in offs)
+    with pytest.raises(ml.MoeLoraError):
+        ml.workspace_layout(Dims(16, 250, 512, 8, 4, 8), 2)
+
+
+def test_activations_over_2gib_rejected():
+    """The activations [capacity][inter] bf16 are read with 32-bit offsets: sizes whose
+    capacity times inter reaches 2 GiB are refused, judged on the capacity the path uses."""
+    # 128-row tiles: capacity = round_up(T*k + 127*E, 256)
+    ok = Dims(200000, 128, 4096, 1, 1, 8)
+    assert ml.workspace_size(ok, 1) > 0
+    too_big = Dims(270000, 128, 4096, 1, 1, 8)  # 270 K rows x 4096 x 2 B > 2 GiB
+    assert ml.workspace_size(too_big, 1) == 0

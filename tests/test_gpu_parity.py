@@ -13,7 +13,7 @@ import lora_mixture_experts_amd as ml
 import oracle
 from synth import configs
 from synth.configs import Workload
-from tests.helpers import check_close, oracle_rows, sample_tokens
+from tests.helpers import check_close, expected_layout, oracle_rows, sample_tokens
 
 pytestmark = pytest.mark.gpu
 
@@ -31,10 +31,13 @@ def _say(msg):
 
 # ----------------------------------------------------------------------------- route + align
 
+# (seg_pad, block_m) settings: every one the forward uses (seg_pad 1 with 16-, 32-, 64-, 128- and
+# 256-row blocks) and a few with padded segments
 ROUTE_CASES = [
     ("tiny", 1, 1), ("tiny", 4, 16), ("decode", 1, 16), ("decode", 16, 16), ("prefill", 1, 64),
     ("prefill", 16, 128), ("fg", 1, 32), ("fg", 8, 32), ("stress_distinct", 1, 64),
-    ("stress_same", 1, 64), ("stress_distinct", 16, 256),
+    ("stress_same", 1, 64), ("stress_distinct", 16, 256), ("prefill", 1, 256), ("prefill", 1, 128),
+    ("stress_distinct", 1, 128), ("stress_same", 1, 256), ("fg", 1, 16), ("tiny", 1, 128),
 ]
 
 
@@ -135,6 +138,33 @@ def _run(inp: dict, topk: int, workspace=None):
     return y
 
 
+def check_forward_tables(ws: torch.Tensor, w: Workload, logits, adapter_ids):
+    """The forward's own routing and sorted-layout tables in its workspace, bit for bit against
+    the oracle's routing and align at the row-block size the call used (seg_pad 1), and the
+    derived tables (row block -> expert and first segment, pair -> row, row -> adapter)."""
+    d = _dims(w)
+    got = ml.read_layout_tables(ws, d, w.topk)
+    bm = got["info"]["block_m"]
+    ref = expected_layout(logits, adapter_ids, w.topk, w.n_experts, w.n_adapters, bm)
+    np.testing.assert_array_equal(got["topk_ids"], ref["topk_ids"])
+    np.testing.assert_allclose(got["topk_w"], ref["topk_w"], rtol=0, atol=2e-6)
+    assert got["n_blocks"] == ref["n_blocks"], (got["n_blocks"], ref["n_blocks"])
+    for key in ("sorted_pairs", "expert_offsets", "seg_table", "block_expert", "block_seg", "pair_row",
+                "sorted_ad"):
+        np.testing.assert_array_equal(got[key], ref[key], err_msg=f"{w.name}: {key} (block_m {bm})")
+    return got
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_forward_layout_tables_bit_exact(name):
+    w = SMALL[name]
+    _say(f"forward tables {name}")
+    inp = _small_inputs(w, 1)
+    ws = ml.new_workspace(_dims(w), w.topk, DEV)
+    _run(inp, w.topk, workspace=ws)
+    check_forward_tables(ws, w, inp["logits"], inp["adapter_ids"])
+
+
 @pytest.mark.parametrize("name", list(SMALL))
 @pytest.mark.parametrize("b_scale", [1.0, 10.0])
 def test_forward_small_vs_oracle(name, b_scale):
@@ -207,8 +237,13 @@ def test_forward_flags_bad_adapter_and_nonfinite_logit():
     check_close(y[torch.from_numpy(keep).long().to(DEV)], oracle_rows(inp, w.topk, keep), what="finite tokens")
 
 
-def test_forward_poisoned_workspace_and_determinism():
-    w = SMALL["fg_small"]
+@pytest.mark.parametrize("name", ["fg_small", "tiled64", "tiled256_r64", "tiled128_runs"])
+def test_forward_poisoned_workspace_and_determinism(name):
+    """Whatever the workspace held before (all-ones bytes, 0x7F bytes, a fresh allocation), the
+    call gives the same bytes, within the bound of the oracle: no stage reads a region it did not
+    write first (z planes, act, the down split parts, align tables)."""
+    w = SMALL[name]
+    _say(f"poisoned workspace {name}")
     inp = _small_inputs(w, 4)
     ws = ml.new_workspace(_dims(w), w.topk, DEV)
     ws.fill_(0xFF)
@@ -222,32 +257,69 @@ def test_forward_poisoned_workspace_and_determinism():
 
 # ----------------------------------------------------------------------------- full-size configs
 
-def _full_case(name: str, seed: int = 0, b_scale: float = 1.0, n_sample: int = 12):
+def _all_tokens_chunked(inp, w, y, what, chunk=256):
+    """y against the oracle on every token, a chunk of tokens at a time (only the adapters a
+    chunk uses are copied to the host)."""
+    worst = 0.0
+    for t0 in range(0, w.T, chunk):
+        toks = np.arange(t0, min(w.T, t0 + chunk), dtype=np.int32)
+        y_ref = oracle_rows(inp, w.topk, toks)
+        worst = max(worst, check_close(y[torch.from_numpy(toks).long().to(DEV)], y_ref,
+                                       what=f"{what} tokens {t0}..{toks[-1]}"))
+    return worst
+
+
+def _block_tokens(tables, topk: int, sub: int = 64) -> np.ndarray:
+    """Tokens of the first and last real row of every `sub`-row sub-block of the sorted layout
+    (so every row block of every expert, every 64-row shrink sub-block and every column tile of
+    those rows is compared), plus the batch's first and last token."""
+    sp = tables["sorted_pairs"]
+    toks = set()
+    for b0 in range(0, len(sp), sub):
+        real = sp[b0:b0 + sub]
+        real = real[real >= 0]
+        if real.size:
+            toks.add(int(real[0]) // topk)
+            toks.add(int(real[-1]) // topk)
+    return np.array(sorted(toks), dtype=np.int32)
+
+
+def _full_case(name: str, seed: int = 0, b_scale: float = 1.0, adapters=None):
+    """Full-size layer call: its routing tables bit for bit, then y against the oracle on every
+    token (prefill: two tokens per 64-row sub-block of the sorted layout)."""
     w = configs.WORKLOADS[name]
     _say(f"full-size {name}: generating inputs on the GPU")
     inp = configs.make_inputs(w, seed, device=DEV, b_scale=b_scale)
+    if adapters is not None:
+        inp["adapter_ids"] = adapters
+    ws = ml.new_workspace(_dims(w), w.topk, DEV)
     _say(f"full-size {name}: forward")
     y = ml.forward(inp["x"], inp["logits"], inp["W1"], inp["W2"], inp["A1"], inp["B1"], inp["A2"],
-                   inp["B2"], inp["adapter_ids"], w.topk)
+                   inp["B2"], inp["adapter_ids"], w.topk, workspace=ws)
     torch.cuda.synchronize()
-    toks = sample_tokens(w.T, n_sample, seed)
-    _say(f"full-size {name}: oracle on {len(toks)} tokens")
-    y_ref = oracle_rows(inp, w.topk, toks)
-    rel = check_close(y[torch.from_numpy(toks).long().to(DEV)], y_ref, what=name)
+    tables = check_forward_tables(ws, w, inp["logits"].cpu(), inp["adapter_ids"].cpu())
+    if w.T <= 1024:
+        _say(f"full-size {name}: oracle on all {w.T} tokens")
+        rel = _all_tokens_chunked(inp, w, y, name)
+    else:
+        toks = _block_tokens(tables, w.topk)
+        _say(f"full-size {name}: oracle on {len(toks)} tokens covering every 64-row sub-block")
+        rel = check_close(y[torch.from_numpy(toks).long().to(DEV)], oracle_rows(inp, w.topk, toks),
+                          what=name)
     _say(f"full-size {name}: max rel err {rel:.2e}")
-    return inp, y
+    return inp, y, ws
 
 
 @pytest.mark.parametrize("name", ["decode", "prefill", "fg"])
-def test_forward_full_size_sampled(name):
-    inp, y = _full_case(name)
-    # the same call again gives the same bytes
+def test_forward_full_size(name):
+    inp, y, ws = _full_case(name)
+    # the same call again, on the same workspace, gives the same bytes
     w = configs.WORKLOADS[name]
     y2 = ml.forward(inp["x"], inp["logits"], inp["W1"], inp["W2"], inp["A1"], inp["B1"], inp["A2"],
-                    inp["B2"], inp["adapter_ids"], w.topk)
+                    inp["B2"], inp["adapter_ids"], w.topk, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(y, y2)
-    del inp
+    del inp, ws
     torch.cuda.empty_cache()
 
 
@@ -256,18 +328,11 @@ def test_forward_full_size_decode_amplified_b():
     torch.cuda.empty_cache()
 
 
-def test_forward_full_size_stress_distinct_and_same():
-    w = configs.WORKLOADS["stress_distinct"]
-    inp, y = _full_case("stress_distinct", n_sample=8)
-    same = dict(inp)
-    same["adapter_ids"] = configs.make_adapter_ids(configs.WORKLOADS["stress_same"], 0, DEV)
-    y_same = ml.forward(same["x"], same["logits"], same["W1"], same["W2"], same["A1"], same["B1"],
-                        same["A2"], same["B2"], same["adapter_ids"], w.topk)
-    torch.cuda.synchronize()
-    toks = sample_tokens(w.T, 8, 1)
-    check_close(y_same[torch.from_numpy(toks).long().to(DEV)], oracle_rows(same, w.topk, toks),
-                what="stress_same")
-    del inp, same
+@pytest.mark.parametrize("name", ["stress_distinct", "stress_same"])
+def test_forward_full_size_stress(name):
+    """The adapter-diversity batch with every token on its own adapter, and the same batch with
+    every token on adapter 0: every token of both against the oracle."""
+    _full_case(name)
     torch.cuda.empty_cache()
 
 
@@ -321,7 +386,7 @@ def test_forward_fp8_tiled_size_unsupported():
 
 
 @pytest.mark.parametrize("name", ["decode", "fg"])
-def test_forward_fp8_full_size_sampled(name):
+def test_forward_fp8_full_size(name):
     w = configs.WORKLOADS[name]
     _say(f"full-size fp8 {name}: generating inputs on the GPU")
     inp = configs.make_inputs_fp8(w, 0, device=DEV)
@@ -330,10 +395,8 @@ def test_forward_fp8_full_size_sampled(name):
             inp["A1"], inp["B1"], inp["A2"], inp["B2"], inp["adapter_ids"], w.topk)
     y = ml.forward_fp8(*args)
     torch.cuda.synchronize()
-    toks = sample_tokens(w.T, 12, 0)
-    _say(f"full-size fp8 {name}: oracle on {len(toks)} tokens")
-    y_ref = oracle_rows(inp, w.topk, toks)
-    rel = check_close(y[torch.from_numpy(toks).long().to(DEV)], y_ref, what=f"fp8 {name}")
+    _say(f"full-size fp8 {name}: oracle on all {w.T} tokens")
+    rel = _all_tokens_chunked(inp, w, y, f"fp8 {name}")
     _say(f"full-size fp8 {name}: max rel err {rel:.2e}")
     y2 = ml.forward_fp8(*args)
     torch.cuda.synchronize()
