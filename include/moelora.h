@@ -56,6 +56,7 @@ extern "C" {
 #define MOELORA_EHIP (-5)        /* a HIP launch or runtime call failed */
 #define MOELORA_EDEVICE (-6)     /* the current device is not gfx950 */
 #define MOELORA_EUNSUPPORTED (-7) /* FP8 weights with more than 24 token-expert pairs per expert */
+#define MOELORA_ESCRATCH (-8)     /* moe_lora_forward_noalloc: the call needs more than its scratch */
 
 /* Device-side flags reported by moe_lora_debug_status. */
 #define MOELORA_FLAG_NONFINITE_LOGIT 1u
@@ -124,6 +125,24 @@ int moe_lora_forward_timed(const void *x, const float *router_logits, const void
                            const void *B2, const int32_t *adapter_ids, int32_t topk,
                            const moe_lora_dims *d, void *y, void *workspace,
                            size_t workspace_bytes, void *stream, void *const *stage_events);
+
+/* moe_lora_forward for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same layer and results,
+ * with the workspace taken from a static device array of 128 MiB inside the library instead of
+ * a caller buffer. Each GPU the library runs on holds its own copy of that array from the
+ * device's first call until the process ends; the call itself allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine). The caller still passes every input and y, device
+ * memory as in moe_lora_forward. Sizes whose workspace (moe_lora_workspace_size) exceeds
+ * 128 MiB are rejected with MOELORA_ESCRATCH before any device work: the decode, fine-grained
+ * and adapter-stress sizes fit, 256-row prefill layouts do not. Every call on one GPU shares
+ * that GPU's array, which keeps the last call's contents: two calls that overlap on one GPU
+ * (different streams, or different threads without ordering) race and must not be issued; calls
+ * ordered on one stream are safe. The data flags of moe_lora_debug_status are not readable for
+ * these calls. Same other errors as moe_lora_forward. */
+int moe_lora_forward_noalloc(const void *x, const float *router_logits, const void *W1,
+                             const void *W2, const void *A1, const void *B1, const void *A2,
+                             const void *B2, const int32_t *adapter_ids, int32_t topk,
+                             const moe_lora_dims *d, void *y, void *stream);
 
 /* Router logits (page "vLLM MoE LoRA SageMaker Bedrock", section "Entendendo os Modelos MoE":
  * the router scores every expert for each token): logits[t][e] = sum_c x[t][c] W_router[e][c],

@@ -16,13 +16,14 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoelora.so")
 
-OK, EINVAL_DIMS, ENULL, EALIGN, EWORKSPACE, EHIP, EDEVICE, EUNSUPPORTED = 0, -1, -2, -3, -4, -5, -6, -7
+OK, EINVAL_DIMS, ENULL, EALIGN, EWORKSPACE, EHIP, EDEVICE, EUNSUPPORTED, ESCRATCH = 0, -1, -2, -3, -4, -5, -6, -7, -8
 FLAG_NONFINITE_LOGIT, FLAG_ADAPTER_RANGE = 1, 2
 
 EXPORTS = ("moe_lora_workspace_size", "moe_lora_forward", "moe_lora_forward_timed", "moe_lora_forward_fp8",
            "moe_lora_sorted_capacity", "moe_lora_route_align", "moe_lora_strerror",
            "moe_lora_debug_status", "moe_lora_sgmv_workspace_size", "moe_lora_sgmv",
-           "moe_lora_router_logits", "moe_lora_forward_routed", "moe_lora_workspace_layout")
+           "moe_lora_router_logits", "moe_lora_forward_routed", "moe_lora_workspace_layout",
+           "moe_lora_forward_noalloc")
 N_STAGES = 7
 STAGES = ("route", "align", "shrink_gate_up", "gate_up", "shrink_down", "down", "combine")
 
@@ -70,6 +71,8 @@ def lib() -> ctypes.CDLL:
         L.moe_lora_forward_fp8.argtypes = [P, P, P, P, P, P, P, P, P, P, P, i32, D, P, P, ctypes.c_size_t, P,
                                            ctypes.POINTER(ctypes.c_void_p)]
         L.moe_lora_forward_fp8.restype = ctypes.c_int
+        L.moe_lora_forward_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, i32, D, P, P]
+        L.moe_lora_forward_noalloc.restype = ctypes.c_int
         L.moe_lora_router_logits.argtypes = [P, P, i32, i32, i32, P, P]
         L.moe_lora_router_logits.restype = ctypes.c_int
         L.moe_lora_forward_routed.argtypes = [P, P, P, P, P, P, P, P, P, i32, D, P, P, ctypes.c_size_t, P]
@@ -219,6 +222,33 @@ def forward(x, router_logits, W1, W2, A1, B1, A2, B2, adapter_ids, topk: int, y=
         handles = (ctypes.c_void_p * (N_STAGES + 1))(
             *[ev.cuda_event if ev is not None else None for ev in stage_events])
         _check(lib().moe_lora_forward_timed(*args, handles), "moe_lora_forward_timed")
+    return y
+
+
+def forward_noalloc(x, router_logits, W1, W2, A1, B1, A2, B2, adapter_ids, topk: int,
+                    y=None) -> torch.Tensor:
+    """forward without a workspace argument (moe_lora_forward_noalloc): the library uses its
+    static 128 MiB device scratch. Raises MoeLoraError(ESCRATCH) when the sizes need more.
+    Calls on one GPU share that scratch and must be ordered on one stream."""
+    d = dims_of(x, W1, A1)
+    T, h, I, E, nA, r = d.T, d.hidden, d.inter, d.n_experts, d.n_adapters, d.rank
+    bf = torch.bfloat16
+    _expect(x, "x", bf, (T, h))
+    _expect(router_logits, "router_logits", torch.float32, (T, E))
+    _expect(W1, "W1", bf, (E, 2 * I, h))
+    _expect(W2, "W2", bf, (E, h, I))
+    _expect(A1, "A1", bf, (nA, E, r, h))
+    _expect(B1, "B1", bf, (nA, E, 2 * I, r))
+    _expect(A2, "A2", bf, (nA, E, r, I))
+    _expect(B2, "B2", bf, (nA, E, h, r))
+    _expect(adapter_ids, "adapter_ids", torch.int32, (T,))
+    if y is None:
+        y = torch.empty((T, h), dtype=bf, device=x.device)
+    _expect(y, "y", bf, (T, h))
+    _check(lib().moe_lora_forward_noalloc(_ptr(x), _ptr(router_logits), _ptr(W1), _ptr(W2), _ptr(A1),
+                                          _ptr(B1), _ptr(A2), _ptr(B2), _ptr(adapter_ids), topk,
+                                          ctypes.byref(d), _ptr(y), _stream(x.device)),
+           "moe_lora_forward_noalloc")
     return y
 
 

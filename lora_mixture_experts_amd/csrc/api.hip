@@ -1,6 +1,7 @@
 // C ABI of libmoelora: argument validation, workspace carve-up and the launch sequence of the
 // fused MoE + multi-LoRA layer (declared in include/moelora.h).
 #include <algorithm>
+#include <mutex>
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
@@ -15,6 +16,7 @@ namespace {
 
 constexpr int kMaxBM = 256;      // largest row block any GEMM path uses
 constexpr int kMaxDownSplit = 2;  // K splits of the down GEMM
+constexpr size_t kScratchBytes = (size_t)128 << 20;  // static scratch of the no-alloc entry
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 int64_t round_up64(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
@@ -388,6 +390,9 @@ const char* moe_lora_strerror(int code) {
     case MOELORA_EHIP: return "HIP launch or runtime error";
     case MOELORA_EDEVICE: return "current device is not gfx950";
     case MOELORA_EUNSUPPORTED: return "FP8 weights take at most 24 token-expert pairs per expert";
+    case MOELORA_ESCRATCH:
+      return "the call needs more workspace than the static scratch of moe_lora_forward_noalloc "
+             "(128 MiB)";
     default: return "unknown error code";
   }
 }
@@ -586,21 +591,25 @@ int check_forward(const void* x, const float* router_logits, const void* W_route
                   const void* W2, const void* A1, const void* B1, const void* A2, const void* B2,
                   const int32_t* adapter_ids, int32_t topk, const moe_lora_dims* d, const void* y,
                   const void* workspace, size_t workspace_bytes, const float* w1_scale,
-                  const float* w2_scale, bool fp8, ForwardPlan* pl, MoeLoraLayout* L) {
+                  const float* w2_scale, bool fp8, ForwardPlan* pl, MoeLoraLayout* L,
+                  bool in_scratch = false) {
   int rc = plan_and_layout(d, topk, fp8, pl, L);
   if (rc != MOELORA_OK) return rc;
   if (fp8 && pl->path.tiled) return MOELORA_EUNSUPPORTED;
+  if (in_scratch && L->total > kScratchBytes) return MOELORA_ESCRATCH;
   if (d->T == 0) return MOELORA_OK;  // empty batch: nothing to do, pointers may be NULL
   const void* logits_or_router = W_router ? W_router : (const void*)router_logits;
+  // (the workspace last: the no-alloc entry has none)
   const void* ptrs[] = {x, logits_or_router, W1, W2, A1, B1, A2, B2, adapter_ids, y, workspace};
-  for (const void* p : ptrs)
-    if (!p) return MOELORA_ENULL;
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return MOELORA_EALIGN;
+  const int n_ptrs = in_scratch ? 10 : 11;
+  for (int i = 0; i < n_ptrs; ++i)
+    if (!ptrs[i]) return MOELORA_ENULL;
+  for (int i = 0; i < n_ptrs; ++i)
+    if (!aligned16(ptrs[i])) return MOELORA_EALIGN;
   if (fp8 && (!w1_scale || !w2_scale)) return MOELORA_ENULL;
   if (fp8 && ((((uintptr_t)w1_scale) | ((uintptr_t)w2_scale)) & 3u) != 0) return MOELORA_EALIGN;
-  if (((uintptr_t)workspace & 255u) != 0) return MOELORA_EWORKSPACE;
-  if (workspace_bytes < L->total) return MOELORA_EWORKSPACE;
+  if (!in_scratch && ((uintptr_t)workspace & 255u) != 0) return MOELORA_EWORKSPACE;
+  if (!in_scratch && workspace_bytes < L->total) return MOELORA_EWORKSPACE;
   return check_device();
 }
 
@@ -686,6 +695,54 @@ int moe_lora_forward_fp8(const void* x, const float* router_logits, const void* 
   }
   return forward_impl(x, router_logits, nullptr, W1q, W2q, A1, B1, A2, B2, adapter_ids, topk, d, y,
                       workspace, workspace_bytes, stream, stage_events, W1_scale, W2_scale);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Static scratch of moe_lora_forward_noalloc: the workspace of a layer call for callers that
+// cannot allocate. One copy per GPU, alive until the process ends. In host code `scratch` is a
+// host-side stand-in for the symbol, never a device address: kernels and copies get the
+// per-device address that hipGetSymbolAddress returns.
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];  // device address of `scratch` on each device, once looked up
+
+// The address of this device's copy of `scratch` (looked up on the device's first call, with
+// that device current), or nullptr on error.
+void* scratch_on_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_lora_forward_noalloc(const void* x, const float* router_logits, const void* W1,
+                             const void* W2, const void* A1, const void* B1, const void* A2,
+                             const void* B2, const int32_t* adapter_ids, int32_t topk,
+                             const moe_lora_dims* d, void* y, void* stream) {
+  ForwardPlan pl;
+  MoeLoraLayout L;
+  const int rc = check_forward(x, router_logits, nullptr, W1, W2, A1, B1, A2, B2, adapter_ids,
+                               topk, d, y, nullptr, 0, nullptr, nullptr, false, &pl, &L, true);
+  if (rc != MOELORA_OK || d->T == 0) return rc;
+  // The layer needs no zeroed workspace: every region a kernel reads was written earlier in the
+  // same call, so nothing is cleared between calls.
+  char* ws = (char*)scratch_on_current_device();
+  if (!ws) return MOELORA_EHIP;
+  return enqueue_forward(pl, L, x, router_logits, nullptr, W1, W2, A1, B1, A2, B2, adapter_ids, topk,
+                         d, y, ws, (hipStream_t)stream, nullptr, nullptr, nullptr);
 }
 
 namespace {

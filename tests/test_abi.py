@@ -206,3 +206,26 @@ def test_activations_over_2gib_rejected():
     assert ml.workspace_size(ok, 1) > 0
     too_big = Dims(270000, 128, 4096, 1, 1, 8)  # 270 K rows x 4096 x 2 B > 2 GiB
     assert ml.workspace_size(too_big, 1) == 0
+
+
+def test_forward_noalloc_host_validation_without_device():
+    """The no-alloc entry takes no workspace: sizes whose workspace exceeds its 128 MiB scratch
+    are refused with ESCRATCH, and pointers are checked, all before any device call."""
+    lib = ml.lib()
+
+    def call(ptrs, d, topk=2):
+        return lib.moe_lora_forward_noalloc(*ptrs[:9], topk, ctypes.byref(d), ptrs[9], None)
+
+    d = Dims(16, 256, 512, 8, 4, 8)
+    for i in range(10):
+        p = list(FAKE[:10])
+        p[i] = None
+        assert call(p, d) == ml.ENULL, i
+        p = list(FAKE[:10])
+        p[i] += 8
+        assert call(p, d) == ml.EALIGN, i
+    prefill = Dims(4096, 4096, 14336, 8, 32, 64)
+    assert ml.workspace_size(prefill, 2) > 128 << 20
+    assert call(FAKE[:10], prefill) == ml.ESCRATCH
+    assert ml.strerror(ml.ESCRATCH) != "unknown error code"
+    assert call([None] * 10, Dims(0, 256, 512, 8, 4, 8)) == ml.OK
