@@ -85,6 +85,70 @@ def measured_traffic(workload: str):
         return None
 
 
+def host_cpu() -> dict:
+    """CPU model and the threads this process may use (for the oracle baseline)."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        avail = os.cpu_count()
+    return {"model": model, "logical_cpus_available": avail}
+
+
+def onbox_peaks(torch, ml, dev) -> dict:
+    """The ceilings this box sustains, measured with the library's probes: a streaming read of
+    4 GiB (HBM) and a loop of independent bf16 32x32x16 MFMAs on every SIMD (two wavefronts
+    each); best of 5 launches after one warm-up, timed with events on the launch stream."""
+    src = torch.empty(4 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    sink = torch.empty(ml.PROBE_READ_SINK, dtype=torch.int32, device=dev)
+    fsink = torch.empty(512 * 256, dtype=torch.float32, device=dev)
+
+    def best(fn, n=5):
+        times = []
+        fn()
+        for _ in range(n):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            times.append(a.elapsed_time(b) * 1e-3)
+        return min(times)
+
+    t_read = best(lambda: ml.probe_read(src, sink))
+    read_bytes = src.numel() + sink.numel() * 4
+    flops = [0]
+
+    def mf():
+        flops[0] = ml.probe_mfma(20000, 512, fsink)
+
+    t_mfma = best(mf)
+    del src
+    torch.cuda.empty_cache()
+    return {"hbm_read_GBs": read_bytes / t_read / 1e9, "mfma_bf16_TFLOPs": flops[0] / t_mfma / 1e12,
+            "how": "moe_lora_probe_read over 4 GiB; moe_lora_probe_mfma, 512 workgroups x 4 "
+                   "wavefronts x 20000 x 8 MFMAs 32x32x16 bf16; best of 5 launches"}
+
+
+def call_stats(ms: list) -> dict:
+    ms = sorted(ms)
+
+    def q(f):
+        i = f * (len(ms) - 1)
+        lo = int(math.floor(i))
+        hi = min(lo + 1, len(ms) - 1)
+        return ms[lo] + (ms[hi] - ms[lo]) * (i - lo)
+
+    return {"median": q(0.5), "p10": q(0.1), "p90": q(0.9), "n": len(ms)}
+
+
 def cpu_baseline(w, inp, n_tokens: int, min_seconds: float):
     """The oracle, as it stands, on a bounded sample of the same workload (host copies made
     before timing), run over the sample repeatedly until at least min_seconds have passed."""
@@ -117,7 +181,8 @@ def cpu_baseline(w, inp, n_tokens: int, min_seconds: float):
     return {"value": passes * len(toks) / dt, "unit": "tokens/s",
             "cores": min(oracle.num_threads(), len(toks)), "kind": "oracle",
             "sample": f"{passes} passes over {len(toks)} of {w.T} tokens of the {w.name} batch, fp64 C "
-                      f"oracle with OpenMP over tokens, inputs already in host memory; {dt:.1f} s wall"}
+                      f"oracle with OpenMP over tokens, inputs already in host memory; {dt:.1f} s wall",
+            "host": host_cpu()}
 
 
 # dense multi-LoRA: a serving batch of 256 tokens on a 4096 x 4096 projection, 64 adapters of
@@ -144,24 +209,37 @@ def run_sgmv(args, torch, ml, dev):
     for _ in range(args.warmup):
         ml.sgmv(xd, Ad, Bd, add, yd, workspace=ws)
     torch.cuda.synchronize()
+    # each call between two events on its stream: the GPU time of the call's three launches (the
+    # host's launch rate does not enter, unlike a wall-clock loop)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for a, b in evs:
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for a, b in evs:
+        a.record()
         ml.sgmv(xd, Ad, Bd, add, yd, workspace=ws)
+        b.record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    call_ms = [a.elapsed_time(b) for a, b in evs]
+    st = call_stats(call_ms)
     n_ad = len(np.unique(ad.numpy()))
     nbytes = n_ad * r * (K + N) * 2 + T * K * 2 + 2 * T * N * 2 + 4 * T
-    per_call = elapsed / args.steps
+    per_call = st["median"] * 1e-3
     ach = nbytes / per_call / 1e9
     out = {
         "metric": "tokens/s of the dense multi-LoRA (SGMV) add",
         "value": T * args.steps / elapsed, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": per_call * 1e3, "higher_is_better": True,
+        "warmup": args.warmup, "ms_per_step": elapsed * 1e3 / args.steps, "higher_is_better": True,
+        "call_ms": st,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "sgmv", "T": T, "in_features": K, "out_features": N,
                    "n_adapters": nA, "rank": r, "tokens_per_adapter_run": c["run"], "seed": args.seed},
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": ach / HBM_PEAK_GBS, "traffic": None, "kernel": "whole call (3 launches)"},
+                     "frac": ach / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "whole call (3 launches), median of per-call event times"},
     }
     if not args.no_cpu_baseline:
         import oracle
@@ -176,7 +254,8 @@ def run_sgmv(args, torch, ml, dev):
                 break
         out["cpu_baseline"] = {"value": passes * len(toks) / dt, "unit": "tokens/s",
                                "cores": min(oracle.num_threads(), len(toks)), "kind": "oracle",
-                               "sample": f"{passes} passes over {len(toks)} of {T} tokens, fp64 C oracle; {dt:.1f} s wall"}
+                               "sample": f"{passes} passes over {len(toks)} of {T} tokens, fp64 C oracle; {dt:.1f} s wall",
+                               "host": host_cpu()}
     print(json.dumps(out), flush=True)
 
 
@@ -196,6 +275,8 @@ def main():
                     help="E4M3 expert weights with per-row scales (decode-sized workloads)")
     ap.add_argument("--routed", action="store_true",
                     help="start from router weights: moe_lora_forward_routed (router GEMM in the step)")
+    ap.add_argument("--no-probes", action="store_true",
+                    help="skip the on-box HBM-read and MFMA-loop probes")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run a device-to-device copy of this size first (counter calibration)")
     args = ap.parse_args()
@@ -286,26 +367,36 @@ def main():
     if args.routed:
         # the routed entry records no stage events: gate_up and the router GEMM are timed in the
         # breakdown pass below, over the same kernels
+        call_events = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+        for ev in call_events:
+            ev.record()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(K):
+            call_events[i].record()
             step()
+        call_events[K].record()
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
+        call_ms = [call_events[i].elapsed_time(call_events[i + 1]) for i in range(K)]
     else:
         gu_events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
-        for evs in gu_events:  # create the HIP events outside the timed region
-            for ev in evs:
-                ev.record()
+        # one event at the start of every call and one after the last: per-call GPU times
+        call_events = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+        for ev in [e for evs in gu_events for e in evs] + call_events:
+            ev.record()  # create the HIP events outside the timed region
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(K):
             evs = [None] * (ml.N_STAGES + 1)
+            evs[0] = call_events[i]
             evs[GU], evs[GU + 1] = gu_events[i]
             step(evs)
+        call_events[K].record()
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
         gu_ms = statistics.fmean(a.elapsed_time(b) for a, b in gu_events)
+        call_ms = [call_events[i].elapsed_time(call_events[i + 1]) for i in range(K)]
 
     # stage breakdown (diagnostics): a few more calls with every boundary recorded
     NB = min(K, 5) if not args.routed else K
@@ -345,6 +436,11 @@ def main():
                                        + ("_routed" if args.routed else ""))
 
     layer_s = elapsed / K
+    cs = call_stats(call_ms)
+    onbox = None if args.no_probes else onbox_peaks(torch, ml, dev)
+    if onbox:
+        roof["frac_onbox"] = roof["achieved"] / (onbox["mfma_bf16_TFLOPs"] if prefill_like
+                                                 else onbox["hbm_read_GBs"])
     out = {
         "metric": "tokens/s of fused MoE-LoRA layer",
         "value": value,
@@ -364,12 +460,17 @@ def main():
                    "expert_weights": "e4m3 + per-row fp32 scale" if args.fp8 else "bf16",
                    "logits": "x W_router^T (routed entry)" if args.routed else "given"},
         "roofline": roof,
+        "call_ms": cs,
         "layer": {"bytes": work["layer_bytes"], "flops": work["layer_flops"],
                   "ms": layer_s * 1e3,
                   "hbm_frac": work["layer_bytes"] / layer_s / 1e9 / HBM_PEAK_GBS,
                   "mfma_frac": work["layer_flops"] / layer_s / 1e12 / BF16_PEAK_TFLOPS},
         "stages_ms": {k: round(v, 4) for k, v in stage_avg.items()},
     }
+    if onbox:
+        out["onbox_peaks"] = onbox
+        out["layer"]["hbm_frac_onbox"] = work["layer_bytes"] / layer_s / 1e9 / onbox["hbm_read_GBs"]
+        out["layer"]["mfma_frac_onbox"] = work["layer_flops"] / layer_s / 1e12 / onbox["mfma_bf16_TFLOPs"]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_tokens, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -23,7 +23,7 @@ EXPORTS = ("moe_lora_workspace_size", "moe_lora_forward", "moe_lora_forward_time
            "moe_lora_sorted_capacity", "moe_lora_route_align", "moe_lora_strerror",
            "moe_lora_debug_status", "moe_lora_sgmv_workspace_size", "moe_lora_sgmv",
            "moe_lora_router_logits", "moe_lora_forward_routed", "moe_lora_workspace_layout",
-           "moe_lora_forward_noalloc")
+           "moe_lora_forward_noalloc", "moe_lora_probe_read", "moe_lora_probe_mfma")
 N_STAGES = 7
 STAGES = ("route", "align", "shrink_gate_up", "gate_up", "shrink_down", "down", "combine")
 
@@ -71,6 +71,10 @@ def lib() -> ctypes.CDLL:
         L.moe_lora_forward_fp8.argtypes = [P, P, P, P, P, P, P, P, P, P, P, i32, D, P, P, ctypes.c_size_t, P,
                                            ctypes.POINTER(ctypes.c_void_p)]
         L.moe_lora_forward_fp8.restype = ctypes.c_int
+        L.moe_lora_probe_read.argtypes = [P, ctypes.c_size_t, P, P]
+        L.moe_lora_probe_read.restype = ctypes.c_int
+        L.moe_lora_probe_mfma.argtypes = [i32, i32, P, P]
+        L.moe_lora_probe_mfma.restype = ctypes.c_int
         L.moe_lora_forward_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, i32, D, P, P]
         L.moe_lora_forward_noalloc.restype = ctypes.c_int
         L.moe_lora_router_logits.argtypes = [P, P, i32, i32, i32, P, P]
@@ -248,7 +252,7 @@ def forward_noalloc(x, router_logits, W1, W2, A1, B1, A2, B2, adapter_ids, topk:
     _check(lib().moe_lora_forward_noalloc(_ptr(x), _ptr(router_logits), _ptr(W1), _ptr(W2), _ptr(A1),
                                           _ptr(B1), _ptr(A2), _ptr(B2), _ptr(adapter_ids), topk,
                                           ctypes.byref(d), _ptr(y), _stream(x.device)),
-           "moe_lora_forward_noalloc")
+           "moe_lora_forward_noalloc", "moe_lora_probe_read", "moe_lora_probe_mfma")
     return y
 
 
@@ -389,6 +393,22 @@ def route_align(router_logits, adapter_ids, topk: int, d: Dims, seg_pad: int = 1
     _check(rc, "moe_lora_route_align")
     out["workspace"] = workspace
     return out
+
+
+PROBE_READ_SINK = 2048 * 256  # uint32 words the read probe writes
+
+
+def probe_read(src: torch.Tensor, sink: torch.Tensor):
+    """Streaming read of src's bytes (moe_lora_probe_read) on the current stream."""
+    _check(lib().moe_lora_probe_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
+                                     _stream(src.device)), "moe_lora_probe_read")
+
+
+def probe_mfma(iters: int, n_workgroups: int, sink: torch.Tensor) -> int:
+    """Loop of bf16 MFMAs (moe_lora_probe_mfma) on the current stream; returns its flops."""
+    _check(lib().moe_lora_probe_mfma(iters, n_workgroups, _ptr(sink), _stream(sink.device)),
+           "moe_lora_probe_mfma")
+    return n_workgroups * 4 * iters * 8 * 32768
 
 
 def debug_status(workspace: torch.Tensor) -> int:

@@ -98,7 +98,8 @@ def uniform_u32(seed: int, tensor_id: int, count: int, device="cpu") -> torch.Te
     return _lsr(hash_range(seed, tensor_id, 0, count, device), 32)
 
 
-_CHUNK = 1 << 24
+_CHUNK = 1 << 24      # elements per generation step on the CPU
+_CHUNK_GPU = 1 << 27  # on a GPU: fewer, larger steps (the values do not depend on the chunking)
 
 
 def normal_(out: torch.Tensor, seed: int, tensor_id: int, sigma: float, mean: float = 0.0) -> torch.Tensor:
@@ -107,8 +108,9 @@ def normal_(out: torch.Tensor, seed: int, tensor_id: int, sigma: float, mean: fl
         raise ValueError("normal_ needs a contiguous tensor")
     flat = out.view(-1)
     n = flat.numel()
-    for start in range(0, n, _CHUNK):
-        cnt = min(_CHUNK, n - start)
+    chunk = _CHUNK_GPU if out.device.type == "cuda" else _CHUNK
+    for start in range(0, n, chunk):
+        cnt = min(chunk, n - start)
         v = _box_muller(hash_range(seed, tensor_id, start, cnt, out.device)) * sigma + mean
         if out.dtype == torch.bfloat16:
             flat[start:start + cnt] = v.to(torch.float32).to(torch.bfloat16)
