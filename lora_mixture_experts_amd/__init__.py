@@ -252,7 +252,7 @@ def forward_noalloc(x, router_logits, W1, W2, A1, B1, A2, B2, adapter_ids, topk:
     _check(lib().moe_lora_forward_noalloc(_ptr(x), _ptr(router_logits), _ptr(W1), _ptr(W2), _ptr(A1),
                                           _ptr(B1), _ptr(A2), _ptr(B2), _ptr(adapter_ids), topk,
                                           ctypes.byref(d), _ptr(y), _stream(x.device)),
-           "moe_lora_forward_noalloc", "moe_lora_probe_read", "moe_lora_probe_mfma")
+           "moe_lora_forward_noalloc")
     return y
 
 
