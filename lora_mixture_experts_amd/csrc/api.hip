@@ -502,6 +502,13 @@ int enqueue_forward(const ForwardPlan& pl, const MoeLoraLayout& L, const void* x
   g.act_out = act;
   g.d_out = dpair;
   g.n_blocks_max = pl.max_blocks;
+  // MOELORA_LORA_EXT=0 keeps every tiled LoRA expand in the epilogue (experiments)
+  static int lora_ext_env = -1;
+  if (lora_ext_env < 0) {
+    const char* env = getenv("MOELORA_LORA_EXT");
+    lora_ext_env = env ? atoi(env) : 1;
+  }
+  g.lora_ext = lora_ext_env != 0 ? 1 : 0;
 
   // gate_up: shrink z1 = x A1, then W1 GEMM + z1 B1 + SiLU-and-mul -> act
   sh.X = (const uint16_t*)x;

@@ -224,6 +224,60 @@ __device__ __forceinline__ void lora_expand_segs(const GemmArgs& a, f32x16 (&acc
   }
 }
 
+// 16 zero bytes: the B-side source of extension-step slices that hold no run.
+__device__ __align__(16) uint32_t g_zero16[4] = {0u, 0u, 0u, 0u};
+
+// Loads of the tiled GEMM: the main K steps read the token rows (X) and the expert's weight rows
+// (W) through buffer descriptors; the extension steps that follow (the LoRA expand as extra K,
+// see tiled_gemm_kernel) read z (bf16, one plane [cap][r]) for the rows of each run, zeros for
+// the other rows, and the runs' B rows through 64-bit addresses (B spans all adapters).
+template <class Pipe>
+struct LoraExtLoader {
+  static constexpr int NA = Pipe::NA, NB = Pipe::NB, BKS = Pipe::SUB * 16;
+  u32x4 xr, wr, zr;
+  uint32_t xo[NA], wo[NB];  // main steps: offsets at step 0
+  int nks;                  // main steps
+  int jrow[NA];             // run holding the A row of load block i (-1: none)
+  uint32_t zo[NA];          // byte offset of that row's chunk in the z plane
+  int slot_a[NA], slot_b[NB];  // run slot (within a step) of the chunk each lane loads
+  uint32_t bo[NB];          // byte offset of the B chunk inside one (adapter, expert) slice
+  const char* bexp;         // B slice of (adapter 0, this expert)
+  size_t a_stride;          // bytes between adapters' slices of one expert
+  int run_ad;               // lane j: adapter of run j
+  int nr, rps;              // runs; runs per extension step
+  uint32_t xe[NA];          // prepared extension step: A offsets
+  const void* be[NB];       // and B addresses
+
+  __device__ __forceinline__ int main_steps() const { return nks; }
+  __device__ __forceinline__ void load_main(int d, int ks, uint32_t lds_addr) {
+    const uint32_t soff = (uint32_t)ks * BKS * 2;
+    if (d < NA) lds_dma16(xr, xo[d], soff, lds_addr);
+    else lds_dma16(wr, wo[d - NA], soff, lds_addr);
+  }
+  __device__ __forceinline__ void prep(int ks) {
+    if (ks < nks) return;
+    const int x = ks - nks;
+#pragma unroll
+    for (int i = 0; i < NA; ++i) xe[i] = (x * rps + slot_a[i] == jrow[i]) ? zo[i] : kOutOfRange;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int j = x * rps + slot_b[i];
+      const int adj = __shfl(run_ad, j < nr ? j : 0);
+      be[i] = j < nr ? (const void*)(bexp + (size_t)adj * a_stride + bo[i]) : (const void*)g_zero16;
+    }
+  }
+  __device__ __forceinline__ void load(int d, int ks, uint32_t lds_addr) {
+    if (ks < nks) {
+      const uint32_t soff = (uint32_t)ks * BKS * 2;
+      if (d < NA) lds_dma16(xr, xo[d], soff, lds_addr);
+      else lds_dma16(wr, wo[d - NA], soff, lds_addr);
+    } else {
+      if (d < NA) lds_dma16(zr, xe[d], 0u, lds_addr);
+      else lds_dma16_global(be[d - NA], lds_addr);
+    }
+  }
+};
+
 template <bool GATEUP, int BM, int BN, int WM, int WN, int BK, int NST, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void tiled_gemm_kernel(GemmArgs a, int n_tiles_n,
                                                             int /*grid_total*/) {
@@ -301,6 +355,96 @@ __global__ __launch_bounds__(64 * NW, 1) void tiled_gemm_kernel(GemmArgs a, int 
   const u32x4 xr = buffer_desc(a.X, a.x_bytes);
   const u32x4 wr = buffer_desc(a.W + (size_t)e * w_rows * K, (uint32_t)(w_rows * K * 2));
 
+  LoraExtLoader<Pipe> ld;
+  ld.xr = xr;
+  ld.wr = wr;
+  ld.zr = buffer_desc(a.zhl, (uint32_t)((size_t)a.cap * a.r * 2));
+  ld.nks = kspan / BK;
+#pragma unroll
+  for (int i = 0; i < NA; ++i) ld.xo[i] = xo[i];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) ld.wo[i] = wo[i];
+  ld.nr = 0;
+  const int r = a.r;
+  ld.rps = BK / r;
+  const int cpr_r = r / 8;  // 16-byte chunks per run in an extension step
+  bool use_ext = false;
+  int nsteps = kspan / BK;
+
+  // The LoRA expand as extra K steps when the tile's runs are few (the adapter segments clipped
+  // to its rows, adapter >= 0): step x multiplies z of the rows of runs x*rps .. x*rps+rps-1,
+  // each run in its own r-wide slice of the step's BK, zeros elsewhere, by the same slices of
+  // the runs' B rows, so the expand streams through the main loop's pipeline. Every wavefront
+  // finds the runs itself (lane j holds run j) while the first K steps' loads are in flight.
+  // More runs than fit one wavefront, or more extension steps than a quarter of the main loop,
+  // take the epilogue instead (lora_expand_segs).
+  auto build_runs = [&]() {
+    const int first = a.block_seg[blk];
+    if (ks != 0 || first < 0 || !a.lora_ext) return;
+    const int sj = first + lane;
+    bool in = false, run = false;
+    int lo = 0, hi = 0, ad = -1;
+    if (sj < *a.n_seg) {
+      const u32x4 sg = *reinterpret_cast<const u32x4*>(a.seg_table + 4 * (size_t)sj);
+      const int st = (int)sg[2], cnt = (int)sg[3];
+      in = st < row0 + BM;
+      lo = max(st - row0, 0);
+      hi = min(st + cnt - row0, BM);
+      ad = sanitize_adapter((int)sg[1], a.nA);
+      run = in && ad >= 0 && hi > lo;
+    }
+    const uint64_t m = __ballot(run);
+    const bool more = (__ballot(in) >> 63) != 0;  // segments past this chunk may overlap the tile
+    const int nr = __popcll(m);
+    const int n_ext = (nr + ld.rps - 1) / ld.rps;
+    if (more || n_ext == 0 || 4 * n_ext > ld.nks) return;
+    // lane j <- run j (lanes without a run send theirs to lane 63, unused when nr < 64)
+    const int tgt = run ? __popcll(m & lanemask_lt()) : 63;
+    const int run_ad = __builtin_amdgcn_ds_permute(tgt * 4, ad);
+    const int run_lo = __builtin_amdgcn_ds_permute(tgt * 4, lo);
+    const int run_hi = __builtin_amdgcn_ds_permute(tgt * 4, hi);
+    use_ext = true;
+    ld.nr = nr;
+    ld.run_ad = run_ad;
+    nsteps = ld.nks + n_ext;
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int row = Pipe::load_row(i, wave, lane);
+      const int chunk = Pipe::load_chunk(row, lane);
+      // runs starting at or before the row (runs are disjoint and in row order); every lane
+      // takes part in every shuffle
+      int b = 0;
+#pragma unroll
+      for (int step = 64; step > 0; step >>= 1) {
+        const int cand = b + step;
+        const int lo_c = __shfl(run_lo, min(cand, nr) - 1);
+        if (cand <= nr && lo_c <= row) b = cand;
+      }
+      const int j = b - 1;
+      const int hi_j = __shfl(run_hi, j >= 0 ? j : 0);
+      ld.jrow[i] = (j >= 0 && row < hi_j) ? j : -1;
+      ld.slot_a[i] = chunk / cpr_r;
+      ld.zo[i] = (uint32_t)(((size_t)(row0 + row) * r + (chunk % cpr_r) * 8) * 2);
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int row = Pipe::load_row(i, wave, lane);
+      const int chunk = Pipe::load_chunk(row, lane);
+      size_t wrow;
+      if (GATEUP) {
+        const int g = row / WN, rr = row % WN;
+        const size_t col = (size_t)ntile * (BN / 2) + g * (WN / 2) + (rr % (WN / 2));
+        wrow = rr < WN / 2 ? col : N + col;
+      } else {
+        wrow = (size_t)ntile * BN + row;
+      }
+      ld.slot_b[i] = chunk / cpr_r;
+      ld.bo[i] = (uint32_t)((wrow * r + (chunk % cpr_r) * 8) * 2);
+    }
+    ld.bexp = reinterpret_cast<const char*>(a.Bw + (size_t)e * w_rows * r);
+    ld.a_stride = (size_t)a.E * w_rows * r * 2;
+  };
+
   f32x16 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -309,12 +453,13 @@ __global__ __launch_bounds__(64 * NW, 1) void tiled_gemm_kernel(GemmArgs a, int 
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  Pipe::run(acc, xr, xo, wr, wo, lds, kspan, wave, lane);
+  Pipe::run_steps(acc, ld, lds, nsteps, wave, lane, build_runs);
 
   __syncthreads();  // every wavefront is done with the main loop's LDS stages
 
-  // the LoRA term goes into K split 0 only (the combine adds the splits)
-  if (ks == 0)
+  // the LoRA term goes into K split 0 only (the combine adds the splits); tiles with many runs
+  // add it here, after the main loop
+  if (ks == 0 && !use_ext)
     lora_expand_segs<GATEUP, BM, BN, WM, WN, FM, FN, Pipe::LDS_BYTES, NW>(a, acc, lds, blk, row0,
                                                                            wm, wn, ntile, e, wave,
                                                                            lane);
@@ -361,6 +506,12 @@ hipError_t launch_tiled(const TiledConfig& c, bool gateup, const GemmArgs& a, hi
   MOELORA_TILED(128, 128, 32, 64, 64, 2, 8)
   MOELORA_TILED(256, 256, 64, 128, 64, 2, 8)
   MOELORA_TILED(64, 256, 32, 64, 64, 2, 8)
+  MOELORA_TILED(192, 256, 96, 64, 64, 2, 8)
+  MOELORA_TILED(128, 256, 64, 64, 64, 2, 8)
+  // down only (one 32-column fragment per wave: no gate/up halves)
+  if (!gateup && c.bm == 192 && c.bn == 128 && c.wm == 96 && c.wn == 32 && c.bk == 64 &&
+      c.nst == 2 && c.nw == 8)
+    return launch_tiled_t<false, 192, 128, 96, 32, 64, 2, 8>(a, n_tiles_n, total, stream);
 #undef MOELORA_TILED
   return hipErrorInvalidValue;
 }

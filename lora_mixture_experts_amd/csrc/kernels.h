@@ -108,6 +108,8 @@ struct GemmArgs {
   int64_t d_split_stride;
   int n_blocks_max;   // row blocks the grid is sized for (>= *n_blocks)
   int n_col_tiles;    // skinny: column tiles of one row block (N / columns per workgroup)
+  int lora_ext;       // tiled: 1 lets tiles with few adapter runs add the LoRA expand as extra K
+                      // steps of the main loop (0: always in the epilogue)
 };
 
 // Dense multi-LoRA expand: y[t] += z[t] B_a^T over the sorted layout of T tokens (k = 1, E = 1).

@@ -39,6 +39,14 @@ __device__ __forceinline__ void lds_dma16(u32x4 rsrc, uint32_t voff, uint32_t so
                : "memory", "m0");
 }
 
+// As lds_dma16 from a 64-bit global address per lane (any buffer size; no zero fill).
+__device__ __forceinline__ void lds_dma16_global(const void* addr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(addr), "s"(lds_addr)
+               : "memory", "m0");
+}
+
 // Buffer descriptor of [base, base + bytes): loads at offsets >= bytes return zeros.
 __device__ __forceinline__ u32x4 buffer_desc(const void* base, uint32_t bytes) {
   const uint64_t b = (uint64_t)base;
@@ -88,20 +96,54 @@ struct TilePipe {
     return swz(row, lane % CPR);
   }
 
-  // xo[NA], wo[NB]: byte offsets (in xr, wr) of the chunk each lane loads at K step 0.
+  // The loads of a K step: PER 1 KB blocks per wavefront, block d (< NA: the A tile, else the B
+  // tile) going to LDS byte address lds_addr. A loader provides prep(ks) (called once before the
+  // loads of step ks are issued), load(d, ks, lds_addr), and main_steps(): steps below it may
+  // also be loaded with load_main(d, ks, lds_addr), which has no step-dependent branch.
+  //
+  // Loader of plain operand tiles: xo[NA], wo[NB] are the byte offsets (in xr, wr) of the chunk
+  // each lane loads at K step 0; step ks adds ks * BK * 2 bytes.
+  struct BufferLoader {
+    u32x4 xr, wr;
+    const uint32_t* xo;
+    const uint32_t* wo;
+    __device__ __forceinline__ int main_steps() const { return 1 << 30; }
+    __device__ __forceinline__ void prep(int) {}
+    __device__ __forceinline__ void load_main(int d, int ks, uint32_t lds_addr) {
+      const uint32_t soff = (uint32_t)ks * BK * 2;
+      if (d < NA) lds_dma16(xr, xo[d], soff, lds_addr);
+      else lds_dma16(wr, wo[d - NA], soff, lds_addr);
+    }
+    __device__ __forceinline__ void load(int d, int ks, uint32_t lds_addr) {
+      load_main(d, ks, lds_addr);
+    }
+  };
+
   __device__ static __forceinline__ void run(f32x16 (&acc)[FM][FN], u32x4 xr, const uint32_t* xo,
                                              u32x4 wr, const uint32_t* wo, uint16_t* lds, int K,
                                              int wave, int lane) {
+    BufferLoader ld{xr, wr, xo, wo};
+    int nks = K / BK;
+    run_steps(acc, ld, lds, nks, wave, lane, [] {});
+  }
+
+  // nks K steps of loads from `ld`; `mid` runs once the first NST steps' loads are in flight,
+  // before the first wait (work that can overlap their latency), and may raise nks (steps past
+  // the first NST only).
+  template <class Loader, class Mid>
+  __device__ static __forceinline__ void run_steps(f32x16 (&acc)[FM][FN], Loader& ld,
+                                                   uint16_t* lds, int& nks, int wave, int lane,
+                                                   Mid mid) {
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
     const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
-    auto issue = [&](int ks, int stage) {
-      const uint32_t soff = (uint32_t)ks * BK * 2;
+    auto block_addr = [&](int d, int stage) {
       const uint32_t sa = lds0 + stage * STAGE_BYTES + wave * 1024;
-      const uint32_t sb = sa + BM * BK * 2;
+      return d < NA ? sa + d * NWAVES * 1024 : sa + BM * BK * 2 + (d - NA) * NWAVES * 1024;
+    };
+    auto issue = [&](int ks, int stage) {
+      ld.prep(ks);
 #pragma unroll
-      for (int i = 0; i < NA; ++i) lds_dma16(xr, xo[i], soff, sa + i * NWAVES * 1024);
-#pragma unroll
-      for (int i = 0; i < NB; ++i) lds_dma16(wr, wo[i], soff, sb + i * NWAVES * 1024);
+      for (int d = 0; d < PER; ++d) ld.load(d, ks, block_addr(d, stage));
     };
     const int fr = lane & 31, fg = lane >> 5;
     auto read_frags = [&](int stage, int j, u32x4* af, u32x4* bf) {
@@ -138,29 +180,26 @@ struct TilePipe {
 
     // The last sub-step's MFMAs with the refill loads of step ks_load spread between them (one
     // load after MFMA floor(d * NM / PER)), so that issuing them does not stall the MFMA pipe.
-    auto mfmas_with_loads = [&](const u32x4* af, const u32x4* bf, int ks_load, int st) {
+    auto mfmas_with_loads = [&](const u32x4* af, const u32x4* bf, int ks_load, int st,
+                                auto&& load_fn) {
       constexpr int NM = FM * FN;
-      const uint32_t soff = (uint32_t)ks_load * BK * 2;
-      const uint32_t sa = lds0 + st * STAGE_BYTES + wave * 1024;
-      const uint32_t sb = sa + BM * BK * 2;
 #pragma unroll
       for (int t = 0; t < NM; ++t) {
         acc[t / FN][t % FN] = mfma32(af[t / FN], bf[t % FN], acc[t / FN][t % FN]);
 #pragma unroll
         for (int d = 0; d < PER; ++d) {
           if ((d * NM) / PER != t) continue;
-          if (d < NA) lds_dma16(xr, xo[d], soff, sa + d * NWAVES * 1024);
-          else lds_dma16(wr, wo[d - NA], soff, sb + (d - NA) * NWAVES * 1024);
+          load_fn(d, ks_load, block_addr(d, st));
         }
         __builtin_amdgcn_sched_barrier(0);
       }
     };
 
-    const int nks = K / BK;
     // prologue: steps 0 .. NST-1 in flight, wait for step 0
 #pragma unroll
     for (int s = 0; s < NST; ++s)
       if (s < nks) issue(s, s);
+    mid();
     if (nks >= NST) wait_vmcnt<(NST - 1) * PER>();
     else wait_vmcnt<0>();
     __syncthreads();
@@ -170,9 +209,11 @@ struct TilePipe {
     __builtin_amdgcn_sched_barrier(0);
     // All steps but the last end with the barrier and the refill. No branch encloses an MFMA
     // (the compiler would keep a second copy of the accumulators): near the end the refill
-    // re-loads the last step into the stage just consumed, which no later step reads.
+    // re-loads the last step into the stage just consumed, which no later step reads. While
+    // the refills are main K steps (ld.main_steps()) the loop takes the loader's branch-free
+    // main-step loads.
     int stage = 0;
-    for (int ks = 0; ks + 1 < nks; ++ks) {
+    auto step = [&](int ks, auto&& load_fn, auto&& prep_fn) {
       const int next = stage + 1 == NST ? 0 : stage + 1;
 #pragma unroll
       for (int j = 0; j < SUB; ++j) {
@@ -193,20 +234,19 @@ struct TilePipe {
         else wait_vmcnt<0>();
         __syncthreads();
         const int ks_load = ks + NST < nks ? ks + NST : nks - 1;
-        if (SPREAD) {
-          read_frags(next, 0, an, bn);
-          __builtin_amdgcn_sched_barrier(0);
-          mfmas_with_loads(ac, bc, ks_load, stage);
-        } else {
-          issue(ks_load, stage);
-          read_frags(next, 0, an, bn);
-          __builtin_amdgcn_sched_barrier(0);
-          mfmas_interleaved(ac, bc, true);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        prep_fn(ks_load);
+        read_frags(next, 0, an, bn);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas_with_loads(ac, bc, ks_load, stage, load_fn);
       }
       stage = next;
-    }
+    };
+    const int main_end = ld.main_steps() - NST;  // refills of steps < main_end + NST are main
+    int ks = 0;
+    for (; ks + 1 < nks && ks < main_end; ++ks)
+      step(ks, [&](int d, int k, uint32_t a) { ld.load_main(d, k, a); }, [](int) {});
+    for (; ks + 1 < nks; ++ks)
+      step(ks, [&](int d, int k, uint32_t a) { ld.load(d, k, a); }, [&](int k) { ld.prep(k); });
     // last step: no barrier, no refill
 #pragma unroll
     for (int j = 0; j < SUB; ++j) {
