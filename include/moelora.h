@@ -55,7 +55,7 @@ extern "C" {
 #define MOELORA_EWORKSPACE (-4)  /* workspace too small or misaligned (256-byte alignment) */
 #define MOELORA_EHIP (-5)        /* a HIP launch or runtime call failed */
 #define MOELORA_EDEVICE (-6)     /* the current device is not gfx950 */
-#define MOELORA_EUNSUPPORTED (-7) /* FP8 weights with more than 24 token-expert pairs per expert */
+#define MOELORA_EUNSUPPORTED (-7) /* reserved: a combination of arguments this build does not run */
 #define MOELORA_ESCRATCH (-8)     /* moe_lora_forward_noalloc: the call needs more than its scratch */
 
 /* Device-side flags reported by moe_lora_debug_status. */
@@ -169,10 +169,10 @@ int moe_lora_forward_routed(const void *x, const void *W_router, const void *W1,
  * bits with bias 7, 3 mantissa bits; no infinities) and W1_scale [E][2I], W2_scale [E][h] one
  * float32 per weight row: weight = decode(code) * scale. Everything else (x, the LoRA weights,
  * y, the workspace and its size) is as in moe_lora_forward, device pointers, caller-owned.
- * The codes are 16-byte aligned, the scales 4-byte aligned. The FP8 path covers the
- * weight-streaming regime (at most 24 token-expert pairs per expert on average, T*topk <=
- * 24*n_experts): larger batches return MOELORA_EUNSUPPORTED before any device work.
- * stage_events, when not NULL, is as in moe_lora_forward_timed. */
+ * The codes are 16-byte aligned, the scales 4-byte aligned. Both GEMM regimes take E4M3
+ * weights: the weight-streaming one (few token-expert pairs per expert) and the LDS-tiled one
+ * (codes staged in LDS as bytes, converted to bf16 after the LDS read); the LoRA weights stay
+ * bf16. stage_events, when not NULL, is as in moe_lora_forward_timed. */
 int moe_lora_forward_fp8(const void *x, const float *router_logits, const void *W1q,
                          const float *W1_scale, const void *W2q, const float *W2_scale,
                          const void *A1, const void *B1, const void *A2, const void *B2,

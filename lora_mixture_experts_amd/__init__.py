@@ -325,7 +325,7 @@ def forward_fp8(x, router_logits, W1q, W1_scale, W2q, W2_scale, A1, B1, A2, B2, 
                 topk: int, y=None, workspace=None, stage_events=None) -> torch.Tensor:
     """forward with E4M3 expert weights (moe_lora_forward_fp8): W1q [E][2I][h] and W2q [E][h][I]
     as uint8 codes, W1_scale [E][2I] and W2_scale [E][h] float32 per-row scales; the rest as
-    in forward. Raises MoeLoraError(EUNSUPPORTED) above 24 token-expert pairs per expert."""
+    in forward."""
     T, h = x.shape
     E, twoI, _ = W1q.shape
     nA, _, r, _ = A1.shape

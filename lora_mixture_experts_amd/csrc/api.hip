@@ -389,7 +389,7 @@ const char* moe_lora_strerror(int code) {
     case MOELORA_EWORKSPACE: return "workspace too small or not 256-byte aligned";
     case MOELORA_EHIP: return "HIP launch or runtime error";
     case MOELORA_EDEVICE: return "current device is not gfx950";
-    case MOELORA_EUNSUPPORTED: return "FP8 weights take at most 24 token-expert pairs per expert";
+    case MOELORA_EUNSUPPORTED: return "this combination of arguments is not supported";
     case MOELORA_ESCRATCH:
       return "the call needs more workspace than the static scratch of moe_lora_forward_noalloc "
              "(128 MiB)";
@@ -545,7 +545,7 @@ int enqueue_forward(const ForwardPlan& pl, const MoeLoraLayout& L, const void* x
   g.d_split_stride = L.cap * (int64_t)h;
   g.n_col_tiles = g.N / (pl.sk.gu.split ? 32 : 64 * pl.sk.gu.rt);
   const hipError_t gu_err = path.tiled
-                                ? launch_tiled(path.tc, true, g, stream)
+                                ? launch_tiled(path.tc, true, g, stream, fp8)
                                 : launch_skinny(pl.sk.gu, true, g, pl.max_blocks, stream, fp8);
   if (gu_err != hipSuccess) return MOELORA_EHIP;
   if (!mark(ev, 4, stream)) return MOELORA_EHIP;
@@ -577,7 +577,7 @@ int enqueue_forward(const ForwardPlan& pl, const MoeLoraLayout& L, const void* x
   g.ksplit = pl.sk.ksplit;
   g.n_col_tiles = g.N / (64 * pl.sk.dn.rt);
   const hipError_t dn_err = path.tiled
-                                ? launch_tiled(path.tc_dn, false, g, stream)
+                                ? launch_tiled(path.tc_dn, false, g, stream, fp8)
                                 : launch_skinny(pl.sk.dn, false, g, pl.max_blocks, stream, fp8);
   if (dn_err != hipSuccess) return MOELORA_EHIP;
   if (!mark(ev, 6, stream)) return MOELORA_EHIP;
@@ -602,7 +602,6 @@ int check_forward(const void* x, const float* router_logits, const void* W_route
                   bool in_scratch = false) {
   int rc = plan_and_layout(d, topk, fp8, pl, L);
   if (rc != MOELORA_OK) return rc;
-  if (fp8 && pl->path.tiled) return MOELORA_EUNSUPPORTED;
   if (in_scratch && L->total > kScratchBytes) return MOELORA_ESCRATCH;
   if (d->T == 0) return MOELORA_OK;  // empty batch: nothing to do, pointers may be NULL
   const void* logits_or_router = W_router ? W_router : (const void*)router_logits;

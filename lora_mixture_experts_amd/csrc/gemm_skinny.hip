@@ -28,22 +28,6 @@
 
 namespace moelora {
 
-// Eight E4M3 codes (half `hi` of the 16 in v, bytes in K order) as one bf16 MFMA operand. The
-// hardware conversion decodes the OCP E4M3 format into float32; the bf16 is its upper half
-// (exact, as E4M3 has 3 mantissa bits and a narrower exponent range).
-__device__ __forceinline__ u32x4 e4m3x8_to_bf16(u32x4 v, int hi) {
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  const uint32_t d0 = hi ? v.z : v.x, d1 = hi ? v.w : v.y;
-  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)d0, false);
-  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)d0, true);
-  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)d1, false);
-  const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)d1, true);
-  auto pack = [](f32x2 f) {
-    return __builtin_amdgcn_perm(__float_as_uint(f.y), __float_as_uint(f.x), 0x07060302u);
-  };
-  return u32x4{pack(a), pack(b), pack(c), pack(d)};
-}
-
 // NT: 16-row token tiles per row block (BM = 16*NT). P: 16-byte loads per lane per weight row
 // and K step (K step = 32*P). RT: 16-row output tiles per wave (per projection for gate_up).
 // Down may split K over gridDim.z: split z writes its partial sums to its own D buffer and only

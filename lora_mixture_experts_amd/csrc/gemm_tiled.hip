@@ -250,9 +250,8 @@ struct LoraExtLoader {
 
   __device__ __forceinline__ int main_steps() const { return nks; }
   __device__ __forceinline__ void load_main(int d, int ks, uint32_t lds_addr) {
-    const uint32_t soff = (uint32_t)ks * BKS * 2;
-    if (d < NA) lds_dma16(xr, xo[d], soff, lds_addr);
-    else lds_dma16(wr, wo[d - NA], soff, lds_addr);
+    if (d < NA) lds_dma16(xr, xo[d], (uint32_t)ks * BKS * 2, lds_addr);
+    else lds_dma16(wr, wo[d - NA], (uint32_t)ks * Pipe::BROW, lds_addr);
   }
   __device__ __forceinline__ void prep(int ks) {
     if (ks < nks) return;
@@ -268,9 +267,7 @@ struct LoraExtLoader {
   }
   __device__ __forceinline__ void load(int d, int ks, uint32_t lds_addr) {
     if (ks < nks) {
-      const uint32_t soff = (uint32_t)ks * BKS * 2;
-      if (d < NA) lds_dma16(xr, xo[d], soff, lds_addr);
-      else lds_dma16(wr, wo[d - NA], soff, lds_addr);
+      load_main(d, ks, lds_addr);
     } else {
       if (d < NA) lds_dma16(zr, xe[d], 0u, lds_addr);
       else lds_dma16_global(be[d - NA], lds_addr);
@@ -278,10 +275,14 @@ struct LoraExtLoader {
   }
 };
 
-template <bool GATEUP, int BM, int BN, int WM, int WN, int BK, int NST, int NW>
+// FP8: the weights are E4M3 codes (a.W8) with one float32 scale per weight row (a.wscale):
+// staged in LDS as bytes, converted to bf16 fragments after the LDS read, and each accumulator
+// column multiplied by its row's scale after the main loop, before the LoRA term (bf16 weights,
+// unscaled, always in the epilogue) is added.
+template <bool GATEUP, int BM, int BN, int WM, int WN, int BK, int NST, int NW, bool FP8 = false>
 __global__ __launch_bounds__(64 * NW, 1) void tiled_gemm_kernel(GemmArgs a, int n_tiles_n,
                                                             int /*grid_total*/) {
-  using Pipe = TilePipe<BM, BN, WM, WN, BK, NST, true, NW>;
+  using Pipe = TilePipe<BM, BN, WM, WN, BK, NST, true, NW, FP8>;
   constexpr int FM = Pipe::FM, FN = Pipe::FN, NA = Pipe::NA, NB = Pipe::NB;
   static_assert(!GATEUP || FN % 2 == 0, "gate_up needs gate and up halves per wave");
 
@@ -338,22 +339,27 @@ __global__ __launch_bounds__(64 * NW, 1) void tiled_gemm_kernel(GemmArgs a, int 
                   : (uint32_t)((GATEUP ? (size_t)(p / a.k) : (size_t)srow) * K * 2) + kbyte0 +
                         16u * chunk;
   }
+  // weight row of tile row n (gate_up: the wave's column range is [gate .. | up ..] of the same
+  // act columns)
+  auto wrow_of = [&](int n) -> size_t {
+    if (GATEUP) {
+      const int g = n / WN, rr = n % WN;
+      const size_t col = (size_t)ntile * (BN / 2) + g * (WN / 2) + (rr % (WN / 2));
+      return rr < WN / 2 ? col : N + col;
+    }
+    return (size_t)ntile * BN + n;
+  };
+  constexpr int WB = FP8 ? 1 : 2;  // bytes per weight
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
-    const int row = Pipe::load_row(i, wave, lane);
-    const int chunk = Pipe::load_chunk(row, lane);
-    size_t wrow;
-    if (GATEUP) {
-      const int g = row / WN, rr = row % WN;
-      const size_t col = (size_t)ntile * (BN / 2) + g * (WN / 2) + (rr % (WN / 2));
-      wrow = rr < WN / 2 ? col : N + col;
-    } else {
-      wrow = (size_t)ntile * BN + row;
-    }
-    wo[i] = (uint32_t)(wrow * K * 2) + kbyte0 + 16u * chunk;
+    const int row = Pipe::load_row_b(i, wave, lane);
+    const int chunk = Pipe::load_chunk_b(row, lane);
+    wo[i] = (uint32_t)(wrow_of(row) * K * WB) + (uint32_t)ks * kspan * WB + 16u * chunk;
   }
   const u32x4 xr = buffer_desc(a.X, a.x_bytes);
-  const u32x4 wr = buffer_desc(a.W + (size_t)e * w_rows * K, (uint32_t)(w_rows * K * 2));
+  const u32x4 wr =
+      FP8 ? buffer_desc(a.W8 + (size_t)e * w_rows * K, (uint32_t)(w_rows * K))
+          : buffer_desc(a.W + (size_t)e * w_rows * K, (uint32_t)(w_rows * K * 2));
 
   LoraExtLoader<Pipe> ld;
   ld.xr = xr;
@@ -380,7 +386,7 @@ __global__ __launch_bounds__(64 * NW, 1) void tiled_gemm_kernel(GemmArgs a, int 
   // take the epilogue instead (lora_expand_segs).
   auto build_runs = [&]() {
     const int first = a.block_seg[blk];
-    if (ks != 0 || first < 0 || !a.lora_ext) return;
+    if (FP8 || ks != 0 || first < 0 || !a.lora_ext) return;
     const int sj = first + lane;
     bool in = false, run = false;
     int lo = 0, hi = 0, ad = -1;
@@ -428,16 +434,9 @@ __global__ __launch_bounds__(64 * NW, 1) void tiled_gemm_kernel(GemmArgs a, int 
     }
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      const int row = Pipe::load_row(i, wave, lane);
-      const int chunk = Pipe::load_chunk(row, lane);
-      size_t wrow;
-      if (GATEUP) {
-        const int g = row / WN, rr = row % WN;
-        const size_t col = (size_t)ntile * (BN / 2) + g * (WN / 2) + (rr % (WN / 2));
-        wrow = rr < WN / 2 ? col : N + col;
-      } else {
-        wrow = (size_t)ntile * BN + row;
-      }
+      const int row = Pipe::load_row_b(i, wave, lane);
+      const int chunk = Pipe::load_chunk_b(row, lane);
+      const size_t wrow = wrow_of(row);
       ld.slot_b[i] = chunk / cpr_r;
       ld.bo[i] = (uint32_t)((wrow * r + (chunk % cpr_r) * 8) * 2);
     }
@@ -457,6 +456,18 @@ __global__ __launch_bounds__(64 * NW, 1) void tiled_gemm_kernel(GemmArgs a, int 
 
   __syncthreads();  // every wavefront is done with the main loop's LDS stages
 
+  if (FP8) {  // per-row scales of the E4M3 weights (lane: column fr of each 32-column fragment)
+    const float* sc = a.wscale + (size_t)e * w_rows;
+#pragma unroll
+    for (int jn = 0; jn < FN; ++jn) {
+      const float s = sc[wrow_of(wn * WN + jn * 32 + (lane & 31))];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][jn][v] *= s;
+    }
+  }
+
   // the LoRA term goes into K split 0 only (the combine adds the splits); tiles with many runs
   // add it here, after the main loop
   if (ks == 0 && !use_ext)
@@ -466,11 +477,11 @@ __global__ __launch_bounds__(64 * NW, 1) void tiled_gemm_kernel(GemmArgs a, int 
   tiled_store<GATEUP, BN, WM, WN, FM, FN>(a, acc, row0, wm, wn, ntile, ks, lane);
 }
 
-template <bool GATEUP, int BM, int BN, int WM, int WN, int BK, int NST, int NW>
+template <bool GATEUP, int BM, int BN, int WM, int WN, int BK, int NST, int NW, bool FP8 = false>
 hipError_t launch_tiled_t(const GemmArgs& a, int n_tiles_n, int total, hipStream_t stream) {
-  constexpr int lds_bytes = TilePipe<BM, BN, WM, WN, BK, NST, true, NW>::LDS_BYTES;
+  constexpr int lds_bytes = TilePipe<BM, BN, WM, WN, BK, NST, true, NW, FP8>::LDS_BYTES;
   static_assert(lds_bytes <= kLdsBytes, "LDS stages must fit");
-  auto kern = tiled_gemm_kernel<GATEUP, BM, BN, WM, WN, BK, NST, NW>;
+  auto kern = tiled_gemm_kernel<GATEUP, BM, BN, WM, WN, BK, NST, NW, FP8>;
   static bool attr_set[64] = {};
   int dev = 0;
   hipError_t err = hipGetDevice(&dev);
@@ -485,7 +496,8 @@ hipError_t launch_tiled_t(const GemmArgs& a, int n_tiles_n, int total, hipStream
   return hipGetLastError();
 }
 
-hipError_t launch_tiled(const TiledConfig& c, bool gateup, const GemmArgs& a, hipStream_t stream) {
+hipError_t launch_tiled(const TiledConfig& c, bool gateup, const GemmArgs& a, hipStream_t stream,
+                        bool fp8) {
   const int cols = gateup ? 2 * a.N : a.N;
   if (cols % c.bn != 0) return hipErrorInvalidValue;
   const int splits = gateup ? 1 : a.ksplit;
@@ -496,6 +508,20 @@ hipError_t launch_tiled(const TiledConfig& c, bool gateup, const GemmArgs& a, hi
   int total = a.n_blocks_max * n_tiles_n * splits;
   total = (total + 7) / 8 * 8;
   if (total <= 0) return hipSuccess;
+  // E4M3 weights: the tiles the path picks by default
+#define MOELORA_TILED8(BM_, BN_, WM_, WN_, GU_)                                                  \
+  if (fp8 && gateup == GU_ && c.bm == BM_ && c.bn == BN_ && c.wm == WM_ && c.wn == WN_ &&        \
+      c.bk == 64 && c.nst == 2 && c.nw == (BM_ * BN_ / (WM_ * WN_)))                            \
+    return launch_tiled_t<GU_, BM_, BN_, WM_, WN_, 64, 2, BM_ * BN_ / (WM_ * WN_), true>(         \
+        a, n_tiles_n, total, stream);
+  MOELORA_TILED8(64, 256, 32, 64, true)
+  MOELORA_TILED8(64, 128, 32, 64, false)
+  MOELORA_TILED8(128, 128, 32, 64, true)
+  MOELORA_TILED8(128, 128, 32, 64, false)
+  MOELORA_TILED8(256, 256, 64, 128, true)
+  MOELORA_TILED8(256, 256, 64, 128, false)
+#undef MOELORA_TILED8
+  if (fp8) return hipErrorInvalidValue;
 #define MOELORA_TILED(BM_, BN_, WM_, WN_, BK_, NST_, NW_)                                   \
   if (c.bm == BM_ && c.bn == BN_ && c.wm == WM_ && c.wn == WN_ && c.bk == BK_ && c.nst == NST_ && \
       c.nw == NW_)                                                                              \

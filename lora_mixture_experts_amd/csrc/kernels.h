@@ -154,7 +154,8 @@ hipError_t launch_zfinal(const float* zpart, int S, int64_t cap, int r, const in
                          int bm, int64_t max_rows, uint16_t* zhl, hipStream_t stream);
 hipError_t launch_skinny(const SkinnyConfig& c, bool gateup, const GemmArgs& a, int grid_y,
                          hipStream_t stream, bool fp8 = false);
-hipError_t launch_tiled(const TiledConfig& c, bool gateup, const GemmArgs& a, hipStream_t stream);
+hipError_t launch_tiled(const TiledConfig& c, bool gateup, const GemmArgs& a, hipStream_t stream,
+                        bool fp8 = false);
 hipError_t launch_sgmv_expand(const SgmvArgs& a, int max_blocks, hipStream_t stream);
 hipError_t launch_combine(const float* D, int ksplit, int64_t split_stride, const int* pair_row,
                           const float* topk_w, int T, int k, int h, uint16_t* y,

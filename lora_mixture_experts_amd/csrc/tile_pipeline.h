@@ -59,22 +59,32 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int NST, bool SPREAD = true, int NWAVES = 4>
+// W8: the B tile holds one-byte E4M3 codes (BK bytes per row) instead of bf16; its fragments are
+// converted to bf16 after the LDS read. The k order inside a stage then differs from the bf16
+// tile's (lane group fg takes k 32 fg + 8 j .. + 7 in sub-step j, on both operands), so that one
+// 16-byte read of a code row serves two sub-steps.
+template <int BM, int BN, int WM, int WN, int BK, int NST, bool SPREAD = true, int NWAVES = 4,
+          bool W8 = false>
 struct TilePipe {
   static_assert(BK == 32 || BK == 64, "K step of 32 or 64");
+  static_assert(!W8 || BK == 64, "E4M3 tiles take 64-wide K steps");
   static_assert(NST >= 2, "at least two LDS stages");
   static constexpr int WAVES_N = BN / WN;
   static_assert((BM / WM) * WAVES_N == NWAVES, "WM x WN wavefront tiles cover the tile");
   static constexpr int FM = WM / 32, FN = WN / 32;
-  static constexpr int CPR = BK / 8;               // 16-byte chunks per tile row
-  static constexpr int RPB = 64 / CPR;             // tile rows per 1 KB load block
+  static constexpr int CPR = BK / 8;               // 16-byte chunks per A tile row
+  static constexpr int RPB = 64 / CPR;             // A tile rows per 1 KB load block
+  static constexpr int BROW = W8 ? BK : 2 * BK;    // bytes per B tile row
+  static constexpr int CPRB = BROW / 16;           // 16-byte chunks per B tile row
+  static constexpr int RPBB = 64 / CPRB;           // B tile rows per 1 KB load block
   static constexpr int NA = BM / RPB / NWAVES;     // load blocks per wavefront and stage (A)
-  static constexpr int NB = BN / RPB / NWAVES;     // (B)
+  static constexpr int NB = BN / RPBB / NWAVES;    // (B)
   static constexpr int PER = NA + NB;              // loads per wavefront and stage
   static constexpr int SUB = BK / 16;              // MFMA sub-steps per stage
-  static constexpr uint32_t STAGE_BYTES = (BM + BN) * BK * 2;
+  static constexpr uint32_t A_BYTES = BM * BK * 2;
+  static constexpr uint32_t STAGE_BYTES = A_BYTES + BN * BROW;
   static constexpr uint32_t LDS_BYTES = NST * STAGE_BYTES;
-  static_assert(NA * RPB * NWAVES == BM && NB * RPB * NWAVES == BN,
+  static_assert(NA * RPB * NWAVES == BM && NB * RPBB * NWAVES == BN,
                 "tiles must split into load blocks");
   static_assert(FM + FN <= 15, "one sub-step of fragment reads must fit the LDS counter");
   static_assert((NST - 1) * PER < 64, "in-flight loads must fit vmcnt");
@@ -86,14 +96,23 @@ struct TilePipe {
   __device__ static __forceinline__ int swz(int r, int c) {
     return BK == 64 ? (c ^ ((r >> 1) & 7)) : (c ^ ((r >> 2) & 3));
   }
+  __device__ static __forceinline__ int swz_b(int r, int c) {
+    return W8 ? (c ^ ((r >> 2) & 3)) : swz(r, c);
+  }
   // Tile row and K chunk that lane `lane` of wavefront `wave` loads in its i-th block of A
-  // (rows of B likewise): the lane fills slot lane % CPR of row lane / CPR of the block, so it
-  // fetches the chunk that the swizzle puts in that slot of that (tile) row.
+  // (load_row_b / load_chunk_b: of B): the lane fills slot lane % CPR of row lane / CPR of the
+  // block, so it fetches the chunk that the swizzle puts in that slot of that (tile) row.
   __device__ static __forceinline__ int load_row(int i, int wave, int lane) {
     return (i * NWAVES + wave) * RPB + lane / CPR;
   }
   __device__ static __forceinline__ int load_chunk(int row, int lane) {
     return swz(row, lane % CPR);
+  }
+  __device__ static __forceinline__ int load_row_b(int i, int wave, int lane) {
+    return (i * NWAVES + wave) * RPBB + lane / CPRB;
+  }
+  __device__ static __forceinline__ int load_chunk_b(int row, int lane) {
+    return swz_b(row, lane % CPRB);
   }
 
   // The loads of a K step: PER 1 KB blocks per wavefront, block d (< NA: the A tile, else the B
@@ -110,9 +129,8 @@ struct TilePipe {
     __device__ __forceinline__ int main_steps() const { return 1 << 30; }
     __device__ __forceinline__ void prep(int) {}
     __device__ __forceinline__ void load_main(int d, int ks, uint32_t lds_addr) {
-      const uint32_t soff = (uint32_t)ks * BK * 2;
-      if (d < NA) lds_dma16(xr, xo[d], soff, lds_addr);
-      else lds_dma16(wr, wo[d - NA], soff, lds_addr);
+      if (d < NA) lds_dma16(xr, xo[d], (uint32_t)ks * BK * 2, lds_addr);
+      else lds_dma16(wr, wo[d - NA], (uint32_t)ks * BROW, lds_addr);
     }
     __device__ __forceinline__ void load(int d, int ks, uint32_t lds_addr) {
       load_main(d, ks, lds_addr);
@@ -138,7 +156,7 @@ struct TilePipe {
     const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
     auto block_addr = [&](int d, int stage) {
       const uint32_t sa = lds0 + stage * STAGE_BYTES + wave * 1024;
-      return d < NA ? sa + d * NWAVES * 1024 : sa + BM * BK * 2 + (d - NA) * NWAVES * 1024;
+      return d < NA ? sa + d * NWAVES * 1024 : sa + A_BYTES + (d - NA) * NWAVES * 1024;
     };
     auto issue = [&](int ks, int stage) {
       ld.prep(ks);
@@ -146,10 +164,11 @@ struct TilePipe {
       for (int d = 0; d < PER; ++d) ld.load(d, ks, block_addr(d, stage));
     };
     const int fr = lane & 31, fg = lane >> 5;
+    u32x4 bq[FN];  // W8: the 16 codes of each B fragment row that serve sub-steps j, j + 1
     auto read_frags = [&](int stage, int j, u32x4* af, u32x4* bf) {
       const uint16_t* A = lds + stage * (STAGE_BYTES / 2);
-      const uint16_t* B = A + BM * BK;
-      const int c = 2 * j + fg;
+      const char* B = reinterpret_cast<const char*>(A) + A_BYTES;
+      const int c = W8 ? 4 * fg + j : 2 * j + fg;
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int r = wm * WM + i * 32 + fr;
@@ -158,7 +177,13 @@ struct TilePipe {
 #pragma unroll
       for (int i = 0; i < FN; ++i) {
         const int r = wn * WN + i * 32 + fr;
-        bf[i] = *reinterpret_cast<const u32x4*>(B + r * BK + 8 * swz(r, c));
+        if (W8) {
+          if ((j & 1) == 0)
+            bq[i] = *reinterpret_cast<const u32x4*>(B + r * BROW + 16 * swz_b(r, 2 * fg + j / 2));
+          bf[i] = e4m3x8_to_bf16(bq[i], j & 1);
+        } else {
+          bf[i] = *reinterpret_cast<const u32x4*>(B + r * BROW + 16 * swz_b(r, c));
+        }
       }
     };
     auto mfmas_interleaved = [&](const u32x4* af, const u32x4* bf, bool reads_pending) {

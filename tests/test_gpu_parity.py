@@ -338,8 +338,9 @@ def test_forward_full_size_stress(name):
 
 # ----------------------------------------------------------------------------- FP8 expert weights
 
-# the skinny-path shapes of SMALL (at most 24 token-expert pairs per expert)
-FP8_SMALL = [n for n, w in SMALL.items() if w.T * w.topk <= 24 * w.n_experts]
+# every small shape: the weight-streaming ones (at most 24 token-expert pairs per expert) and the
+# LDS-tiled ones (64-, 128- and 256-row blocks)
+FP8_SMALL = list(SMALL)
 
 
 def _run_fp8(inp: dict, topk: int, workspace=None):
@@ -351,8 +352,10 @@ def _run_fp8(inp: dict, topk: int, workspace=None):
     return y
 
 
-def test_fp8_small_cases_exist():
+def test_fp8_small_cases_cover_both_paths():
+    tiled = {n for n in FP8_SMALL if SMALL[n].T * SMALL[n].topk > 24 * SMALL[n].n_experts}
     assert {"tiny", "ragged", "r8_k1", "r32_k4", "r64_E1", "fg_small", "one_token"} <= set(FP8_SMALL)
+    assert {"tiled64", "tiled128_r64", "tiled256_r64", "tiled256_shortk"} <= tiled
 
 
 @pytest.mark.parametrize("name", FP8_SMALL)
@@ -366,26 +369,19 @@ def test_forward_fp8_small_vs_oracle(name, b_scale):
     check_close(y, oracle_rows(inp, w.topk), what=f"fp8 {name} b_scale={b_scale}")
 
 
-def test_forward_fp8_scales_matter():
+@pytest.mark.parametrize("name", ["ragged", "tiled64", "tiled256_r64"])
+def test_forward_fp8_scales_matter(name):
     """Doubling one expert's scales doubles its base term: the output changes where the oracle
     says it does (a kernel that ignored the scales, or applied them to the wrong rows, fails)."""
-    w = SMALL["ragged"]
+    w = SMALL[name]
     inp = configs.make_inputs_fp8(w, 4)
     inp["W1_scale"][1] *= 2.0
-    inp["W2_scale"][3] *= 0.5
+    inp["W2_scale"][0, : w.hidden // 2] *= 0.5
     y = _run_fp8(inp, w.topk)
-    check_close(y, oracle_rows(inp, w.topk), what="fp8 rescaled experts")
+    check_close(y, oracle_rows(inp, w.topk), what=f"fp8 rescaled experts {name}")
 
 
-def test_forward_fp8_tiled_size_unsupported():
-    w = SMALL["mid"]  # 50 pairs per expert
-    inp = configs.make_inputs_fp8(w, 1)
-    with pytest.raises(ml.MoeLoraError) as ei:
-        _run_fp8(inp, w.topk)
-    assert ei.value.code == ml.EUNSUPPORTED
-
-
-@pytest.mark.parametrize("name", ["decode", "fg"])
+@pytest.mark.parametrize("name", ["decode", "fg", "stress_same", "prefill"])
 def test_forward_fp8_full_size(name):
     w = configs.WORKLOADS[name]
     _say(f"full-size fp8 {name}: generating inputs on the GPU")
@@ -395,8 +391,18 @@ def test_forward_fp8_full_size(name):
             inp["A1"], inp["B1"], inp["A2"], inp["B2"], inp["adapter_ids"], w.topk)
     y = ml.forward_fp8(*args)
     torch.cuda.synchronize()
-    _say(f"full-size fp8 {name}: oracle on all {w.T} tokens")
-    rel = _all_tokens_chunked(inp, w, y, f"fp8 {name}")
+    if w.T <= 1024:
+        _say(f"full-size fp8 {name}: oracle on all {w.T} tokens")
+        rel = _all_tokens_chunked(inp, w, y, f"fp8 {name}")
+    else:
+        ws = ml.new_workspace(_dims(w), w.topk, DEV)
+        ml.forward_fp8(*args, workspace=ws)
+        torch.cuda.synchronize()
+        toks = _block_tokens(ml.read_layout_tables(ws, _dims(w), w.topk), w.topk)
+        del ws
+        _say(f"full-size fp8 {name}: oracle on {len(toks)} tokens covering every 64-row sub-block")
+        rel = check_close(y[torch.from_numpy(toks).long().to(DEV)], oracle_rows(inp, w.topk, toks),
+                          what=f"fp8 {name}")
     _say(f"full-size fp8 {name}: max rel err {rel:.2e}")
     y2 = ml.forward_fp8(*args)
     torch.cuda.synchronize()
