@@ -93,14 +93,21 @@ PathPlan pick_path(int64_t P, int E, int h, int I) {
   // 128- and 256-row tiles run eight wavefronts (two per SIMD): one wavefront's LDS waits and
   // barriers are covered by the other's MFMAs
   const TiledConfig t64{64, 128, 32, 64, 64, 2, 4}, t64w{64, 256, 32, 64, 64, 2, 8},
-      t128{128, 128, 32, 64, 64, 2, 8}, t256{256, 256, 64, 128, 64, 2, 8};
+      t128{128, 128, 32, 64, 64, 2, 8}, t192{192, 256, 96, 64, 64, 2, 8},
+      t256{256, 256, 64, 128, 64, 2, 8};
   const bool fits256 = (2 * I) % 256 == 0 && h % 256 == 0;
   pl.tc = mean < 192.0 ? t64 : (mean < 768.0 || !fits256 ? t128 : t256);
   pl.tc_dn = pl.tc;
   // 64-row blocks: gate_up (2I wide) takes 256 columns per tile with eight wavefronts
   if (mean < 192.0) pl.tc = t64w;
+  // About 100 to 160 rows per expert (weight-streaming bound): the layout pads each expert to
+  // 192 rows, so that down reads every expert's W2 once, in 192-row tiles; gate_up walks the
+  // same layout in 64-row tiles (tiles of padding only are skipped), which keeps two workgroups
+  // per CU and its LoRA epilogue short when many adapters share a tile (measured on the
+  // adapter-stress batches, ~128 rows per expert: down 0.44 -> 0.35 ms with one adapter)
+  if (mean >= 96.0 && mean <= 160.0 && fits256) pl.tc_dn = t192;
   // MOELORA_TILED="bm,bn,wm,wn,bk,nst[,nw][;...]" forces the tiles of gate_up (and of
-  // down when a second set with the same bm follows) for experiments
+  // down when a second set follows) for experiments
   static int forced = -1;  // -1 unread, 0 none, 1 skinny, 2 tiled, 3/4 skinny with 1/2 tiles
   static TiledConfig ft, ftd;
   if (forced < 0) {
@@ -123,7 +130,7 @@ PathPlan pick_path(int64_t P, int E, int h, int I) {
         ftd = ft;
         const char* semi = strchr(tenv, ';');
         TiledConfig d2;
-        if (semi && parse(semi + 1, &d2) && d2.bm == ft.bm) ftd = d2;
+        if (semi && parse(semi + 1, &d2)) ftd = d2;
         forced = 2;
       }
     }
@@ -138,12 +145,14 @@ PathPlan pick_path(int64_t P, int E, int h, int I) {
     pl.tc = ft;
     pl.tc_dn = ftd;
   }
-  // column tiles must divide the GEMM widths (2I for gate_up, h for down); 128 always does
-  if ((2 * I) % pl.tc.bn != 0 || h % pl.tc_dn.bn != 0) {
+  // column tiles must divide the GEMM widths (2I for gate_up, h for down; 128 always does), and
+  // the smaller row tile must divide the larger (the layout's row block)
+  const int bmax = std::max(pl.tc.bm, pl.tc_dn.bm), bmin = std::min(pl.tc.bm, pl.tc_dn.bm);
+  if ((2 * I) % pl.tc.bn != 0 || h % pl.tc_dn.bn != 0 || bmin <= 0 || bmax % bmin != 0) {
     pl.tc = mean < 192.0 ? t64 : t128;
     pl.tc_dn = pl.tc;
   }
-  pl.bm = pl.tiled ? pl.tc.bm : 16 * pl.nt;
+  pl.bm = pl.tiled ? std::max(pl.tc.bm, pl.tc_dn.bm) : 16 * pl.nt;
   return pl;
 }
 
@@ -247,7 +256,7 @@ ForwardPlan make_plan(const moe_lora_dims* d, int topk, bool fp8) {
     // last, partial round of 256x256 tiles then costs a large share of the time)
     const int64_t est_tiles =
         (int64_t)((pl.P + pl.bm - 1) / pl.bm + E) * (h / pl.path.tc_dn.bn);
-    pl.sk.ksplit = est_tiles < 4 * 256 ? kMaxDownSplit : 1;
+    pl.sk.ksplit = est_tiles < 4 * 256 && pl.path.tc_dn.bm != 192 ? kMaxDownSplit : 1;
     // MOELORA_DOWN_SPLIT=1|2 overrides it (experiments)
     static int down_split = -1;
     if (down_split < 0) {
@@ -309,6 +318,8 @@ bool moelora_make_layout(int T, int h, int I, int E, int nA, int r, int topk, in
   L->block_seg = take(4 * (size_t)(L->cap / 16 + 1));
   L->pair_row = take(4 * (size_t)P);
   L->sorted_ad = take(4 * (size_t)L->cap);
+  L->sub_row0 = take(4 * (size_t)(L->cap / 64 + E + 1));
+  L->n_sub = take(4);
   L->seg_table = take(16 * (size_t)P);
   L->n_seg = take(4);
   L->z1 = take(4 * (size_t)kMaxSplit * L->cap * r);
@@ -464,6 +475,11 @@ int enqueue_forward(const ForwardPlan& pl, const MoeLoraLayout& L, const void* x
   al.pair_row = pair_row;
   al.sorted_ad = sorted_ad;
   al.n_blocks = n_blocks;
+  // tiled GEMMs smaller than the layout's blocks walk its live 64-row sub-tiles
+  const bool subtiles = path.tiled && std::min(path.tc.bm, path.tc_dn.bm) < bm;
+  al.sub_row0 = subtiles ? (int*)(ws + L.sub_row0) : nullptr;
+  al.n_sub = subtiles ? (int*)(ws + L.n_sub) : nullptr;
+  al.sub_m = 64;
   al.g_lists = (int*)(ws + L.align_lists);
   const size_t lds = align_lds_plan(T, topk, E, nA, &al);
   if (launch_align(al, lds, stream) != hipSuccess) return MOELORA_EHIP;
@@ -502,6 +518,9 @@ int enqueue_forward(const ForwardPlan& pl, const MoeLoraLayout& L, const void* x
   g.act_out = act;
   g.d_out = dpair;
   g.n_blocks_max = pl.max_blocks;
+  g.layout_bm = bm;
+  g.sub_row0 = al.sub_row0;
+  g.n_sub = al.n_sub;
   // MOELORA_LORA_EXT=0 keeps every tiled LoRA expand in the epilogue (experiments)
   static int lora_ext_env = -1;
   if (lora_ext_env < 0) {
@@ -850,6 +869,9 @@ int moe_lora_sgmv(const void* x, const void* A, const void* B, const int32_t* ad
   al.pair_row = nullptr;
   al.sorted_ad = (int*)(ws + L.sorted_ad);
   al.n_blocks = (int*)(ws + L.n_blocks);
+  al.sub_row0 = nullptr;
+  al.n_sub = nullptr;
+  al.sub_m = 64;
   al.g_lists = (int*)(ws + L.align_lists);
   const size_t lds = align_lds_plan(T, 1, 1, nA, &al);
   if (launch_align(al, lds, stream) != hipSuccess) return MOELORA_EHIP;
@@ -946,6 +968,9 @@ int moe_lora_route_align(const float* router_logits, const int32_t* adapter_ids,
   al.pair_row = nullptr;
   al.sorted_ad = nullptr;
   al.n_blocks = nullptr;
+  al.sub_row0 = nullptr;
+  al.n_sub = nullptr;
+  al.sub_m = 64;
   al.g_lists = (int*)(ws + L.align_lists);
   const size_t lds = align_lds_plan(d->T, topk, d->n_experts, d->n_adapters, &al);
   if (launch_align(al, lds, stream) != hipSuccess) return MOELORA_EHIP;

@@ -153,7 +153,7 @@ __device__ __forceinline__ void lora_expand_segs(const GemmArgs& a, f32x16 (&acc
       ad = sanitize_adapter((int)sg[1], a.nA);
     }
     in_mask = __ballot(in);
-    runs = __ballot(in && ad >= 0);
+    runs = __ballot(in && ad >= 0 && hi > lo);
   };
   // the next chunk with runs with an adapter, if any
   auto next_runs = [&]() {
@@ -300,7 +300,10 @@ __global__ __launch_bounds__(64 * NW, 1) void tiled_gemm_kernel(GemmArgs a, int 
   // numbering: the workgroups it runs at once cover a few groups, every token tile and weight
   // tile fetched into its L2 serves several of them, and no XCD gets more tiles than another.
   // (down may also split K: split ks of every tile comes after all tiles of split ks - 1)
-  const int nblk = *a.n_blocks;
+  // row tiles: the layout's row blocks, or (tiles smaller than the layout's blocks) the live
+  // 64-row sub-tiles listed by the align, so that tiles of padding only never run
+  const int sub = a.layout_bm / BM;
+  const int nblk = sub > 1 ? *a.n_sub : *a.n_blocks;
   const int tiles = nblk * n_tiles_n;
   const int live = tiles * (GATEUP ? 1 : a.ksplit);
   const int per_xcd = (live + 7) >> 3;
@@ -317,14 +320,15 @@ __global__ __launch_bounds__(64 * NW, 1) void tiled_gemm_kernel(GemmArgs a, int 
   const int rg = u / (GR * cols);                 // row group (all but the last GR tall)
   const int rows = min(GR, nblk - rg * GR);
   const int w = u - rg * GR * cols;
-  const int blk = rg * GR + w % rows;
+  const int rt = rg * GR + w % rows;  // row tile
   const int ntile = cg * GC + w / rows;
+  const int row0 = sub > 1 ? a.sub_row0[rt] : rt * BM;
+  const int blk = row0 / a.layout_bm;  // its row block of the layout
   const int e = a.block_expert[blk];
   const int K = a.K;
   const int kspan = GATEUP ? K : K / a.ksplit;  // this split's K range: [ks * kspan, +kspan)
   const uint32_t kbyte0 = (uint32_t)ks * kspan * 2;
   const size_t N = (size_t)a.N;
-  const int row0 = blk * BM;
   const size_t w_rows = GATEUP ? 2 * N : N;  // weight rows of one expert
 
   // byte offsets of the chunk each lane loads at K step 0 (padding rows: out of range, zeros)
@@ -505,7 +509,9 @@ hipError_t launch_tiled(const TiledConfig& c, bool gateup, const GemmArgs& a, hi
   const int n_tiles_n = cols / c.bn;
   // one workgroup per (row block, column tile, K split) for the largest row-block count,
   // rounded up to a multiple of the 8 XCDs
-  int total = a.n_blocks_max * n_tiles_n * splits;
+  if (a.layout_bm % c.bm != 0 || (a.layout_bm != c.bm && (c.bm != 64 || !a.sub_row0)))
+    return hipErrorInvalidValue;
+  int total = a.n_blocks_max * (a.layout_bm / c.bm) * n_tiles_n * splits;
   total = (total + 7) / 8 * 8;
   if (total <= 0) return hipSuccess;
   // E4M3 weights: the tiles the path picks by default
@@ -520,6 +526,7 @@ hipError_t launch_tiled(const TiledConfig& c, bool gateup, const GemmArgs& a, hi
   MOELORA_TILED8(128, 128, 32, 64, false)
   MOELORA_TILED8(256, 256, 64, 128, true)
   MOELORA_TILED8(256, 256, 64, 128, false)
+  MOELORA_TILED8(192, 256, 96, 64, false)
 #undef MOELORA_TILED8
   if (fp8) return hipErrorInvalidValue;
 #define MOELORA_TILED(BM_, BN_, WM_, WN_, BK_, NST_, NW_)                                   \
@@ -534,6 +541,7 @@ hipError_t launch_tiled(const TiledConfig& c, bool gateup, const GemmArgs& a, hi
   MOELORA_TILED(64, 256, 32, 64, 64, 2, 8)
   MOELORA_TILED(192, 256, 96, 64, 64, 2, 8)
   MOELORA_TILED(128, 256, 64, 64, 64, 2, 8)
+  MOELORA_TILED(256, 256, 128, 128, 64, 2, 4)
   // down only (one 32-column fragment per wave: no gate/up halves)
   if (!gateup && c.bm == 192 && c.bn == 128 && c.wm == 96 && c.wn == 32 && c.bk == 64 &&
       c.nst == 2 && c.nw == 8)

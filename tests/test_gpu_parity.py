@@ -120,6 +120,10 @@ SMALL = {
     "tiled256_r64": Workload("tiled256_r64", 2048, 256, 384, 4, 2, 6, 64, adapters="zipf_runs", run=100),
     "tiled256_k1": Workload("tiled256_k1", 1600, 512, 640, 2, 1, 4, 16),
     "tiled256_shortk": Workload("tiled256_shortk", 1700, 256, 128, 3, 2, 4, 16),  # down: 2 K steps
+    # about 100 to 160 rows per expert: 192-row layout blocks, gate_up in 64-row sub-tiles (tiles
+    # of padding only skipped), down in 192-row tiles
+    "tiled192": Workload("tiled192", 512, 256, 384, 8, 2, 6, 16),
+    "tiled192_distinct": Workload("tiled192_distinct", 600, 256, 256, 8, 2, 600, 16, adapters="distinct"),
 }
 
 
@@ -237,7 +241,7 @@ def test_forward_flags_bad_adapter_and_nonfinite_logit():
     check_close(y[torch.from_numpy(keep).long().to(DEV)], oracle_rows(inp, w.topk, keep), what="finite tokens")
 
 
-@pytest.mark.parametrize("name", ["fg_small", "tiled64", "tiled256_r64", "tiled128_runs"])
+@pytest.mark.parametrize("name", ["fg_small", "tiled64", "tiled256_r64", "tiled128_runs", "tiled192"])
 def test_forward_poisoned_workspace_and_determinism(name):
     """Whatever the workspace held before (all-ones bytes, 0x7F bytes, a fresh allocation), the
     call gives the same bytes, within the bound of the oracle: no stage reads a region it did not
