@@ -404,7 +404,12 @@ __global__ __launch_bounds__(64 * NW, 1) void tiled_gemm_kernel(GemmArgs a, int 
       run = in && ad >= 0 && hi > lo;
     }
     const uint64_t m = __ballot(run);
-    const bool more = (__ballot(in) >> 63) != 0;  // segments past this chunk may overlap the tile
+    // the chunk's last segment starts inside the tile: the next one may too
+    bool more = (__ballot(in) >> 63) != 0;
+    if (more) {
+      const int sn = first + 64;
+      more = sn < *a.n_seg && a.seg_table[4 * (size_t)sn + 2] < row0 + BM;
+    }
     const int nr = __popcll(m);
     const int n_ext = (nr + ld.rps - 1) / ld.rps;
     if (more || n_ext == 0 || 4 * n_ext > ld.nks) return;
