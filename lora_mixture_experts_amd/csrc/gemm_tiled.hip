@@ -29,37 +29,66 @@
 
 namespace moelora {
 
-// Store of a finished tile at its rows of the sorted layout: SiLU-and-mul (gate_up, into act) or
-// the plain store (down, into the K split's part of D). Padding rows hold zeros (their token rows
-// were loaded as zeros and carry no adapter) and are stored like the others, so the store needs
-// no per-row lookup. Lane l holds rows 8*(v/4) + 4*(l/32) + (v%4) of each 32-row group and column
-// (l % 32) of each 32-column fragment.
-template <bool GATEUP, int BN, int WM, int WN, int FM, int FN>
-__device__ __forceinline__ void tiled_store(const GemmArgs& a, f32x16 (&acc)[FM][FN], int row0,
-                                            int wm, int wn, int ntile, int ks, int lane) {
-  const size_t N = (size_t)a.N;
+// Store of a finished tile at its rows of the sorted layout: SiLU-and-mul (gate_up, into act as
+// bf16) or the plain fp32 store (down, into the K split's part of D). Padding rows hold zeros
+// (their token rows were loaded as zeros and carry no adapter) and are stored like the others,
+// so the store needs no per-row lookup. Lane l holds rows 8*(v/4) + 4*(l/32) + (v%4) of each
+// 32-row group and column (l % 32) of each 32-column fragment, so it goes through LDS (the main
+// loop's stages are free by then): 16 rows at a time, each wavefront writes its values into its
+// own region, row-major (rows padded so that the two lane halves, 4 rows apart, hit different
+// banks), then reads whole 16-byte pieces of rows back and stores them: one global store per
+// 1 KB rather than one per element column and row.
+template <bool GATEUP, int BN, int WM, int WN, int FM, int FN, int NW, uint32_t LDS_BYTES>
+__device__ __forceinline__ void tiled_store(const GemmArgs& a, f32x16 (&acc)[FM][FN],
+                                            uint16_t* lds, int row0, int wm, int wn, int ntile,
+                                            int ks, int wave, int lane) {
+  constexpr int EB = GATEUP ? 2 : 4;          // bytes per stored element
+  constexpr int COLS = GATEUP ? WN / 2 : WN;  // stored columns of the wavefront
+  constexpr int STRIDE = COLS * EB + 32;      // LDS bytes per row
+  constexpr int PR = 16;                      // rows per pass
+  constexpr int CPRW = COLS * EB / 16;        // 16-byte pieces per row
+  static_assert(NW * PR * STRIDE <= (int)LDS_BYTES, "store staging must fit the LDS stages");
+  static_assert((PR * CPRW) % 64 == 0, "whole pieces per lane");
   const int fr = lane & 31, fg = lane >> 5;
-  // column of fragment jn: gate_up act column (gate and up halves share it); down output column
-  auto col_of = [&](int jn) -> size_t {
-    if (GATEUP) return (size_t)ntile * (BN / 2) + wn * (WN / 2) + (jn % (FN / 2)) * 32 + fr;
-    return (size_t)ntile * BN + wn * WN + jn * 32 + fr;
-  };
+  char* base = reinterpret_cast<char*>(lds) + wave * (PR * STRIDE);
+  const size_t N = (size_t)a.N;
+  const size_t col0 =
+      GATEUP ? (size_t)ntile * (BN / 2) + wn * (WN / 2) : (size_t)ntile * BN + wn * WN;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const size_t srow = (size_t)row0 + wm * WM + i * 32 + 8 * (v / 4) + 4 * fg + (v % 4);
-      if (GATEUP) {
+    for (int h = 0; h < 2; ++h) {
+      __syncthreads();  // the previous pass's pieces are read
 #pragma unroll
-        for (int jn = 0; jn < FN / 2; ++jn) {
-          const float g = acc[i][jn][v], u = acc[i][jn + FN / 2][v];
-          const float hv = g / (1.f + __expf(-g)) * u;
-          a.act_out[srow * N + col_of(jn)] = (uint16_t)f32_to_bf16_bits(hv);
+      for (int vv = 0; vv < 8; ++vv) {
+        const int v = 8 * h + vv;
+        const int r = 8 * (vv / 4) + 4 * fg + (vv % 4);  // row within the pass
+        if (GATEUP) {
+#pragma unroll
+          for (int jn = 0; jn < FN / 2; ++jn) {
+            const float g = acc[i][jn][v], u = acc[i][jn + FN / 2][v];
+            const float hv = g / (1.f + __expf(-g)) * u;
+            *reinterpret_cast<uint16_t*>(base + r * STRIDE + (jn * 32 + fr) * 2) =
+                (uint16_t)f32_to_bf16_bits(hv);
+          }
+        } else {
+#pragma unroll
+          for (int jn = 0; jn < FN; ++jn)
+            *reinterpret_cast<float*>(base + r * STRIDE + (jn * 32 + fr) * 4) = acc[i][jn][v];
         }
-      } else {
+      }
+      __syncthreads();
 #pragma unroll
-        for (int jn = 0; jn < FN; ++jn)
-          a.d_out[ks * a.d_split_stride + srow * N + col_of(jn)] = acc[i][jn][v];
+      for (int it = 0; it < PR * CPRW / 64; ++it) {
+        const int idx = it * 64 + lane;
+        const int r = idx / CPRW, c = idx % CPRW;
+        const u32x4 val = *reinterpret_cast<const u32x4*>(base + r * STRIDE + c * 16);
+        const size_t srow = (size_t)row0 + wm * WM + i * 32 + 16 * h + r;
+        if (GATEUP)
+          *reinterpret_cast<u32x4*>(a.act_out + srow * N + col0 + c * 8) = val;
+        else
+          *reinterpret_cast<u32x4*>(a.d_out + ks * a.d_split_stride + srow * N + col0 + c * 4) =
+              val;
       }
     }
   }
@@ -483,7 +512,8 @@ __global__ __launch_bounds__(64 * NW, 1) void tiled_gemm_kernel(GemmArgs a, int 
     lora_expand_segs<GATEUP, BM, BN, WM, WN, FM, FN, Pipe::LDS_BYTES, NW>(a, acc, lds, blk, row0,
                                                                            wm, wn, ntile, e, wave,
                                                                            lane);
-  tiled_store<GATEUP, BN, WM, WN, FM, FN>(a, acc, row0, wm, wn, ntile, ks, lane);
+  tiled_store<GATEUP, BN, WM, WN, FM, FN, NW, Pipe::LDS_BYTES>(a, acc, lds, row0, wm, wn, ntile, ks,
+                                                                wave, lane);
 }
 
 template <bool GATEUP, int BM, int BN, int WM, int WN, int BK, int NST, int NW, bool FP8 = false>
