@@ -209,20 +209,24 @@ def run_sgmv(args, torch, ml, dev):
     for _ in range(args.warmup):
         ml.sgmv(xd, Ad, Bd, add, yd, workspace=ws)
     torch.cuda.synchronize()
-    # each call between two events on its stream: the GPU time of the call's three launches (the
-    # host's launch rate does not enter, unlike a wall-clock loop)
+    # the timed region: K back-to-back calls (value); then K more calls, each between two events
+    # on its stream, for the per-call GPU time of its three launches (median and spread; the
+    # roofline uses the median)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        ml.sgmv(xd, Ad, Bd, add, yd, workspace=ws)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     for a, b in evs:
         a.record()
         b.record()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for a, b in evs:
         a.record()
         ml.sgmv(xd, Ad, Bd, add, yd, workspace=ws)
         b.record()
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
     call_ms = [a.elapsed_time(b) for a, b in evs]
     st = call_stats(call_ms)
     n_ad = len(np.unique(ad.numpy()))
