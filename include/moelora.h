@@ -133,8 +133,8 @@ int moe_lora_forward_timed(const void *x, const float *router_logits, const void
  * device's first call until the process ends; the call itself allocates nothing (no hipMalloc,
  * hipFree or allocating library routine). The caller still passes every input and y, device
  * memory as in moe_lora_forward. Sizes whose workspace (moe_lora_workspace_size) exceeds
- * 128 MiB are rejected with MOELORA_ESCRATCH before any device work: the decode, fine-grained
- * and adapter-stress sizes fit, 256-row prefill layouts do not. Every call on one GPU shares
+ * 128 MiB are rejected with MOELORA_ESCRATCH before any device work: the decode-sized layouts
+ * (few token-expert pairs per expert) fit, the tiled layouts of large batches may not. Every call on one GPU shares
  * that GPU's array, which keeps the last call's contents: two calls that overlap on one GPU
  * (different streams, or different threads without ordering) race and must not be issued; calls
  * ordered on one stream are safe. The data flags of moe_lora_debug_status are not readable for

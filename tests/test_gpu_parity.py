@@ -31,13 +31,14 @@ def _say(msg):
 
 # ----------------------------------------------------------------------------- route + align
 
-# (seg_pad, block_m) settings: every one the forward uses (seg_pad 1 with 16-, 32-, 64-, 128- and
-# 256-row blocks) and a few with padded segments
+# (seg_pad, block_m) settings: every one the forward uses (seg_pad 1 with 16-, 32-, 64-, 128-, 192-
+# and 256-row blocks) and a few with padded segments
 ROUTE_CASES = [
     ("tiny", 1, 1), ("tiny", 4, 16), ("decode", 1, 16), ("decode", 16, 16), ("prefill", 1, 64),
     ("prefill", 16, 128), ("fg", 1, 32), ("fg", 8, 32), ("stress_distinct", 1, 64),
     ("stress_same", 1, 64), ("stress_distinct", 16, 256), ("prefill", 1, 256), ("prefill", 1, 128),
     ("stress_distinct", 1, 128), ("stress_same", 1, 256), ("fg", 1, 16), ("tiny", 1, 128),
+    ("stress_distinct", 1, 192), ("stress_same", 1, 192), ("tiny", 3, 192),
 ]
 
 
