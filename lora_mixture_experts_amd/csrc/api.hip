@@ -56,6 +56,20 @@ int check_device() {
   return known[dev] == 1 ? MOELORA_OK : MOELORA_EDEVICE;
 }
 
+// Workgroups of the 256-row tiled GEMM resident at once: one per CU, rounded down to the 8 XCDs
+// (per device, looked up once); 0 on error.
+int resident_tiles() {
+  static int known[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (known[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    known[dev] = n / 8 * 8;
+  }
+  return known[dev];
+}
+
 // Align kernel's LDS: its arrays (keys, two pair-id buffers, segment starts and deltas, with the
 // radix digit counts overlaying the segment region) when they fit, else the digit counts only
 // and the arrays go to the workspace. Returns the dynamic LDS bytes and fills the kernel's sizes.
@@ -235,12 +249,15 @@ struct ForwardPlan {
   int n_sub_max;   // 64-row sub-blocks of it
   int s1, s2;      // K splits of the gate_up and down shrinks
   bool shrink64;   // 64-row shrink on the tiled path
+  int tail_split;  // tiled down: K parts of the last round's tiles (0: sk.ksplit for every tile)
+  int d_parts() const { return tail_split > 1 ? tail_split : sk.ksplit; }
 };
 
 ForwardPlan make_plan(const moe_lora_dims* d, int topk, bool fp8) {
   ForwardPlan pl;
   const int h = d->hidden, I = d->inter, E = d->n_experts, r = d->rank;
   pl.P = (int64_t)d->T * topk;
+  pl.tail_split = 0;
   pl.path = pick_path(pl.P, E, h, I);
   pl.bm = pl.path.bm;
   pl.sk = pick_skinny(pl.path.nt, h, I);
@@ -257,13 +274,27 @@ ForwardPlan make_plan(const moe_lora_dims* d, int topk, bool fp8) {
     const int64_t est_tiles =
         (int64_t)((pl.P + pl.bm - 1) / pl.bm + E) * (h / pl.path.tc_dn.bn);
     pl.sk.ksplit = est_tiles < 4 * 256 && pl.path.tc_dn.bm != 192 ? kMaxDownSplit : 1;
+    // 256-row tiles (one per CU): only the last, partial round splits K, in four parts
+    // (MOELORA_DOWN_TAIL=0 keeps the split of every tile, for experiments)
+    static int down_tail = -1;
+    if (down_tail < 0) {
+      const char* env = getenv("MOELORA_DOWN_TAIL");
+      down_tail = env ? atoi(env) : 1;
+    }
+    if (down_tail && pl.sk.ksplit > 1 && pl.path.tc_dn.bm == 256 && (I / 64) % 4 == 0) {
+      pl.tail_split = 4;
+      pl.sk.ksplit = 1;
+    }
     // MOELORA_DOWN_SPLIT=1|2 overrides it (experiments)
     static int down_split = -1;
     if (down_split < 0) {
       const char* env = getenv("MOELORA_DOWN_SPLIT");
       down_split = env ? atoi(env) : 0;
     }
-    if (down_split == 1 || down_split == 2) pl.sk.ksplit = down_split;
+    if (down_split == 1 || down_split == 2) {
+      pl.sk.ksplit = down_split;
+      pl.tail_split = 0;
+    }
   }
   const int64_t max_rows = pl.P + (int64_t)E * (pl.bm - 1);
   pl.max_blocks = (int)((max_rows + pl.bm - 1) / pl.bm);
@@ -327,6 +358,7 @@ bool moelora_make_layout(int T, int h, int I, int E, int nA, int r, int topk, in
   L->zhl = take(2 * 2 * (size_t)L->cap * r);
   L->act = take(2 * (size_t)L->cap * I);
   L->dpair = take(4 * (size_t)dsplit * L->cap * h);
+  L->d_parts = take(4 * (size_t)(L->cap / 64 + 1) * (size_t)(h / 64 + 1));
   L->align_lists = take(4 * align_list_ints(T, topk, E, nA));
   L->logits = take(4 * (size_t)T * E);
   L->total = off;
@@ -343,7 +375,7 @@ int plan_and_layout(const moe_lora_dims* d, int32_t topk, bool fp8, ForwardPlan*
   if (rc != MOELORA_OK) return rc;
   *pl = make_plan(d, topk, fp8);
   moelora_make_layout(d->T, d->hidden, d->inter, d->n_experts, d->n_adapters, d->rank, topk, pl->bm,
-                      pl->sk.ksplit, L);
+                      pl->d_parts(), L);
   // act [cap][I] bf16 is read with 32-bit buffer offsets, and padding lanes use offset 2^31
   if (L->cap * (int64_t)d->inter * 2 >= ((int64_t)1 << 31)) return MOELORA_EINVAL_DIMS;
   return MOELORA_OK;
@@ -503,6 +535,9 @@ int enqueue_forward(const ForwardPlan& pl, const MoeLoraLayout& L, const void* x
 
   GemmArgs g;
   g.cap = L.cap;
+  g.tail_split = 0;
+  g.n_cu = 0;
+  g.d_parts = nullptr;
   g.sorted_pairs = sorted;
   g.sorted_ad = sorted_ad;
   g.block_expert = block_expert;
@@ -594,6 +629,14 @@ int enqueue_forward(const ForwardPlan& pl, const MoeLoraLayout& L, const void* x
   g.K = I;
   g.N = h;
   g.ksplit = pl.sk.ksplit;
+  g.tail_split = path.tiled ? pl.tail_split : 0;
+  g.n_cu = 0;
+  g.d_parts = nullptr;
+  if (g.tail_split > 1) {
+    g.n_cu = resident_tiles();
+    if (g.n_cu <= 0) return MOELORA_EHIP;
+    g.d_parts = (int*)(ws + L.d_parts);
+  }
   g.n_col_tiles = g.N / (64 * pl.sk.dn.rt);
   const hipError_t dn_err = path.tiled
                                 ? launch_tiled(path.tc_dn, false, g, stream, fp8)
@@ -602,9 +645,21 @@ int enqueue_forward(const ForwardPlan& pl, const MoeLoraLayout& L, const void* x
   if (!mark(ev, 6, stream)) return MOELORA_EHIP;
 
   // weighted top-k combine -> y (bf16)
-  if (launch_combine(dpair, pl.sk.ksplit, L.cap * (int64_t)h, pair_row, topk_w, T, topk, h,
-                     (uint16_t*)y, stream) != hipSuccess)
-    return MOELORA_EHIP;
+  CombineArgs cb;
+  cb.D = dpair;
+  cb.ksplit = pl.sk.ksplit;
+  cb.split_stride = L.cap * (int64_t)h;
+  cb.d_parts = g.d_parts;
+  cb.part_rows = path.tc_dn.bm;
+  cb.part_cols = path.tc_dn.bn;
+  cb.part_ncol = h / path.tc_dn.bn;
+  cb.pair_row = pair_row;
+  cb.topk_w = topk_w;
+  cb.T = T;
+  cb.k = topk;
+  cb.h = h;
+  cb.y = (uint16_t*)y;
+  if (launch_combine(cb, stream) != hipSuccess) return MOELORA_EHIP;
   if (!mark(ev, 7, stream)) return MOELORA_EHIP;
   return MOELORA_OK;
 }

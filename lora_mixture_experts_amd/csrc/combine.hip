@@ -1,7 +1,8 @@
 // Weighted top-k combine: y[t] = sum_j w[t][j] * D[row(t*k + j)], summed in slot order in fp32,
 // then rounded once to bf16 (round-to-nearest-even). D holds the down GEMM's output rows in the
 // sorted (expert, adapter) order; pair_row maps a pair to its row. D may arrive as two partial
-// buffers (split-K of the down GEMM, ksplit = 2); they are added in split order first.
+// buffers (split-K of the down GEMM: every tile in ksplit parts, or, per tile as d_parts says,
+// 1 to 4 parts); a row's parts are added in part order first.
 //
 // Page "vLLM MoE LoRA SageMaker Bedrock", section "Entendendo os Modelos MoE": the outputs of
 // the experts a token was sent to are aggregated. Each thread owns four consecutive features of
@@ -11,68 +12,81 @@
 
 namespace moelora {
 
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ D, int ksplit,
-                                                      int64_t split_stride,
-                                                      const int* __restrict__ pair_row,
-                                                      const float* __restrict__ topk_w, int T,
-                                                      int k, int h, uint16_t* __restrict__ y) {
+// MAXP: the most parts a row can have (1 or 2: every row has ksplit; 4: d_parts says)
+template <int MAXP>
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+  const int h = a.h, k = a.k;
   const int h4 = h >> 2;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)T * h4) return;
+  if (idx >= (int64_t)a.T * h4) return;
   const int t = (int)(idx / h4);
   const int c = (int)(idx - (int64_t)t * h4) * 4;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   // the pair rows and weights of all slots are loaded first, then the D rows of four slots at a
-  // time (both split parts), so the slots cost a few memory round trips instead of two each
-  int rows[kMaxTopk];
+  // time (every part), so the slots cost a few memory round trips instead of two each
+  int rows[kMaxTopk], np[kMaxTopk];
   float wts[kMaxTopk];
 #pragma unroll
   for (int j = 0; j < kMaxTopk; ++j) {
     if (j < k) {
-      wts[j] = topk_w[(size_t)t * k + j];
-      rows[j] = pair_row[(size_t)t * k + j];
+      wts[j] = a.topk_w[(size_t)t * k + j];
+      rows[j] = a.pair_row[(size_t)t * k + j];
     }
   }
+  const bool per_tile = MAXP > 2;
+  const int ct = per_tile ? c / a.part_cols : 0;
+#pragma unroll
+  for (int j = 0; j < kMaxTopk; ++j)
+    if (j < k)
+      np[j] = per_tile ? a.d_parts[(size_t)(rows[j] / a.part_rows) * a.part_ncol + ct] : a.ksplit;
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j0 = 0; j0 < kMaxTopk; j0 += 4) {
     if (j0 >= k) break;
-    f32x4 d0[4], d1[4];
+    f32x4 d[4][MAXP];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const int j = j0 + jj;
-      d0[jj] = zero;
-      d1[jj] = zero;
-      if (j < k) {
-        const size_t off = (size_t)rows[j] * h + c;
-        d0[jj] = *reinterpret_cast<const f32x4*>(D + off);
-        if (ksplit > 1) d1[jj] = *reinterpret_cast<const f32x4*>(D + split_stride + off);
+      const size_t off = j < k ? (size_t)rows[j] * h + c : 0;
+#pragma unroll
+      for (int p = 0; p < MAXP; ++p) {
+        d[jj][p] = zero;
+        if (j < k && p < np[j]) d[jj][p] = *reinterpret_cast<const f32x4*>(a.D + p * a.split_stride + off);
       }
     }
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const int j = j0 + jj;
       if (j < k) {
-        f32x4 d = d0[jj];
-        if (ksplit > 1) d += d1[jj];  // split order
+        f32x4 dv = d[jj][0];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(wts[j], d[v], acc[v]);
+        for (int p = 1; p < MAXP; ++p)
+          if (p < np[j]) dv += d[jj][p];  // part order
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(wts[j], dv[v], acc[v]);
       }
     }
     __builtin_amdgcn_sched_barrier(0);  // (keeps the next slots' loads, and registers, apart)
   }
   u32x2 packed = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-  *reinterpret_cast<u32x2*>(y + (size_t)t * h + c) = packed;
+  *reinterpret_cast<u32x2*>(a.y + (size_t)t * h + c) = packed;
 }
 
-hipError_t launch_combine(const float* D, int ksplit, int64_t split_stride, const int* pair_row,
-                          const float* topk_w, int T, int k, int h, uint16_t* y,
-                          hipStream_t stream) {
-  const int64_t n = (int64_t)T * (h / 4);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
+  const int64_t n = (int64_t)a.T * (a.h / 4);
   if (n <= 0) return hipSuccess;
-  if (ksplit < 1 || ksplit > 2 || k < 1 || k > kMaxTopk) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, D,
-                     ksplit, split_stride, pair_row, topk_w, T, k, h, y);
+  if (a.ksplit < 1 || a.ksplit > kMaxParts || a.k < 1 || a.k > kMaxTopk) return hipErrorInvalidValue;
+  if (a.d_parts && (a.part_rows <= 0 || a.part_cols <= 0 || a.part_cols % 4 != 0))
+    return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (a.d_parts)
+    hipLaunchKernelGGL(combine_kernel<kMaxParts>, grid, dim3(256), 0, stream, a);
+  else if (a.ksplit == 1)
+    hipLaunchKernelGGL(combine_kernel<1>, grid, dim3(256), 0, stream, a);
+  else if (a.ksplit == 2)
+    hipLaunchKernelGGL(combine_kernel<2>, grid, dim3(256), 0, stream, a);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

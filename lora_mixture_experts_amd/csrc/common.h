@@ -16,6 +16,7 @@ constexpr int kWave = 64;
 constexpr int kMaxTopk = 16;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxSplit = 8;  // split-K parts of the LoRA shrink
+constexpr int kMaxParts = 4;  // K parts of the down GEMM's output D
 
 // ------------------------------------------------------------------------------------------
 // bf16 <-> f32. A bf16 is the upper half of an IEEE binary32.
@@ -99,8 +100,8 @@ __device__ __forceinline__ int sanitize_adapter(int a, int nA) {
 // ------------------------------------------------------------------------------------------
 struct MoeLoraLayout {
   size_t topk_ids, topk_w, tok_flags, flags, sorted, expert_off, n_blocks, block_expert, block_seg,
-      pair_row, sorted_ad, sub_row0, n_sub, seg_table, n_seg, z1, z2, zhl, act, dpair, align_lists,
-      logits;
+      pair_row, sorted_ad, sub_row0, n_sub, seg_table, n_seg, z1, z2, zhl, act, dpair, d_parts,
+      align_lists, logits;
   size_t total;
   int64_t cap;     // rows of the sorted layout at the largest row-block size
   int max_bm;      // largest row-block size any path uses

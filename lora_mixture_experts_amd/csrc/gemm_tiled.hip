@@ -334,14 +334,35 @@ __global__ __launch_bounds__(64 * NW, 1) void tiled_gemm_kernel(GemmArgs a, int 
   const int sub = a.layout_bm / BM;
   const int nblk = sub > 1 ? *a.n_sub : *a.n_blocks;
   const int tiles = nblk * n_tiles_n;
-  const int live = tiles * (GATEUP ? 1 : a.ksplit);
-  const int per_xcd = (live + 7) >> 3;
   const int hw = blockIdx.x;
   const int slot = hw >> 3;
-  const int tk = (hw & 7) * per_xcd + slot;
-  if (slot >= per_xcd || tk >= live) return;
-  const int ks = GATEUP ? 0 : tk / tiles;        // K split
-  const int t = tk - ks * tiles;
+  int ks, t, nparts;  // K part of this workgroup, its tile, the tile's parts
+  if (!GATEUP && a.tail_split > 1) {
+    // Tail split: the tiles that fill whole rounds of n_cu resident workgroups run undivided
+    // (each XCD an equal contiguous range, as below); the tiles of the last, partial round split
+    // K in tail_split parts, dealt to the XCDs in turn, so that round is as full as the others.
+    const int full = tiles / a.n_cu * a.n_cu, tail = tiles - full;
+    const int fpx = full >> 3;
+    if (slot < fpx) {
+      t = (hw & 7) * fpx + slot;
+      ks = 0;
+      nparts = 1;
+    } else {
+      const int v = (slot - fpx) * 8 + (hw & 7);
+      if (v >= tail * a.tail_split) return;
+      t = full + v / a.tail_split;
+      ks = v % a.tail_split;
+      nparts = a.tail_split;
+    }
+  } else {
+    const int live = tiles * (GATEUP ? 1 : a.ksplit);
+    const int per_xcd = (live + 7) >> 3;
+    const int tk = (hw & 7) * per_xcd + slot;
+    if (slot >= per_xcd || tk >= live) return;
+    ks = GATEUP ? 0 : tk / tiles;  // K split
+    t = tk - ks * tiles;
+    nparts = GATEUP ? 1 : a.ksplit;
+  }
   constexpr int GR = 4, GC = 4;                   // row blocks and column tiles per group
   const int cg = t / (nblk * GC);                 // column group (all but the last GC wide)
   const int cols = min(GC, n_tiles_n - cg * GC);
@@ -355,7 +376,9 @@ __global__ __launch_bounds__(64 * NW, 1) void tiled_gemm_kernel(GemmArgs a, int 
   const int blk = row0 / a.layout_bm;  // its row block of the layout
   const int e = a.block_expert[blk];
   const int K = a.K;
-  const int kspan = GATEUP ? K : K / a.ksplit;  // this split's K range: [ks * kspan, +kspan)
+  const int kspan = K / nparts;  // this part's K range: [ks * kspan, +kspan)
+  // the combine learns from d_parts how many parts of D hold this tile
+  if (!GATEUP && ks == 0 && a.d_parts) a.d_parts[(size_t)rt * n_tiles_n + ntile] = nparts;
   const uint32_t kbyte0 = (uint32_t)ks * kspan * 2;
   const size_t N = (size_t)a.N;
   const size_t w_rows = GATEUP ? 2 * N : N;  // weight rows of one expert
@@ -539,8 +562,11 @@ hipError_t launch_tiled(const TiledConfig& c, bool gateup, const GemmArgs& a, hi
                         bool fp8) {
   const int cols = gateup ? 2 * a.N : a.N;
   if (cols % c.bn != 0) return hipErrorInvalidValue;
-  const int splits = gateup ? 1 : a.ksplit;
-  if (splits < 1 || (a.K / splits) % c.bk != 0 || a.K % splits != 0) return hipErrorInvalidValue;
+  const int splits = gateup ? 1 : (a.tail_split > 1 ? a.tail_split : a.ksplit);
+  if (splits < 1 || splits > kMaxParts || (a.K / splits) % c.bk != 0 || a.K % splits != 0)
+    return hipErrorInvalidValue;
+  if (!gateup && a.tail_split > 1 && (a.n_cu <= 0 || a.n_cu % 8 != 0 || !a.d_parts))
+    return hipErrorInvalidValue;
   const int n_tiles_n = cols / c.bn;
   // one workgroup per (row block, column tile, K split) for the largest row-block count,
   // rounded up to a multiple of the 8 XCDs

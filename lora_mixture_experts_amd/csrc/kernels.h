@@ -107,9 +107,13 @@ struct GemmArgs {
   int K;  // reduction length
   int N;  // gate_up: I (act columns); down: h
   uint16_t* act_out;  // gate_up: [cap][I]
-  float* d_out;       // down: [ksplit][cap][h] partial sums, rows in sorted order
-  int ksplit;         // down: K splits (gridDim.z); gate_up: 1
+  float* d_out;       // down: [parts][cap][h] partial sums, rows in sorted order
+  int ksplit;         // down: K splits of every tile; gate_up: 1
   int64_t d_split_stride;
+  int tail_split;     // tiled down, > 1: the tiles of the last partial round of n_cu workgroups
+                      // split K in tail_split parts (the others none); 0: ksplit for all
+  int n_cu;           // workgroups resident at once (one tiled tile per CU), a multiple of 8
+  int* d_parts;       // tiled down: [row tile][column tile] K parts written (combine reads it)
   int n_blocks_max;   // row blocks the grid is sized for (>= *n_blocks)
   int layout_bm;      // tiled: row-block size of the sorted layout (a multiple of the tile's BM;
                       // a larger one is walked in the sub-tiles of the align's sub-tile list)
@@ -165,8 +169,19 @@ hipError_t launch_skinny(const SkinnyConfig& c, bool gateup, const GemmArgs& a, 
 hipError_t launch_tiled(const TiledConfig& c, bool gateup, const GemmArgs& a, hipStream_t stream,
                         bool fp8 = false);
 hipError_t launch_sgmv_expand(const SgmvArgs& a, int max_blocks, hipStream_t stream);
-hipError_t launch_combine(const float* D, int ksplit, int64_t split_stride, const int* pair_row,
-                          const float* topk_w, int T, int k, int h, uint16_t* y,
-                          hipStream_t stream);
+// D parts: d_parts == nullptr: ksplit parts for every row; else d_parts[(row / part_rows) *
+// part_ncol + col / part_cols] parts (1 to 4) for the tile holding (row, col).
+struct CombineArgs {
+  const float* D;
+  int ksplit;
+  int64_t split_stride;
+  const int* d_parts;
+  int part_rows, part_cols, part_ncol;
+  const int* pair_row;
+  const float* topk_w;
+  int T, k, h;
+  uint16_t* y;
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 
 }  // namespace moelora

@@ -35,9 +35,6 @@ hipError_t launch_tiled(const TiledConfig&, bool, const GemmArgs&, hipStream_t, 
   reached("tiled");
 }
 hipError_t launch_sgmv_expand(const SgmvArgs&, int, hipStream_t) { reached("sgmv_expand"); }
-hipError_t launch_combine(const float*, int, int64_t, const int*, const float*, int, int, int,
-                          uint16_t*, hipStream_t) {
-  reached("combine");
-}
+hipError_t launch_combine(const CombineArgs&, hipStream_t) { reached("combine"); }
 
 }  // namespace moelora
