@@ -928,8 +928,23 @@ int moe_lora_sgmv(const void* x, const void* A, const void* B, const int32_t* ad
   al.n_sub = nullptr;
   al.sub_m = 64;
   al.g_lists = (int*)(ws + L.align_lists);
-  const size_t lds = align_lds_plan(T, 1, 1, nA, &al);
-  if (launch_align(al, lds, stream) != hipSuccess) return MOELORA_EHIP;
+  if (T <= kSgmvSortMaxTokens && nA <= kSgmvSortMaxAdapters) {
+    // up to 1024 tokens and adapters: one pass of a one-workgroup sort of the tokens with an
+    // adapter (the shrink and expand read the rows, their adapters and the block count only)
+    SgmvSortArgs so;
+    so.adapter_ids = adapter_ids;
+    so.T = T;
+    so.nA = nA;
+    so.sorted_pairs = al.sorted_pairs;
+    so.sorted_ad = al.sorted_ad;
+    so.block_expert = al.block_expert;
+    so.n_blocks = al.n_blocks;
+    so.flags = al.flags;
+    if (launch_sgmv_sort(so, stream) != hipSuccess) return MOELORA_EHIP;
+  } else {
+    const size_t lds = align_lds_plan(T, 1, 1, nA, &al);
+    if (launch_align(al, lds, stream) != hipSuccess) return MOELORA_EHIP;
+  }
 
   // shrink z = x A_a^T over 16-row tiles, split over K
   ShrinkArgs sh;

@@ -59,6 +59,20 @@ inline size_t align_list_ints(int T, int k, int E, int nA) {
   return 3 * (size_t)T * k + 2 * (size_t)align_seg_cap(T, k, E, nA);
 }
 
+// Adapter segments of a dense multi-LoRA batch (sgmv_sort_kernel): the sorted layout of the
+// tokens that carry an adapter, by (adapter, token), in 16-row blocks.
+constexpr int kSgmvSortMaxTokens = 1024;
+constexpr int kSgmvSortMaxAdapters = 1024;
+struct SgmvSortArgs {
+  const int* adapter_ids;  // [T]
+  int T, nA;
+  int* sorted_pairs;  // [>= round_up(T, 16)]: token of each row, -1 for padding
+  int* sorted_ad;     // its adapter, -1 for padding
+  int* block_expert;  // [blocks]: 0
+  int* n_blocks;      // [1]
+  int* flags;         // [1]: MOELORA_FLAG_ADAPTER_RANGE when an id is out of range
+};
+
 // LoRA shrink z = X A^T for the rows of the sorted layout.
 struct ShrinkArgs {
   const uint16_t* X;  // gather: x [T][K]; otherwise act [cap][K]
@@ -157,6 +171,7 @@ struct SkinnyConfig {
 hipError_t launch_route(const float* logits, int T, int E, int k, int* topk_ids, float* topk_w,
                         int* tok_flags, hipStream_t stream);
 hipError_t launch_align(const AlignArgs& a, size_t dyn_lds, hipStream_t stream);
+hipError_t launch_sgmv_sort(const SgmvSortArgs& a, hipStream_t stream);
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* W, int T, int K, int E,
                                 float* logits, hipStream_t stream);
 hipError_t launch_shrink(bool gather, const ShrinkArgs& a, int tiles, hipStream_t stream);

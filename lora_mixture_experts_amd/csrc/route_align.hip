@@ -612,6 +612,88 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int* topk_ids,
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------------------------------
+// Adapter segments of a dense multi-LoRA batch (one projection, no experts) for up to 1024 tokens
+// and 1024 adapters: one workgroup, one token per thread. The tokens that carry an adapter are
+// sorted by (adapter, token): a token's rank among the equal adapters of earlier lanes of its
+// wavefront comes from a ballot match, the per-(adapter, wavefront) counts are scanned in
+// adapter-major order, and each token lands at its adapter's offset plus its rank. The layout
+// is padded to 16-row blocks with -1 (block -> expert 0). Tokens without an adapter, or with one
+// out of range (flagged), are left out: nothing of the multi-LoRA add applies to them.
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void sgmv_sort_kernel(SgmvSortArgs a) {
+  extern __shared__ int cnt[];  // [nA][16]: count, then offset, of adapter x wavefront
+  __shared__ int s_red[72];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nA = a.nA, n_ent = nA * 16;
+  for (int i = tid; i < n_ent; i += 1024) cnt[i] = 0;
+  int ad = -1;
+  bool bad = false;
+  if (tid < a.T) {
+    ad = a.adapter_ids[tid];
+    if (ad < -1 || ad >= nA) {
+      bad = true;
+      ad = -1;
+    }
+  }
+  const bool member = ad >= 0;
+  int nbits = 1;
+  while ((1 << nbits) < nA) ++nbits;
+  const uint64_t eq = match_key(member, member ? ad : 0, nbits);
+  const int rank = (int)__popcll(eq & lanemask_lt());
+  const int any_bad = __syncthreads_or(bad);
+  if (member && rank == 0) cnt[ad * 16 + wave] = (int)__popcll(eq);
+  __syncthreads();
+  // exclusive scan of the entries in (adapter, wavefront) order, per = entries per thread
+  const int per = (n_ent + 1023) / 1024;
+  const int e0 = tid * per;
+  int local = 0;
+  for (int j = 0; j < per; ++j)
+    if (e0 + j < n_ent) local += cnt[e0 + j];
+  int ex, d0, total, d1;
+  block_excl_scan2(local, 0, ex, d0, total, d1, s_red);
+  for (int j = 0; j < per; ++j)
+    if (e0 + j < n_ent) {
+      const int v = cnt[e0 + j];
+      cnt[e0 + j] = ex;
+      ex += v;
+    }
+  __syncthreads();
+  if (member) {
+    const int pos = cnt[ad * 16 + wave] + rank;
+    a.sorted_pairs[pos] = tid;
+    a.sorted_ad[pos] = ad;
+  }
+  const int padded = round_up_i(total, 16);
+  for (int q = total + tid; q < padded; q += 1024) {
+    a.sorted_pairs[q] = -1;
+    a.sorted_ad[q] = -1;
+  }
+  for (int b = tid; b < padded / 16; b += 1024) a.block_expert[b] = 0;
+  if (tid == 0) {
+    *a.n_blocks = padded / 16;
+    *a.flags = any_bad ? 2 : 0;
+  }
+}
+
+hipError_t launch_sgmv_sort(const SgmvSortArgs& a, hipStream_t stream) {
+  if (a.T < 0 || a.T > kSgmvSortMaxTokens || a.nA < 1 || a.nA > kSgmvSortMaxAdapters)
+    return hipErrorInvalidValue;
+  static bool attr_set[64] = {};
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev >= 0 && dev < 64 && !attr_set[dev]) {
+    err = hipFuncSetAttribute((const void*)sgmv_sort_kernel,
+                              hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)sizeof(int) * 16 * kSgmvSortMaxAdapters);
+    if (err != hipSuccess) return err;
+    attr_set[dev] = true;
+  }
+  hipLaunchKernelGGL(sgmv_sort_kernel, dim3(1), dim3(1024), sizeof(int) * 16 * a.nA, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_align(const AlignArgs& a, size_t dyn_lds, hipStream_t stream) {
   static bool attr_set[64] = {};
   int dev = 0;

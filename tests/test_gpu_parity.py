@@ -463,6 +463,10 @@ SGMV_CASES = [
     (64, 256, 128, 1, 16, "same"),
     (700, 256, 256, 700, 16, "distinct"),
     (2000, 128, 64, 8, 8, "runs"),
+    # the one-workgroup adapter sort's limits (1024 tokens, 1024 adapters) and just past them
+    (1024, 256, 128, 1024, 8, "distinct"),
+    (1025, 128, 64, 5, 16, "uniform"),
+    (1000, 128, 64, 1100, 8, "uniform"),
 ]
 
 
