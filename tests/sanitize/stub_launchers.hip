@@ -36,5 +36,6 @@ hipError_t launch_tiled(const TiledConfig&, bool, const GemmArgs&, hipStream_t, 
 }
 hipError_t launch_sgmv_expand(const SgmvArgs&, int, hipStream_t) { reached("sgmv_expand"); }
 hipError_t launch_combine(const CombineArgs&, hipStream_t) { reached("combine"); }
+hipError_t launch_sgmv_sort(const SgmvSortArgs&, hipStream_t) { reached("sgmv_sort"); }
 
 }  // namespace moelora
