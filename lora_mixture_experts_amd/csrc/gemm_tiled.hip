@@ -30,9 +30,7 @@
 namespace moelora {
 
 // Store of a finished tile at its rows of the sorted layout: SiLU-and-mul (gate_up, into act as
-// bf16) or the plain fp32 store (down, into the K split's part of D). Padding rows hold zeros
-// (their token rows were loaded as zeros and carry no adapter) and are stored like the others,
-// so the store needs no per-row lookup. Lane l holds rows 8*(v/4) + 4*(l/32) + (v%4) of each
+// bf16) or the plain fp32 store (down, into the K split's part of D), real rows only. Lane l holds rows 8*(v/4) + 4*(l/32) + (v%4) of each
 // 32-row group and column (l % 32) of each 32-column fragment, so it goes through LDS (the main
 // loop's stages are free by then): 16 rows at a time, each wavefront writes its values into its
 // own region, row-major (rows padded so that the two lane halves, 4 rows apart, hit different
@@ -52,6 +50,16 @@ __device__ __forceinline__ void tiled_store(const GemmArgs& a, f32x16 (&acc)[FM]
   const int fr = lane & 31, fg = lane >> 5;
   char* base = reinterpret_cast<char*>(lds) + wave * (PR * STRIDE);
   const size_t N = (size_t)a.N;
+  // rows of this wavefront past the expert's last real row are padding: nothing reads them (the
+  // down GEMM, the shrink and the combine take real rows only), so they are not stored. The
+  // padding of an expert's block is a suffix: its start is the count of real rows.
+  int wave_real = 0;
+#pragma unroll
+  for (int i = 0; i < (WM + 63) / 64; ++i) {
+    const int rr = i * 64 + lane;
+    const bool real = rr < WM && a.sorted_pairs[(size_t)row0 + wm * WM + rr] >= 0;
+    wave_real += (int)__popcll(__ballot(real));
+  }
   const size_t col0 =
       GATEUP ? (size_t)ntile * (BN / 2) + wn * (WN / 2) : (size_t)ntile * BN + wn * WN;
 #pragma unroll
@@ -84,6 +92,7 @@ __device__ __forceinline__ void tiled_store(const GemmArgs& a, f32x16 (&acc)[FM]
         const int r = idx / CPRW, c = idx % CPRW;
         const u32x4 val = *reinterpret_cast<const u32x4*>(base + r * STRIDE + c * 16);
         const size_t srow = (size_t)row0 + wm * WM + i * 32 + 16 * h + r;
+        if (i * 32 + 16 * h + r >= wave_real) continue;
         if (GATEUP)
           *reinterpret_cast<u32x4*>(a.act_out + srow * N + col0 + c * 8) = val;
         else
