@@ -24,7 +24,7 @@ namespace moelora {
 
 namespace {
 constexpr int kSubRows = 64;  // rows of the sorted layout per workgroup
-using ShrinkPipe = TilePipe<kSubRows, 64, 32, 32, 64, 3, true, 4>;
+using ShrinkPipe = TilePipe<kSubRows, 64, 32, 32, 64, 3, false, 4>;
 }  // namespace
 
 template <bool GATHER>

@@ -63,7 +63,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 // converted to bf16 after the LDS read. The k order inside a stage then differs from the bf16
 // tile's (lane group fg takes k 32 fg + 8 j .. + 7 in sub-step j, on both operands), so that one
 // 16-byte read of a code row serves two sub-steps.
-template <int BM, int BN, int WM, int WN, int BK, int NST, bool SPREAD = true, int NWAVES = 4,
+//
+// ILV: the fragment reads of the next sub-step are issued between the MFMAs of the current one
+// (one read after each MFMA) instead of ahead of them.
+template <int BM, int BN, int WM, int WN, int BK, int NST, bool ILV = false, int NWAVES = 4,
           bool W8 = false>
 struct TilePipe {
   static_assert(BK == 32 || BK == 64, "K step of 32 or 64");
@@ -248,7 +251,7 @@ struct TilePipe {
         const u32x4* bc = (j & 1) ? bf1 : bf0;
         if (j < SUB - 1) {
           read_frags(stage, j + 1, an, bn);
-          __builtin_amdgcn_sched_barrier(0);
+          if (!ILV) __builtin_amdgcn_sched_barrier(0);
           mfmas_interleaved(ac, bc, true);
           __builtin_amdgcn_sched_barrier(0);
           continue;
