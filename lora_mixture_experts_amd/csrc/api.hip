@@ -578,9 +578,21 @@ int enqueue_forward(const ForwardPlan& pl, const MoeLoraLayout& L, const void* x
   sh.zpart = z1;
   sh.cap = L.cap;
   sh.after64 = pl.shrink64 ? 1 : 0;
-  if (pl.shrink64 && launch_shrink_tiled(true, sh, pl.n_sub_max, stream) != hipSuccess)
-    return MOELORA_EHIP;
-  if (launch_shrink(true, sh, pl.tiles16, stream) != hipSuccess) return MOELORA_EHIP;
+  // weight-streaming path (a few rows per expert, runs of a row or two): one wavefront per
+  // adapter segment and K split (MOELORA_SEGSHRINK=0: the 16-row shrink, for experiments)
+  static int seg_env = -1;
+  if (seg_env < 0) {
+    const char* env = getenv("MOELORA_SEGSHRINK");
+    seg_env = env ? atoi(env) : 1;
+  }
+  const bool seg_shrink = !path.tiled && seg_env != 0;
+  auto shrink = [&](bool gather) {
+    if (pl.shrink64 && launch_shrink_tiled(gather, sh, pl.n_sub_max, stream) != hipSuccess)
+      return false;
+    return (seg_shrink ? launch_shrink_seg(gather, sh, (int)pl.P, stream)
+                       : launch_shrink(gather, sh, pl.tiles16, stream)) == hipSuccess;
+  };
+  if (!shrink(true)) return MOELORA_EHIP;
   uint16_t* zhl = path.tiled ? (uint16_t*)(ws + L.zhl) : nullptr;
   // the skinny GEMMs add the split parts themselves (one launch fewer per projection); the
   // tiled GEMMs take z as bf16 high and low planes, made by zfinal
@@ -616,9 +628,7 @@ int enqueue_forward(const ForwardPlan& pl, const MoeLoraLayout& L, const void* x
   sh.K = I;
   sh.S = pl.s2;
   sh.zpart = z2;
-  if (pl.shrink64 && launch_shrink_tiled(false, sh, pl.n_sub_max, stream) != hipSuccess)
-    return MOELORA_EHIP;
-  if (launch_shrink(false, sh, pl.tiles16, stream) != hipSuccess) return MOELORA_EHIP;
+  if (!shrink(false)) return MOELORA_EHIP;
   if (path.tiled &&
       launch_zfinal(z2, pl.s2, L.cap, r, n_blocks, bm, max_rows, zhl, stream) != hipSuccess)
     return MOELORA_EHIP;

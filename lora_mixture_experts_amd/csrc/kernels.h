@@ -175,6 +175,9 @@ hipError_t launch_sgmv_sort(const SgmvSortArgs& a, hipStream_t stream);
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* W, int T, int K, int E,
                                 float* logits, hipStream_t stream);
 hipError_t launch_shrink(bool gather, const ShrinkArgs& a, int tiles, hipStream_t stream);
+// one wavefront per (adapter segment, K split), for up to max_segments segments (short runs)
+hipError_t launch_shrink_seg(bool gather, const ShrinkArgs& a, int max_segments,
+                             hipStream_t stream);
 hipError_t launch_shrink_tiled(bool gather, const ShrinkArgs& a, int n_sub_max,
                                hipStream_t stream);
 hipError_t launch_zfinal(const float* zpart, int S, int64_t cap, int r, const int* n_blocks,

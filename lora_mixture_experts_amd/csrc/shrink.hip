@@ -204,6 +204,128 @@ __global__ __launch_bounds__(256) void lora_shrink_kernel(ShrinkArgs a) {
   }
 }
 
+// Segment shrink, for layouts whose adapter runs are short (a few rows per expert, many
+// adapters): one wavefront per (adapter segment, K split), where the 16-row shrink walks the
+// runs of a tile one after another. The segment table gives the run (expert, adapter, first
+// row, rows), so the A loads of the split are issued as soon as the table entry has arrived,
+// next to the row ids; a run's rows are taken 16 at a time (one 16 x r x K product each, rows
+// past the run load zeros). Each wavefront keeps two 128-wide K steps of loads in flight (the
+// same step order and split boundaries as the 16-row shrink) and writes the run's rows of
+// zpart[s]; the wavefronts of a workgroup are independent (no LDS, no barrier).
+template <bool GATHER, int NCT>
+__global__ __launch_bounds__(256) void lora_shrink_seg_kernel(ShrinkArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int task = blockIdx.x * 4 + wave;
+  const int j = task / a.S, s = task - j * a.S;  // the S splits of a segment on neighbours
+  if (j >= *a.n_seg) return;
+  const u32x4 sg = *reinterpret_cast<const u32x4*>(a.seg_table + 4 * (size_t)j);
+  const int e = __builtin_amdgcn_readfirstlane((int)sg[0]);
+  const int ad = __builtin_amdgcn_readfirstlane(sanitize_adapter((int)sg[1], a.nA));
+  const int st = __builtin_amdgcn_readfirstlane((int)sg[2]);
+  const int cnt = __builtin_amdgcn_readfirstlane((int)sg[3]);
+  if (ad < 0 || cnt <= 0) return;
+  const int K = a.K, r = a.r;
+  const int nks = K / 128;
+  const int per = (nks + a.S - 1) / a.S;
+  const int ks0 = min(nks, s * per), ks1 = min(nks, ks0 + per);
+  const int n = ks1 - ks0;
+  if (n <= 0) return;
+  const int m = lane & 15, kq = lane >> 4;
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.X, a.x_bytes);
+  const __amdgpu_buffer_rsrc_t ar =
+      make_rsrc(a.Aw + ((size_t)ad * a.E + e) * (size_t)r * K, (uint32_t)((size_t)r * K * 2));
+  uint32_t ao[NCT];
+#pragma unroll
+  for (int c = 0; c < NCT; ++c) {
+    const int q = c * 16 + m;
+    ao[c] = q < r ? (uint32_t)((size_t)q * K * 2) : kOutOfRange;
+  }
+  for (int c0 = 0; c0 < cnt; c0 += 16) {
+    const int p = c0 + m < cnt ? a.sorted_pairs[st + c0 + m] : -1;
+    const uint32_t xo =
+        p < 0 ? kOutOfRange
+              : (uint32_t)((GATHER ? (size_t)(p / a.k) : (size_t)(st + c0 + m)) * K * 2);
+    f32x4 acc[NCT];
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x4 xa0[4], bw0[NCT][4], xa1[4], bw1[NCT][4];
+    // step ks covers k in [128 ks, 128 ks + 128); MFMA jj takes k = 32 jj + 8 kq .. + 8
+    auto load_a = [&](int ks, u32x4 (*bw)[4]) {
+      const uint32_t kb = (uint32_t)(ks * 128 + kq * 8) * 2;
+#pragma unroll
+      for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) bw[c][jj] = bufld16(ar, ao[c] + kb + 64u * jj);
+    };
+    auto load_x = [&](int ks, u32x4* xa) {
+      const uint32_t kb = (uint32_t)(ks * 128 + kq * 8) * 2;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) xa[jj] = bufld16(xr, xo + kb + 64u * jj);
+    };
+    auto mma = [&](const u32x4* xa, const u32x4 (*bw)[4]) {
+#pragma unroll
+      for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) acc[c] = mfma16(xa[jj], bw[c][jj], acc[c]);
+    };
+    // steps in pairs with ping-pong register sets; every load is unconditional (past the end it
+    // re-reads the last step) and no branch encloses an MFMA
+    load_a(ks0, bw0);
+    load_x(ks0, xa0);
+    int i = 0;
+    for (; i + 2 <= n; i += 2) {
+      load_a(ks0 + i + 1, bw1);
+      load_x(ks0 + i + 1, xa1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(xa0, bw0);
+      __builtin_amdgcn_sched_barrier(0);
+      const int nx = min(ks0 + i + 2, ks1 - 1);
+      load_a(nx, bw0);
+      load_x(nx, xa0);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(xa1, bw1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (i < n) mma(xa0, bw0);
+    // acc[c] holds rows 4 kq + v of the chunk, column q = 16 c + m
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) {
+      const int q = c * 16 + m;
+      if (q < r) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int row = c0 + 4 * kq + v;
+          if (row < cnt) a.zpart[((size_t)s * a.cap + st + row) * r + q] = acc[c][v];
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_shrink_seg(bool gather, const ShrinkArgs& a, int max_segments,
+                             hipStream_t stream) {
+  if (max_segments <= 0) return hipSuccess;
+  if (a.S < 1 || a.S > kMaxSplit || a.K % 128 != 0) return hipErrorInvalidValue;
+  dim3 grid((unsigned)(((int64_t)max_segments * a.S + 3) / 4));
+#define MOELORA_SHRINK_SEG(NCT_)                                                             \
+  if (gather)                                                                                \
+    hipLaunchKernelGGL((lora_shrink_seg_kernel<true, NCT_>), grid, dim3(256), 0, stream, a);  \
+  else                                                                                       \
+    hipLaunchKernelGGL((lora_shrink_seg_kernel<false, NCT_>), grid, dim3(256), 0, stream, a);
+  if (a.r <= 16) {
+    MOELORA_SHRINK_SEG(1)
+  } else if (a.r == 32) {
+    MOELORA_SHRINK_SEG(2)
+  } else if (a.r == 64) {
+    MOELORA_SHRINK_SEG(4)
+  } else {
+    return hipErrorInvalidValue;
+  }
+#undef MOELORA_SHRINK_SEG
+  return hipGetLastError();
+}
+
 // z for the LDS-tiled GEMM epilogues: the S split parts of each row added in split order, once
 // (every workgroup reading a row's z then loads it once instead of S times), and split into bf16
 // high and low parts (hi = bf16(z), lo = bf16(z - hi)), written as two planes [cap][r] that

@@ -37,5 +37,6 @@ hipError_t launch_tiled(const TiledConfig&, bool, const GemmArgs&, hipStream_t, 
 hipError_t launch_sgmv_expand(const SgmvArgs&, int, hipStream_t) { reached("sgmv_expand"); }
 hipError_t launch_combine(const CombineArgs&, hipStream_t) { reached("combine"); }
 hipError_t launch_sgmv_sort(const SgmvSortArgs&, hipStream_t) { reached("sgmv_sort"); }
+hipError_t launch_shrink_seg(bool, const ShrinkArgs&, int, hipStream_t) { reached("shrink_seg"); }
 
 }  // namespace moelora
