@@ -578,14 +578,16 @@ int enqueue_forward(const ForwardPlan& pl, const MoeLoraLayout& L, const void* x
   sh.zpart = z1;
   sh.cap = L.cap;
   sh.after64 = pl.shrink64 ? 1 : 0;
-  // weight-streaming path (a few rows per expert, runs of a row or two): one wavefront per
-  // adapter segment and K split (MOELORA_SEGSHRINK=0: the 16-row shrink, for experiments)
+  // rows the 64-row shrink leaves (all rows on the weight-streaming path, where runs are a row
+  // or two): one wavefront per adapter segment and K split (MOELORA_SEGSHRINK=0: the 16-row
+  // shrink, for experiments; measured: fine-grained layer 0.483 -> 0.453 ms, one adapter per
+  // token 1.85 -> 1.81 ms)
   static int seg_env = -1;
   if (seg_env < 0) {
     const char* env = getenv("MOELORA_SEGSHRINK");
     seg_env = env ? atoi(env) : 1;
   }
-  const bool seg_shrink = !path.tiled && seg_env != 0;
+  const bool seg_shrink = seg_env != 0;
   auto shrink = [&](bool gather) {
     if (pl.shrink64 && launch_shrink_tiled(gather, sh, pl.n_sub_max, stream) != hipSuccess)
       return false;

@@ -206,7 +206,8 @@ __global__ __launch_bounds__(256) void lora_shrink_kernel(ShrinkArgs a) {
 
 // Segment shrink, for layouts whose adapter runs are short (a few rows per expert, many
 // adapters): one wavefront per (adapter segment, K split), where the 16-row shrink walks the
-// runs of a tile one after another. The segment table gives the run (expert, adapter, first
+// runs of a tile one after another. After the 64-row shrink (after64) it takes only the rows
+// of the 64-row sub-blocks that one leaves (more than kShrink64MaxRuns runs). The segment table gives the run (expert, adapter, first
 // row, rows), so the A loads of the split are issued as soon as the table entry has arrived,
 // next to the row ids; a run's rows are taken 16 at a time (one 16 x r x K product each, rows
 // past the run load zeros). Each wavefront keeps two 128-wide K steps of loads in flight (the
@@ -241,8 +242,27 @@ __global__ __launch_bounds__(256) void lora_shrink_seg_kernel(ShrinkArgs a) {
     const int q = c * 16 + m;
     ao[c] = q < r ? (uint32_t)((size_t)q * K * 2) : kOutOfRange;
   }
+  const int nseg = *a.n_seg;
   for (int c0 = 0; c0 < cnt; c0 += 16) {
-    const int p = c0 + m < cnt ? a.sorted_pairs[st + c0 + m] : -1;
+    // take: bit i for row st + c0 + i. After the 64-row shrink, the rows of the 64-row
+    // sub-blocks it took (few runs) are not this kernel's.
+    uint32_t take = 0xffffu;
+    if (a.after64) {
+      const int r0 = st + c0, r1 = st + min(cnt, c0 + 16) - 1;
+      const int sb0 = r0 & ~63, sb1 = r1 & ~63;
+      const bool many0 = count_runs64(a.block_seg, a.seg_table, nseg, a.nA, sb0 / a.bm, sb0,
+                                      kShrink64MaxRuns) > kShrink64MaxRuns;
+      const bool many1 = sb1 == sb0 ? many0
+                                    : count_runs64(a.block_seg, a.seg_table, nseg, a.nA,
+                                                   sb1 / a.bm, sb1, kShrink64MaxRuns) >
+                                          kShrink64MaxRuns;
+      const int in0 = min(16, sb0 + 64 - r0);  // rows of the chunk in sub-block sb0
+      const uint32_t m0 = (1u << in0) - 1u;
+      take = (many0 ? m0 : 0u) | (many1 ? (0xffffu & ~m0) : 0u);
+      if (take == 0u) continue;
+    }
+    const bool mine = c0 + m < cnt && ((take >> m) & 1u);
+    const int p = mine ? a.sorted_pairs[st + c0 + m] : -1;
     const uint32_t xo =
         p < 0 ? kOutOfRange
               : (uint32_t)((GATHER ? (size_t)(p / a.k) : (size_t)(st + c0 + m)) * K * 2);
@@ -296,7 +316,8 @@ __global__ __launch_bounds__(256) void lora_shrink_seg_kernel(ShrinkArgs a) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int row = c0 + 4 * kq + v;
-          if (row < cnt) a.zpart[((size_t)s * a.cap + st + row) * r + q] = acc[c][v];
+          if (row < cnt && ((take >> (4 * kq + v)) & 1u))
+            a.zpart[((size_t)s * a.cap + st + row) * r + q] = acc[c][v];
         }
       }
     }
