@@ -206,13 +206,14 @@ __global__ __launch_bounds__(256) void lora_shrink_kernel(ShrinkArgs a) {
 
 // Segment shrink, for layouts whose adapter runs are short (a few rows per expert, many
 // adapters): one wavefront per (adapter segment, K split), where the 16-row shrink walks the
-// runs of a tile one after another. After the 64-row shrink (after64) it takes only the rows
-// of the 64-row sub-blocks that one leaves (more than kShrink64MaxRuns runs). The segment table gives the run (expert, adapter, first
+// runs of a tile one after another. The segment table gives the run (expert, adapter, first
 // row, rows), so the A loads of the split are issued as soon as the table entry has arrived,
 // next to the row ids; a run's rows are taken 16 at a time (one 16 x r x K product each, rows
 // past the run load zeros). Each wavefront keeps two 128-wide K steps of loads in flight (the
 // same step order and split boundaries as the 16-row shrink) and writes the run's rows of
-// zpart[s]; the wavefronts of a workgroup are independent (no LDS, no barrier).
+// zpart[s]; the wavefronts of a workgroup are independent (no LDS, no barrier). After the
+// 64-row shrink (after64) it takes only the rows of the 64-row sub-blocks that one leaves (more
+// than kShrink64MaxRuns runs), so every row is written by one of the two.
 template <bool GATHER, int NCT>
 __global__ __launch_bounds__(256) void lora_shrink_seg_kernel(ShrinkArgs a) {
   const int lane = threadIdx.x & 63;
