@@ -286,8 +286,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the layer runs on a single MI355X here; "
-              "multi-GPU (expert-parallel) runs are not part of this build", file=sys.stderr)
+        print("bench.py measures one GPU: the layer runs on a single MI355X; multi-GPU "
+              "(expert-parallel) runs are not implemented", file=sys.stderr)
         sys.exit(2)
 
     import torch
