@@ -39,6 +39,17 @@ __device__ __forceinline__ void lds_dma16(u32x4 rsrc, uint32_t voff, uint32_t so
                : "memory", "m0");
 }
 
+// As lds_dma16 with the non-temporal hint: for operands streamed through once (read by one
+// tile), so that they do not evict from L2 what other tiles of the same wave of workgroups
+// read again.
+__device__ __forceinline__ void lds_dma16_nt(u32x4 rsrc, uint32_t voff, uint32_t soff,
+                                             uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, %3 offen nt lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(lds_addr), "s"(soff)
+               : "memory", "m0");
+}
+
 // As lds_dma16 from a 64-bit global address per lane (any buffer size; no zero fill).
 __device__ __forceinline__ void lds_dma16_global(const void* addr, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
