@@ -196,8 +196,9 @@ def test_forward_all_adapters_off_and_on():
 
 
 def test_forward_tiled_mixed_run_lengths():
-    """Long adapter runs (64-row shrink) next to one adapter per token (16-row shrink) in the
-    same batch, on 256-row tiles: every sub-block is taken by exactly one of the two shrinks."""
+    """Long adapter runs (64-row shrink) next to one adapter per token (segment shrink) in the
+    same batch, on 256-row tiles: every 64-row sub-block is taken by exactly one of the two
+    shrinks, and a segment that crosses into a sub-block of long runs leaves its rows there."""
     w = Workload("tiled256_mixed", 2048, 256, 384, 4, 2, 40, 32, adapters="zipf_runs", run=128)
     _say("forward tiled256_mixed")
     inp = _small_inputs(w, 3, 10.0, no_adapter_every=0)
