@@ -354,8 +354,6 @@ bool moelora_make_layout(int T, int h, int I, int E, int nA, int r, int topk, in
   L->block_seg = take(4 * (size_t)(L->cap / 16 + 1));
   L->pair_row = take(4 * (size_t)P);
   L->sorted_ad = take(4 * (size_t)L->cap);
-  L->sub_row0 = take(4 * (size_t)(L->cap / 64 + E + 1));
-  L->n_sub = take(4);
   L->seg_table = take(16 * (size_t)P);
   L->n_seg = take(4);
   L->z1 = take(4 * (size_t)kMaxSplit * L->cap * r);
@@ -512,11 +510,6 @@ int enqueue_forward(const ForwardPlan& pl, const MoeLoraLayout& L, const void* x
   al.pair_row = pair_row;
   al.sorted_ad = sorted_ad;
   al.n_blocks = n_blocks;
-  // tiled GEMMs smaller than the layout's blocks walk its live 64-row sub-tiles
-  const bool subtiles = path.tiled && std::min(path.tc.bm, path.tc_dn.bm) < bm;
-  al.sub_row0 = subtiles ? (int*)(ws + L.sub_row0) : nullptr;
-  al.n_sub = subtiles ? (int*)(ws + L.n_sub) : nullptr;
-  al.sub_m = 64;
   al.g_lists = (int*)(ws + L.align_lists);
   const size_t lds = align_lds_plan(T, topk, E, nA, &al);
   if (launch_align(al, lds, stream) != hipSuccess) return MOELORA_EHIP;
@@ -559,8 +552,6 @@ int enqueue_forward(const ForwardPlan& pl, const MoeLoraLayout& L, const void* x
   g.d_out = dpair;
   g.n_blocks_max = pl.max_blocks;
   g.layout_bm = bm;
-  g.sub_row0 = al.sub_row0;
-  g.n_sub = al.n_sub;
   // MOELORA_LORA_EXT=0 keeps every tiled LoRA expand in the epilogue (experiments)
   static int lora_ext_env = -1;
   if (lora_ext_env < 0) {
@@ -941,9 +932,6 @@ int moe_lora_sgmv(const void* x, const void* A, const void* B, const int32_t* ad
   al.pair_row = nullptr;
   al.sorted_ad = (int*)(ws + L.sorted_ad);
   al.n_blocks = (int*)(ws + L.n_blocks);
-  al.sub_row0 = nullptr;
-  al.n_sub = nullptr;
-  al.sub_m = 64;
   al.g_lists = (int*)(ws + L.align_lists);
   if (T <= kSgmvSortMaxTokens && nA <= kSgmvSortMaxAdapters) {
     // up to 1024 tokens and adapters: one pass of a one-workgroup sort of the tokens with an
@@ -1055,9 +1043,6 @@ int moe_lora_route_align(const float* router_logits, const int32_t* adapter_ids,
   al.pair_row = nullptr;
   al.sorted_ad = nullptr;
   al.n_blocks = nullptr;
-  al.sub_row0 = nullptr;
-  al.n_sub = nullptr;
-  al.sub_m = 64;
   al.g_lists = (int*)(ws + L.align_lists);
   const size_t lds = align_lds_plan(d->T, topk, d->n_experts, d->n_adapters, &al);
   if (launch_align(al, lds, stream) != hipSuccess) return MOELORA_EHIP;

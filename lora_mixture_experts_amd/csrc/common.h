@@ -100,7 +100,7 @@ __device__ __forceinline__ int sanitize_adapter(int a, int nA) {
 // ------------------------------------------------------------------------------------------
 struct MoeLoraLayout {
   size_t topk_ids, topk_w, tok_flags, flags, sorted, expert_off, n_blocks, block_expert, block_seg,
-      pair_row, sorted_ad, sub_row0, n_sub, seg_table, n_seg, z1, z2, zhl, act, dpair, d_parts,
+      pair_row, sorted_ad, seg_table, n_seg, z1, z2, zhl, act, dpair, d_parts,
       align_lists, logits;
   size_t total;
   int64_t cap;     // rows of the sorted layout at the largest row-block size

@@ -26,10 +26,6 @@ struct AlignArgs {
   int* sorted_ad;       // [>= padded total]: adapter of each sorted row (-1: none or padding),
                         // or nullptr
   int* n_blocks;        // [1] or nullptr
-  int* sub_row0;        // [<= T*k/sub_m + E]: first row of every sub_m-row tile holding rows of
-                        // an expert (row order), or nullptr
-  int* n_sub;           // [1]: entries of sub_row0
-  int sub_m;            // sub-tile rows (a divisor of block_m)
   int* g_lists;         // workspace for the arrays when they do not fit in LDS
   int lists_in_lds;
   int digit_bits;  // radix digit width D (1..10)
@@ -130,9 +126,7 @@ struct GemmArgs {
   int* d_parts;       // tiled down: [row tile][column tile] K parts written (combine reads it)
   int n_blocks_max;   // row blocks the grid is sized for (>= *n_blocks)
   int layout_bm;      // tiled: row-block size of the sorted layout (a multiple of the tile's BM;
-                      // a larger one is walked in the sub-tiles of the align's sub-tile list)
-  const int* sub_row0;  // first row of each sub-tile of 64 rows that holds rows
-  const int* n_sub;
+                      // a larger one is walked in BM-row sub-tiles)
   int n_col_tiles;    // skinny: column tiles of one row block (N / columns per workgroup)
   int lora_ext;       // tiled: 1 lets tiles with few adapter runs add the LoRA expand as extra K
                       // steps of the main loop (0: always in the epilogue)

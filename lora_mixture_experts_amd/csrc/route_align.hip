@@ -441,22 +441,16 @@ __global__ __launch_bounds__(1024) void align_kernel(AlignArgs a) {
   }
   __syncthreads();
   {
-    // padded length of each expert's region, and (when asked) its sub_m-row tiles that hold
-    // rows: their first rows, in row order, form the sub-tile list
-    int len = 0, subs = 0;
+    // padded length of each expert's region
+    int len = 0;
     if (tid < E) {
       s_sexp[tid] -= s_g0[tid];
       len = round_up_i(s_sexp[tid], block_m);
-      if (a.sub_row0) subs = (s_sexp[tid] + a.sub_m - 1) / a.sub_m;
     }
-    int eo, so, tot, stot;
-    block_excl_scan2(len, subs, eo, so, tot, stot, s_red);
+    int eo, d0, tot, d1;
+    block_excl_scan2(len, 0, eo, d0, tot, d1, s_red);
     if (tid < E) s_off[tid] = eo;
     if (tid == 0) s_off[E] = tot;
-    if (a.sub_row0) {
-      for (int j = 0; j < subs; ++j) a.sub_row0[so + j] = eo + j * a.sub_m;
-      if (tid == 0) *a.n_sub = stot;
-    }
   }
   __syncthreads();
   {
