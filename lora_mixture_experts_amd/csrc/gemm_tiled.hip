@@ -339,7 +339,7 @@ __global__ __launch_bounds__(64 * NW, 1) void tiled_gemm_kernel(GemmArgs a, int 
   // Tile order. The live tiles (n_blocks row blocks x n_tiles_n column tiles; the grid is
   // sized for the largest n_blocks) are numbered column group by column group, row group by row
   // group, in groups of up to 4 row blocks x 4 column tiles (measured best of the shapes from
-  // 2x8 to 16x8 on prefill and both adapter-stress batches). Hardware workgroup ids go
+  // 2x8 to 16x8 on prefill and both adapter-stress batches; sub-tiles: below). Hardware workgroup ids go
   // round-robin over the 8 XCDs, so each XCD is given an equal contiguous range of that
   // numbering: the workgroups it runs at once cover a few groups, every token tile and weight
   // tile fetched into its L2 serves several of them, and no XCD gets more tiles than another.
@@ -383,7 +383,8 @@ __global__ __launch_bounds__(64 * NW, 1) void tiled_gemm_kernel(GemmArgs a, int 
     nparts = GATEUP ? 1 : a.ksplit;
   }
   const int GR = sub > 1 ? sub : 4;                // row tiles per group
-  constexpr int GC = 4;                            // column tiles per group
+  const int GC = sub > 1 ? 8 : 4;                  // column tiles per group (8 with sub-tiles:
+                                                   // their token rows re-read half as often, -2%)
   const int cg = t / (nblk * GC);                 // column group (all but the last GC wide)
   const int cols = min(GC, n_tiles_n - cg * GC);
   const int u = t - cg * nblk * GC;
