@@ -275,6 +275,11 @@ __device__ __align__(16) uint32_t g_zero16[4] = {0u, 0u, 0u, 0u};
 template <class Pipe, bool STREAM_W = false>
 struct LoraExtLoader {
   static constexpr int NA = Pipe::NA, NB = Pipe::NB, BKS = Pipe::SUB * 16;
+  // 64-run chunks of the run tables: one run per row of the 192-row tiles of the adapter-stress
+  // layouts (down, many one-row runs: 0.45 -> 0.39 ms with one adapter per token); one chunk
+  // for the others, where more runs than fit the quarter-of-the-loop rule never occur (prefill's
+  // 256-row tiles: at most 16 runs of rank 64) and the extra search costs the main loop 3%
+  static constexpr int RC = Pipe::TILE_M == 192 ? 3 : 1;
   u32x4 xr, wr, zr;
   uint32_t xo[NA], wo[NB];  // main steps: offsets at step 0
   int nks;                  // main steps
@@ -284,7 +289,7 @@ struct LoraExtLoader {
   uint32_t bo[NB];          // byte offset of the B chunk inside one (adapter, expert) slice
   const char* bexp;         // B slice of (adapter 0, this expert)
   size_t a_stride;          // bytes between adapters' slices of one expert
-  int run_ad;               // lane j: adapter of run j
+  int run_ad[RC];           // lane j of chunk c: adapter of run 64 c + j
   int nr, rps;              // runs; runs per extension step
   uint32_t xe[NA];          // prepared extension step: A offsets
   const void* be[NB];       // and B addresses
@@ -303,7 +308,13 @@ struct LoraExtLoader {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const int j = x * rps + slot_b[i];
-      const int adj = __shfl(run_ad, j < nr ? j : 0);
+      const int jj = j < nr ? j : 0;
+      int adj = __shfl(run_ad[0], jj & 63);
+#pragma unroll
+      for (int c = 1; c < RC; ++c) {
+        const int v = __shfl(run_ad[c], jj & 63);
+        adj = (jj >> 6) == c ? v : adj;
+      }
       be[i] = j < nr ? (const void*)(bexp + (size_t)adj * a_stride + bo[i]) : (const void*)g_zero16;
     }
   }
@@ -463,58 +474,83 @@ __global__ __launch_bounds__(64 * NW, 1) void tiled_gemm_kernel(GemmArgs a, int 
   // to its rows, adapter >= 0): step x multiplies z of the rows of runs x*rps .. x*rps+rps-1,
   // each run in its own r-wide slice of the step's BK, zeros elsewhere, by the same slices of
   // the runs' B rows, so the expand streams through the main loop's pipeline. Every wavefront
-  // finds the runs itself (lane j holds run j) while the first K steps' loads are in flight.
-  // More runs than fit one wavefront, or more extension steps than a quarter of the main loop,
-  // take the epilogue instead (lora_expand_segs).
+  // finds the runs itself (lane j of register c holds run 64 c + j; 192-row tiles: one run per
+  // row, others up to 64) while the first K steps' loads are in flight. Tiles with more extension steps than a
+  // quarter of the main loop take the epilogue instead (lora_expand_segs).
   auto build_runs = [&]() {
     const int first = a.block_seg[blk];
     if (FP8 || ks != 0 || first < 0 || !a.lora_ext) return;
-    const int sj = first + lane;
-    bool in = false, run = false;
-    int lo = 0, hi = 0, ad = -1;
-    if (sj < *a.n_seg) {
-      const u32x4 sg = *reinterpret_cast<const u32x4*>(a.seg_table + 4 * (size_t)sj);
-      const int st = (int)sg[2], cnt = (int)sg[3];
-      in = st < row0 + BM;
-      lo = max(st - row0, 0);
-      hi = min(st + cnt - row0, BM);
-      ad = sanitize_adapter((int)sg[1], a.nA);
-      run = in && ad >= 0 && hi > lo;
+    // up to RC chunks of 64 segments from the block's first; lane j of chunk c holds the chunk's
+    // j-th run (compacted), whose index among the tile's runs is base[c] + j
+    constexpr int RC = decltype(ld)::RC;
+    int run_ad[RC], run_lo[RC], run_hi[RC], base[RC + 1];
+    base[0] = 0;
+    bool more = true;  // the last segment looked at starts inside the tile: the next one may too
+#pragma unroll
+    for (int c = 0; c < RC; ++c) {
+      run_ad[c] = 0;
+      run_lo[c] = 0;
+      run_hi[c] = 0;
+      base[c + 1] = base[c];
+      if (!more) continue;
+      const int sj = first + 64 * c + lane;
+      bool in = false, run = false;
+      int lo = 0, hi = 0, ad = -1;
+      if (sj < *a.n_seg) {
+        const u32x4 sg = *reinterpret_cast<const u32x4*>(a.seg_table + 4 * (size_t)sj);
+        const int st = (int)sg[2], cnt = (int)sg[3];
+        in = st < row0 + BM;
+        lo = max(st - row0, 0);
+        hi = min(st + cnt - row0, BM);
+        ad = sanitize_adapter((int)sg[1], a.nA);
+        run = in && ad >= 0 && hi > lo;
+      }
+      const uint64_t m = __ballot(run);
+      more = (__ballot(in) >> 63) != 0;
+      // lane j <- run j (lanes without a run send theirs to lane 63, unused past the count)
+      const int tgt = run ? __popcll(m & lanemask_lt()) : 63;
+      run_ad[c] = __builtin_amdgcn_ds_permute(tgt * 4, ad);
+      run_lo[c] = __builtin_amdgcn_ds_permute(tgt * 4, lo);
+      run_hi[c] = __builtin_amdgcn_ds_permute(tgt * 4, hi);
+      base[c + 1] = base[c] + __popcll(m);
     }
-    const uint64_t m = __ballot(run);
-    // the chunk's last segment starts inside the tile: the next one may too
-    bool more = (__ballot(in) >> 63) != 0;
     if (more) {
-      const int sn = first + 64;
+      const int sn = first + 64 * RC;
       more = sn < *a.n_seg && a.seg_table[4 * (size_t)sn + 2] < row0 + BM;
     }
-    const int nr = __popcll(m);
+    const int nr = base[RC];
     const int n_ext = (nr + ld.rps - 1) / ld.rps;
     if (more || n_ext == 0 || 4 * n_ext > ld.nks) return;
-    // lane j <- run j (lanes without a run send theirs to lane 63, unused when nr < 64)
-    const int tgt = run ? __popcll(m & lanemask_lt()) : 63;
-    const int run_ad = __builtin_amdgcn_ds_permute(tgt * 4, ad);
-    const int run_lo = __builtin_amdgcn_ds_permute(tgt * 4, lo);
-    const int run_hi = __builtin_amdgcn_ds_permute(tgt * 4, hi);
     use_ext = true;
     ld.nr = nr;
-    ld.run_ad = run_ad;
+#pragma unroll
+    for (int c = 0; c < RC; ++c) ld.run_ad[c] = run_ad[c];
     nsteps = ld.nks + n_ext;
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
       const int row = Pipe::load_row(i, wave, lane);
       const int chunk = Pipe::load_chunk(row, lane);
-      // runs starting at or before the row (runs are disjoint and in row order); every lane
-      // takes part in every shuffle
-      int b = 0;
+      // the last run starting at or before the row (runs are disjoint and in row order): in
+      // each chunk, the count of its runs that start at or before it; every lane takes part in
+      // every shuffle
+      int j = -1, hi_j = 0;
 #pragma unroll
-      for (int step = 64; step > 0; step >>= 1) {
-        const int cand = b + step;
-        const int lo_c = __shfl(run_lo, min(cand, nr) - 1);
-        if (cand <= nr && lo_c <= row) b = cand;
+      for (int c = 0; c < RC; ++c) {
+        const int nc = base[c + 1] - base[c];
+        if (nc == 0) continue;  // (wavefront-uniform)
+        int b = 0;
+#pragma unroll
+        for (int step = 64; step > 0; step >>= 1) {
+          const int cand = b + step;
+          const int lo_c = __shfl(run_lo[c], max(min(cand, nc) - 1, 0));
+          if (cand <= nc && lo_c <= row) b = cand;
+        }
+        const int h = __shfl(run_hi[c], b > 0 ? b - 1 : 0);
+        if (b > 0) {
+          j = base[c] + b - 1;
+          hi_j = h;
+        }
       }
-      const int j = b - 1;
-      const int hi_j = __shfl(run_hi, j >= 0 ? j : 0);
       ld.jrow[i] = (j >= 0 && row < hi_j) ? j : -1;
       ld.slot_a[i] = chunk / cpr_r;
       ld.zo[i] = (uint32_t)(((size_t)(row0 + row) * r + (chunk % cpr_r) * 8) * 2);

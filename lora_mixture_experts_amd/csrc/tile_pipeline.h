@@ -83,6 +83,7 @@ struct TilePipe {
   static_assert(BK == 32 || BK == 64, "K step of 32 or 64");
   static_assert(!W8 || BK == 64, "E4M3 tiles take 64-wide K steps");
   static_assert(NST >= 2, "at least two LDS stages");
+  static constexpr int TILE_M = BM;
   static constexpr int WAVES_N = BN / WN;
   static_assert((BM / WM) * WAVES_N == NWAVES, "WM x WN wavefront tiles cover the tile");
   static constexpr int FM = WM / 32, FN = WN / 32;
